@@ -1,0 +1,169 @@
+"""Plain-definition attention in float64 on the CPU (the oracle).
+
+TEST INFRASTRUCTURE ONLY -- see ``oracle/__init__.py``.  The product path must
+never import this module.
+
+What is computed follows the definition the three source pages share:
+
+* "Flash Attention, From First Principles", section "What is attention?":
+  O = softmax(Q K^T) V, with the 1/sqrt(d) factor applied to the scores before
+  the softmax (the page drops it for the derivation and notes the code applies
+  it).  Here the factor is an explicit ``scale`` argument.
+* same page, "Stop 2.5: don't set the machine on fire": subtract the row max
+  before exponentiating; shift invariance makes that exact.
+* same page, "Stop 3: the pour": row i of O is the P-weighted blend of V rows.
+* "LLM Architecture Refresh [3]: Flash Attention Is Exact, and Here's the
+  Proof", section 5: causal masking forces scores above the diagonal to -inf
+  before the softmax, so key j is visible to query i iff j <= i.
+* "FlashAttention from scratch", Follow-up questions: the saved statistic is
+  the log-sum-exp L = m + log(l), natural log, in scaled-score units.
+
+The backward is the softmax Jacobian written out (not the kernel's D shortcut):
+dV = P^T dO and the matmul rule dA = dC B^T, dB = A^T dC ("Flash Attention, From
+First Principles", "The ghost at the door"); dP = dO V^T;
+dS_ij = P_ij (dP_ij - sum_k P_ik dP_ik); dQ = s dS K, dK = s dS^T Q, the scale
+factor s multiplying both ("FlashAttention from scratch", Follow-up questions).
+
+To bound memory the score matrix is formed ``row_chunk`` query rows at a time;
+each row's arithmetic is unchanged by that (softmax is row-wise).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+_DEFAULT_ROW_CHUNK = 256
+
+
+def _as_f64(x) -> np.ndarray:
+    a = np.asarray(x, dtype=np.float64)
+    return a
+
+
+def softmax_rows(s) -> np.ndarray:
+    """Row-wise softmax with the max subtracted first.
+
+    "Flash Attention, From First Principles", "Stop 2: from scores to
+    proportions" (exponentiate, then divide by the sum) and "Stop 2.5"
+    (subtract the row max; shift invariance licenses it).  Rows that are
+    entirely -inf return all zeros (a row with nothing visible has no mass).
+    """
+    s = _as_f64(s)
+    m = np.max(s, axis=-1, keepdims=True)
+    m_safe = np.where(np.isfinite(m), m, 0.0)
+    e = np.exp(s - m_safe)
+    den = np.sum(e, axis=-1, keepdims=True)
+    den_safe = np.where(den > 0, den, 1.0)
+    return e / den_safe
+
+
+def visible_mask(n_q: int, n_k: int, causal: bool, row0: int = 0) -> np.ndarray:
+    """Boolean [rows, n_k] mask of visible keys for query rows row0..row0+n_q-1.
+
+    Causal rule ("LLM Architecture Refresh [3]", sections 5 and 7): key j is
+    visible to query i iff j <= i.  Non-causal: every key is visible.
+    """
+    if not causal:
+        return np.ones((n_q, n_k), dtype=bool)
+    i = np.arange(row0, row0 + n_q)[:, None]
+    j = np.arange(n_k)[None, :]
+    return j <= i
+
+
+def _scores(q_rows, k, scale, causal, row0):
+    s = scale * (q_rows @ k.T)
+    if causal:
+        mask = visible_mask(q_rows.shape[0], k.shape[0], True, row0)
+        s = np.where(mask, s, -np.inf)
+    return s
+
+
+def naive_probs(q, k, scale: float, causal: bool = False) -> np.ndarray:
+    """The full probability matrix P = softmax(scale * Q K^T) for one head.
+
+    Small inputs only (materialises N x N).  q: [N, d], k: [N, d].
+    """
+    q = _as_f64(q)
+    k = _as_f64(k)
+    return softmax_rows(_scores(q, k, float(scale), causal, 0))
+
+
+def _fwd_head(q, k, v, scale, causal, row_chunk):
+    n, d = q.shape
+    o = np.empty((n, v.shape[1]), dtype=np.float64)
+    lse = np.empty((n,), dtype=np.float64)
+    for r0 in range(0, n, row_chunk):
+        r1 = min(n, r0 + row_chunk)
+        s = _scores(q[r0:r1], k, scale, causal, r0)          # S = s Q K^T, masked
+        m = np.max(s, axis=1, keepdims=True)                  # row max
+        e = np.exp(s - m)                                     # shifted exponentials
+        l = np.sum(e, axis=1, keepdims=True)                  # row sum
+        p = e / l                                             # softmax
+        o[r0:r1] = p @ v                                      # the pour
+        lse[r0:r1] = (m + np.log(l))[:, 0]                    # L = m + log l
+    return o, lse
+
+
+def naive_fwd(q, k, v, scale: float, causal: bool = False,
+              row_chunk: int = _DEFAULT_ROW_CHUNK):
+    """Exact attention forward.  Returns (O, lse) in float64.
+
+    q, k, v: arrays of shape [..., N, d] (any leading batch/head dims; q and k
+    share N and d, v shares N).  ``scale`` multiplies Q K^T before the softmax.
+    lse has shape [..., N].
+    """
+    q = _as_f64(q)
+    k = _as_f64(k)
+    v = _as_f64(v)
+    scale = float(scale)
+    lead = q.shape[:-2]
+    n = q.shape[-2]
+    o = np.empty(lead + (n, v.shape[-1]), dtype=np.float64)
+    lse = np.empty(lead + (n,), dtype=np.float64)
+    if n == 0:
+        return o, lse
+    for idx in np.ndindex(*lead):
+        o[idx], lse[idx] = _fwd_head(q[idx], k[idx], v[idx], scale, causal,
+                                     row_chunk)
+    return o, lse
+
+
+def _bwd_head(q, k, v, do, scale, causal, row_chunk):
+    n = q.shape[0]
+    dq = np.empty_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for r0 in range(0, n, row_chunk):
+        r1 = min(n, r0 + row_chunk)
+        s = _scores(q[r0:r1], k, scale, causal, r0)
+        p = softmax_rows(s)                                   # P, masked entries 0
+        dv += p.T @ do[r0:r1]                                 # dV = P^T dO
+        dp = do[r0:r1] @ v.T                                  # dP = dO V^T
+        # softmax Jacobian: dS_ij = P_ij (dP_ij - sum_k P_ik dP_ik)
+        ds = p * (dp - np.sum(p * dp, axis=1, keepdims=True))
+        dq[r0:r1] = scale * (ds @ k)                          # dQ = s dS K
+        dk += scale * (ds.T @ q[r0:r1])                       # dK = s dS^T Q
+    return dq, dk, dv
+
+
+def naive_bwd(q, k, v, do, scale: float, causal: bool = False,
+              row_chunk: int = _DEFAULT_ROW_CHUNK):
+    """Gradients (dQ, dK, dV) of sum(O * dO) for O = naive_fwd(q, k, v).
+
+    Shapes as ``naive_fwd``; ``do`` has O's shape.  float64 throughout.
+    """
+    q = _as_f64(q)
+    k = _as_f64(k)
+    v = _as_f64(v)
+    do = _as_f64(do)
+    scale = float(scale)
+    lead = q.shape[:-2]
+    dq = np.empty_like(q)
+    dk = np.empty_like(k)
+    dv = np.empty_like(v)
+    if q.shape[-2] == 0:
+        return dq, dk, dv
+    for idx in np.ndindex(*lead):
+        dq[idx], dk[idx], dv[idx] = _bwd_head(q[idx], k[idx], v[idx], do[idx],
+                                              scale, causal, row_chunk)
+    return dq, dk, dv
