@@ -1,0 +1,233 @@
+"""Exact tiled attention (FlashAttention forward and backward) on MI355X.
+
+A thin ctypes binding over ``libfa.so``, the C ABI declared in
+``include/fa.h``.  Every step of the computation runs in the library's HIP
+kernels; this module only checks tensor metadata, allocates outputs with torch
+and passes raw device pointers and the current HIP stream.  There is no CPU
+fallback: if the library is missing, every call raises.
+
+Low-level entry points carry the C names (``fa_fwd``, ``fa_fwd_f32``,
+``fa_bwd``, ``fa_bwd_workspace_size``, ``fa_status_string``) and take
+preallocated tensors; ``forward``/``backward``/``attention`` allocate.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = [
+    "FAError", "library_path", "load_library",
+    "fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_bwd_workspace_size", "fa_status_string",
+    "forward", "backward", "attention",
+    "FA_OK", "FA_ERR_NULL", "FA_ERR_SHAPE", "FA_ERR_HEADDIM", "FA_ERR_ALIGN",
+    "FA_ERR_ALIAS", "FA_ERR_SCALE", "FA_ERR_HIP", "FA_ERR_WORKSPACE", "FA_MAX_N",
+]
+
+FA_OK = 0
+FA_ERR_NULL = 1
+FA_ERR_SHAPE = 2
+FA_ERR_HEADDIM = 3
+FA_ERR_ALIGN = 4
+FA_ERR_ALIAS = 5
+FA_ERR_SCALE = 6
+FA_ERR_HIP = 7
+FA_ERR_WORKSPACE = 8
+FA_MAX_N = 1 << 22
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+
+class FAError(RuntimeError):
+    """A nonzero status returned by libfa.so."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({fa_status_string(status)})")
+
+
+def library_path() -> str:
+    return os.path.join(_PKG, "libfa.so")
+
+
+def load_library():
+    """Load libfa.so (built in-tree by ``build.py``); raise if it is absent."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m exact_tiled_attention_10_amd.build` "
+            "(there is no fallback implementation)")
+    lib = ctypes.CDLL(path)
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
+    lib.fa_fwd.restype = i
+    lib.fa_fwd_f32.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
+    lib.fa_fwd_f32.restype = i
+    lib.fa_bwd_workspace_size.argtypes = [i, i, i, i]
+    lib.fa_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                           i, i, i, i, i, f, vp]
+    lib.fa_bwd.restype = i
+    lib.fa_status_string.argtypes = [i]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    _LIB = lib
+    return lib
+
+
+def fa_status_string(status: int) -> str:
+    return load_library().fa_status_string(int(status)).decode()
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    return t.data_ptr() or None
+
+
+def _stream_handle(device: torch.device, stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    h = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    return h or None
+
+
+def _dims(q: torch.Tensor):
+    if q.dim() != 4:
+        raise ValueError(f"expected a [B, H, N, d] tensor, got shape {tuple(q.shape)}")
+    return tuple(int(x) for x in q.shape)
+
+
+def _check(t: torch.Tensor, name: str, shape, dtype, device):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)} != {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype} != {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name}: device {t.device} != {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+def _default_scale(d: int, scale: Optional[float]) -> float:
+    return 1.0 / math.sqrt(d) if scale is None else float(scale)
+
+
+def _raise(status: int, where: str):
+    if status != FA_OK:
+        raise FAError(status, where)
+
+
+# ---------------------------------------------------------------------------
+# low-level entry points (preallocated outputs), same names as the C ABI
+# ---------------------------------------------------------------------------
+
+def fa_fwd(q, k, v, o, lse, causal: bool, scale: float, stream=None) -> None:
+    """bf16 forward into preallocated ``o`` [B,H,N,d] bf16 and ``lse`` [B,H,N] f32."""
+    B, H, N, d = _dims(q)
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
+        _check(t, nm, (B, H, N, d), torch.bfloat16, q.device)
+    _check(lse, "lse", (B, H, N), torch.float32, q.device)
+    st = load_library().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
+                               int(bool(causal)), float(scale),
+                               _stream_handle(q.device, stream))
+    _raise(st, "fa_fwd")
+
+
+def fa_fwd_f32(q, k, v, o, lse, causal: bool, scale: float, stream=None) -> None:
+    """fp32 forward into preallocated ``o`` [B,H,N,d] f32 and ``lse`` [B,H,N] f32."""
+    B, H, N, d = _dims(q)
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
+        _check(t, nm, (B, H, N, d), torch.float32, q.device)
+    _check(lse, "lse", (B, H, N), torch.float32, q.device)
+    st = load_library().fa_fwd_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
+                                   int(bool(causal)), float(scale),
+                                   _stream_handle(q.device, stream))
+    _raise(st, "fa_fwd_f32")
+
+
+def fa_bwd_workspace_size(B: int, H: int, N: int, d: int) -> int:
+    return int(load_library().fa_bwd_workspace_size(B, H, N, d))
+
+
+def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, causal: bool, scale: float,
+           stream=None) -> None:
+    """bf16 backward into preallocated ``dq``, ``dk``, ``dv``; ``workspace`` is a
+    uint8 device tensor of at least ``fa_bwd_workspace_size`` bytes."""
+    B, H, N, d = _dims(q)
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout"), (dq, "dq"),
+                  (dk, "dk"), (dv, "dv")):
+        _check(t, nm, (B, H, N, d), torch.bfloat16, q.device)
+    _check(lse, "lse", (B, H, N), torch.float32, q.device)
+    if workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace: must be a contiguous tensor on q's device")
+    nbytes = workspace.numel() * workspace.element_size()
+    st = load_library().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+                               _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), nbytes,
+                               B, H, N, d, int(bool(causal)), float(scale),
+                               _stream_handle(q.device, stream))
+    _raise(st, "fa_bwd")
+
+
+# ---------------------------------------------------------------------------
+# allocating wrappers
+# ---------------------------------------------------------------------------
+
+def forward(q, k, v, causal: bool = False, scale: Optional[float] = None,
+            stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """O, lse = exact attention of [B,H,N,d] bf16 or fp32 tensors on the GPU."""
+    B, H, N, d = _dims(q)
+    s = _default_scale(d, scale)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if q.dtype == torch.float32:
+        fa_fwd_f32(q, k, v, o, lse, causal, s, stream)
+    else:
+        fa_fwd(q, k, v, o, lse, causal, s, stream)
+    return o, lse
+
+
+def backward(q, k, v, o, lse, do, causal: bool = False, scale: Optional[float] = None,
+             stream=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """dQ, dK, dV for bf16 tensors, recomputing P from ``lse``."""
+    B, H, N, d = _dims(q)
+    s = _default_scale(d, scale)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    ws = torch.empty(max(1, fa_bwd_workspace_size(B, H, N, d)), dtype=torch.uint8,
+                     device=q.device)
+    fa_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, causal, s, stream)
+    return dq, dk, dv
+
+
+class _Attention(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, causal, scale):
+        o, lse = forward(q, k, v, causal, scale)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.causal = causal
+        ctx.scale = scale
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse = ctx.saved_tensors
+        dq, dk, dv = backward(q, k, v, o, lse, do.contiguous(), ctx.causal, ctx.scale)
+        return dq, dk, dv, None, None
+
+
+def attention(q, k, v, causal: bool = False, scale: Optional[float] = None):
+    """Differentiable exact attention (bf16): O = softmax(scale Q K^T) V."""
+    return _Attention.apply(q, k, v, causal, scale)

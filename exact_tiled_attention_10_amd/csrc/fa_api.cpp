@@ -1,0 +1,141 @@
+// C ABI of libfa.so: argument validation, then the kernel launchers.
+//
+// Every check runs before any HIP call, so a rejected call never touches the
+// device or the stream (and can be exercised on a machine without a GPU).
+#include "fa.h"
+
+#include <limits.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "fa_internal.h"
+
+namespace {
+
+struct Range {
+  uintptr_t lo;
+  uintptr_t hi;  // one past the end
+};
+
+Range range_of(const void* p, size_t bytes) {
+  uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Range{a, a + bytes};
+}
+
+bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+// Shape, head-dim and scale checks shared by every entry point.  On success
+// writes the element count of one [B, H, N, d] tensor and of one [B, H, N]
+// statistic.
+int check_common(int B, int H, int N, int d, float scale, size_t* tensor_elems,
+                 size_t* row_elems) {
+  if (B < 0 || H < 0 || N < 0 || N > FA_MAX_N) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  const long long bh = (long long)B * (long long)H;
+  if (bh > INT_MAX) return FA_ERR_SHAPE;
+  // grid size: one workgroup per (batch*head, 64-row tile) at most
+  if (bh * (((long long)N + 63) / 64) > INT_MAX) return FA_ERR_SHAPE;
+  if (!isfinite(scale)) return FA_ERR_SCALE;
+  *row_elems = (size_t)bh * (size_t)N;
+  *tensor_elems = *row_elems * (size_t)d;
+  return FA_OK;
+}
+
+int from_hip(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+           int d, int causal, float scale, hipStream_t stream) {
+  size_t te = 0, re = 0;
+  int st = check_common(B, H, N, d, scale, &te, &re);
+  if (st != FA_OK) return st;
+  if (re == 0) return FA_OK;
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(lse))
+    return FA_ERR_ALIGN;
+  const size_t tb = te * 2;
+  const Range in[3] = {range_of(q, tb), range_of(k, tb), range_of(v, tb)};
+  const Range ro = range_of(o, tb), rl = range_of(lse, re * 4);
+  for (const Range& r : in)
+    if (overlaps(r, ro) || overlaps(r, rl)) return FA_ERR_ALIAS;
+  if (overlaps(ro, rl)) return FA_ERR_ALIAS;
+  return from_hip(fa::launch_fwd_bf16(q, k, v, o, lse, B * H, N, d, causal != 0, scale, stream));
+}
+
+int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H,
+               int N, int d, int causal, float scale, hipStream_t stream) {
+  size_t te = 0, re = 0;
+  int st = check_common(B, H, N, d, scale, &te, &re);
+  if (st != FA_OK) return st;
+  if (re == 0) return FA_OK;
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(lse))
+    return FA_ERR_ALIGN;
+  const size_t tb = te * 4;
+  const Range in[3] = {range_of(q, tb), range_of(k, tb), range_of(v, tb)};
+  const Range ro = range_of(o, tb), rl = range_of(lse, re * 4);
+  for (const Range& r : in)
+    if (overlaps(r, ro) || overlaps(r, rl)) return FA_ERR_ALIAS;
+  if (overlaps(ro, rl)) return FA_ERR_ALIAS;
+  return from_hip(fa::launch_fwd_f32(q, k, v, o, lse, B * H, N, d, causal != 0, scale, stream));
+}
+
+size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
+  size_t te = 0, re = 0;
+  if (check_common(B, H, N, d, 1.0f, &te, &re) != FA_OK) return 0;
+  return fa::bwd_workspace_bytes(B * H, N, d);
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, void* dq, void* dk, void* dv, void* workspace,
+           size_t workspace_bytes, int B, int H, int N, int d, int causal, float scale,
+           hipStream_t stream) {
+  size_t te = 0, re = 0;
+  int st = check_common(B, H, N, d, scale, &te, &re);
+  if (st != FA_OK) return st;
+  if (re == 0) return FA_OK;
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace)
+    return FA_ERR_NULL;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(dout) ||
+      misaligned(lse) || misaligned(dq) || misaligned(dk) || misaligned(dv) ||
+      misaligned(workspace))
+    return FA_ERR_ALIGN;
+  const size_t need = fa::bwd_workspace_bytes(B * H, N, d);
+  if (workspace_bytes < need) return FA_ERR_WORKSPACE;
+  const size_t tb = te * 2;
+  const Range in[6] = {range_of(q, tb),    range_of(k, tb),    range_of(v, tb),
+                       range_of(o, tb),    range_of(dout, tb), range_of(lse, re * 4)};
+  const Range out[4] = {range_of(dq, tb), range_of(dk, tb), range_of(dv, tb),
+                        range_of(workspace, need)};
+  for (const Range& a : out) {
+    for (const Range& b : in)
+      if (overlaps(a, b)) return FA_ERR_ALIAS;
+  }
+  for (int i = 0; i < 4; ++i)
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(out[i], out[j])) return FA_ERR_ALIAS;
+  return from_hip(fa::launch_bwd_bf16(q, k, v, o, dout, lse, dq, dk, dv, workspace, B * H, N, d,
+                                      causal != 0, scale, stream));
+}
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL: return "a required pointer is NULL";
+    case FA_ERR_SHAPE: return "invalid shape (B, H or N negative, N too large, or size overflow)";
+    case FA_ERR_HEADDIM: return "unsupported head dimension (must be 64 or 128)";
+    case FA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
+    case FA_ERR_ALIAS: return "an output overlaps an input or another output";
+    case FA_ERR_SCALE: return "scale is not finite";
+    case FA_ERR_HIP: return "HIP kernel launch failed";
+    case FA_ERR_WORKSPACE: return "backward workspace too small";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,93 @@
+// Shared device helpers for the gfx950 attention kernels.
+//
+// MFMA layout facts used throughout (CDNA3/CDNA4 matrix-core operand layout,
+// 64-lane wavefront):
+//   v_mfma_f32_32x32x16_bf16  D[32x32] += A[32x16] * B[16x32]
+//     A: lane l holds row m = l % 32 and 8 k-values chosen by (l / 32, t)
+//     B: lane l holds column n = l % 32 and the same 8 k-values
+//     D: lane l, register r holds D[8*(r/4) + 4*(l/32) + r%4][l % 32]
+//   v_mfma_f32_32x32x2_f32: as above with one k-value per lane, k = l / 32.
+// The mapping of (l / 32, t) to k never matters to the kernels: A and B always
+// carry the same logical key (or feature) in the same slot, and the product
+// sums over every slot.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+__device__ __forceinline__ f32x16 mfma_32x32x16_bf16(const bf16x8& a,
+                                                     const bf16x8& b,
+                                                     const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma_32x32x2_f32(float a, float b,
+                                                   const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// Round-to-nearest-even float -> bf16 pair packed in one dword (lo = a).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  __bf16 x = (__bf16)a;
+  __bf16 y = (__bf16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, x) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+
+// Low (sel = 0x05040100) or high (sel = 0x07060302) 16-bit halves of a and b
+// packed as {a_half, b_half}.
+__device__ __forceinline__ uint32_t pack_lo16(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t pack_hi16(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
+  return __builtin_bit_cast(float, bits16 << 16);
+}
+
+__device__ __forceinline__ float wave_xor32(float x) {
+  // exchange with the lane 32 positions away (the other half of the wave)
+  return __shfl_xor(x, 32, 64);
+}
+
+// Work-tile order for the forward and backward grids.
+//
+// Workgroups are dispatched round-robin over the 8 XCDs (workgroup i lands on
+// XCD i % 8), and each XCD has its own L2.  When the (batch*head) count
+// divides by 8, every XCD is given whole heads, so the key/value tiles a head
+// streams stay in one L2; within an XCD the tiles are issued heaviest first
+// (highest query tile first, which under causal masking carries the most key
+// tiles) so the long tiles do not trail at the end.  Otherwise fall back to
+// heaviest first across all heads.
+__device__ __forceinline__ void map_tile(int bid, int BH, int ntiles, bool heavy_first,
+                                         int* bh, int* tile) {
+  int t, h;
+  if ((BH & 7) == 0) {
+    const int xcd = bid & 7;
+    const int j = bid >> 3;
+    const int hpx = BH >> 3;
+    t = j / hpx;
+    h = xcd * hpx + (j - t * hpx);
+  } else {
+    t = bid / BH;
+    h = bid - t * BH;
+  }
+  *bh = h;
+  *tile = heavy_first ? (ntiles - 1 - t) : t;
+}
+
+}  // namespace fa

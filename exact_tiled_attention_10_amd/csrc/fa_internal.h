@@ -1,0 +1,26 @@
+// Kernel launchers called by the C ABI layer (fa_api.cpp).  Arguments are
+// already validated there; each launcher only enqueues work on `stream` and
+// returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+
+namespace fa {
+
+hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int BH, int N, int d, bool causal, float scale, hipStream_t stream);
+
+hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                          int BH, int N, int d, bool causal, float scale, hipStream_t stream);
+
+// Backward: D = rowsum(dO * O) and dQ accumulator zeroing, the key-tile
+// kernel (dK, dV, atomic dQ), then dQ conversion.  `ws` holds D (BH*N floats,
+// rounded up to 256 bytes) followed by the fp32 dQ accumulator.
+size_t bwd_workspace_bytes(int BH, int N, int d);
+hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
+                           const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                           void* ws, int BH, int N, int d, bool causal, float scale,
+                           hipStream_t stream);
+
+}  // namespace fa

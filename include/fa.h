@@ -1,0 +1,137 @@
+/*
+ * fa.h -- C ABI of the exact tiled attention library (libfa.so, gfx950).
+ *
+ * Computes exact attention O = softmax(scale * Q K^T) V and its gradients on
+ * one MI355X, tiled so the N x N score matrix never exists in device memory.
+ *
+ * The operation ("Flash Attention, From First Principles", sections "What is
+ * attention?" and "Stop 3: the pour"; "LLM Architecture Refresh [3]: Flash
+ * Attention Is Exact, and Here's the Proof", sections 2, 4 and 7):
+ *
+ *   S   = scale * Q K^T                      (per batch b, head h)
+ *   S_ij = -inf where causal and j > i        (key j visible to query i iff j <= i)
+ *   P   = softmax(S) row-wise;  O = P V
+ *   lse_i = log(sum_j exp(S_ij))             (natural log, scaled-score units)
+ *
+ * The saved statistic lse is the log-sum-exp L = m + log(l) of "FlashAttention
+ * from scratch: how it works and how to code it", Follow-up questions; the
+ * backward rebuilds P = exp(S - L) from it instead of storing P.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Layout   Every tensor is a contiguous row-major [B, H, N, d] array (query,
+ *          key, value, output and gradient tensors alike); lse and the
+ *          backward's D are contiguous [B, H, N] float arrays.  Queries and
+ *          keys have the same length N.
+ * Pointers All pointers are DEVICE pointers (memory from hipMalloc or any
+ *          allocator handing out device memory).  Tensor pointers must be
+ *          16-byte aligned.  Inputs are only read.  Outputs must not overlap
+ *          any input or each other.
+ * Ownership The caller owns every buffer, including the backward workspace.
+ *          The library allocates nothing, keeps no mutable global state and
+ *          may be called from several host threads at once.
+ * Streams  Work is enqueued on `stream` (0 = the null stream) and the call
+ *          returns without waiting.  Faults during execution surface at the
+ *          caller's next synchronisation on that stream.
+ * Errors   Every call returns an int status (FA_OK == 0).  Arguments are
+ *          validated before any HIP call is made, so a rejected call touches
+ *          neither the device nor the stream.  B*H*N == 0 is a valid no-op.
+ *          Nothing is thrown across the ABI.
+ * Sizes    d must be 64 or 128.  B, H >= 0; 0 <= N <= FA_MAX_N.
+ * Scale    Any finite float (the usual value is 1/sqrt(d)).
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+enum {
+  FA_OK = 0,
+  FA_ERR_NULL = 1,      /* a required pointer is NULL                        */
+  FA_ERR_SHAPE = 2,     /* B, H or N negative, or N > FA_MAX_N, or overflow   */
+  FA_ERR_HEADDIM = 3,   /* d is not 64 or 128                                 */
+  FA_ERR_ALIGN = 4,     /* a tensor pointer is not 16-byte aligned            */
+  FA_ERR_ALIAS = 5,     /* an output overlaps an input or another output      */
+  FA_ERR_SCALE = 6,     /* scale is NaN or infinite                           */
+  FA_ERR_HIP = 7,       /* a kernel launch was rejected by the HIP runtime    */
+  FA_ERR_WORKSPACE = 8  /* backward workspace smaller than required           */
+};
+
+/* Largest supported sequence length (keeps every per-head offset in 31 bits). */
+#define FA_MAX_N (1 << 22)
+
+/*
+ * fa_fwd -- forward pass, bfloat16 tensors.
+ *
+ *   q, k, v  [B, H, N, d] bfloat16 inputs (read only).
+ *   o        [B, H, N, d] bfloat16 output, O rounded to nearest even.
+ *   lse      [B, H, N] float32 output, natural-log log-sum-exp of each row of
+ *            scale * Q K^T over its visible keys.
+ *   causal   0 = every key visible; nonzero = key j visible to query i iff j <= i.
+ *   scale    multiplies Q K^T before the softmax.
+ *
+ * Scores, the running max / running sum and the output accumulator are fp32;
+ * the probability tile is rounded to bfloat16 for the P V product.  Tiles
+ * whose keys all lie in the future of every query of the tile are skipped
+ * ("LLM Architecture Refresh [3]", section 7).
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int N, int d, int causal, float scale,
+           hipStream_t stream);
+
+/*
+ * fa_fwd_f32 -- forward pass, float32 tensors end to end.
+ *
+ * Same operation, layout and rules as fa_fwd with every tensor float32 and
+ * every product carried out in float32 (fp32 MFMA).
+ */
+int fa_fwd_f32(const float* q, const float* k, const float* v, float* o,
+               float* lse, int B, int H, int N, int d, int causal, float scale,
+               hipStream_t stream);
+
+/*
+ * fa_bwd_workspace_size -- bytes of device workspace fa_bwd needs.
+ *
+ * Returns 0 for invalid shapes.  The workspace holds D = rowsum(dO * O)
+ * ([B, H, N] float32) and the float32 dQ accumulator ([B, H, N, d]).
+ */
+size_t fa_bwd_workspace_size(int B, int H, int N, int d);
+
+/*
+ * fa_bwd -- backward pass, bfloat16 tensors.
+ *
+ *   q, k, v, o  [B, H, N, d] bfloat16: the forward's inputs and output.
+ *   dout        [B, H, N, d] bfloat16: gradient of the loss w.r.t. O
+ *               (named for the dO of the pages; `do` is a C keyword).
+ *   lse         [B, H, N] float32 from fa_fwd on the same inputs.
+ *   dq, dk, dv  [B, H, N, d] bfloat16 outputs.
+ *   workspace   device buffer of at least fa_bwd_workspace_size(B, H, N, d)
+ *               bytes, 16-byte aligned; contents on entry are ignored and
+ *               overwritten.  workspace_bytes is its size.
+ *
+ * Recomputes every probability tile from Q, K and lse ("FlashAttention from
+ * scratch", Follow-up questions): P = exp(S - L); dV += P^T dO; dP = dO V^T;
+ * D = rowsum(dO * O); dS = P * (dP - D); dK += scale * dS^T Q; dQ += scale *
+ * dS K.  dK and dV accumulate per key tile; dQ accumulates across key tiles
+ * in the float32 workspace with atomic adds, so dQ may differ between runs in
+ * its last bits.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o,
+           const void* dout, const float* lse, void* dq, void* dk, void* dv,
+           void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+           int causal, float scale, hipStream_t stream);
+
+/* fa_status_string -- static, human-readable text for a status code. */
+const char* fa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

@@ -21,6 +21,7 @@ from .attention import (
     softmax_rows,
     naive_probs,
     naive_fwd,
+    naive_fwd_rows,
     naive_bwd,
     visible_mask,
 )
@@ -35,6 +36,7 @@ __all__ = [
     "softmax_rows",
     "naive_probs",
     "naive_fwd",
+    "naive_fwd_rows",
     "naive_bwd",
     "visible_mask",
     "online_normaliser",

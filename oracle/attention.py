@@ -128,6 +128,26 @@ def naive_fwd(q, k, v, scale: float, causal: bool = False,
     return o, lse
 
 
+def naive_fwd_rows(q_rows, k, v, scale: float, causal: bool, positions):
+    """Exact attention for selected query rows of one head (sampled checks).
+
+    q_rows: [R, d] queries sitting at sequence positions ``positions`` (R ints);
+    k, v: [N, d] the head's full keys and values.  Returns (O [R, d], lse [R]).
+    Same definition as ``naive_fwd``; the causal rule uses each row's position.
+    """
+    q_rows = _as_f64(q_rows)
+    k = _as_f64(k)
+    v = _as_f64(v)
+    pos = np.asarray(positions, dtype=np.int64)
+    s = float(scale) * (q_rows @ k.T)
+    if causal:
+        s = np.where(np.arange(k.shape[0])[None, :] <= pos[:, None], s, -np.inf)
+    m = np.max(s, axis=1, keepdims=True)
+    e = np.exp(s - m)
+    l = np.sum(e, axis=1, keepdims=True)
+    return (e / l) @ v, (m + np.log(l))[:, 0]
+
+
 def _bwd_head(q, k, v, do, scale, causal, row_chunk):
     n = q.shape[0]
     dq = np.empty_like(q)

@@ -1,0 +1,138 @@
+"""The C ABI boundary on a host without a GPU.
+
+libfa.so must load, export every function include/fa.h declares, and reject
+invalid arguments with the documented status before making any HIP call (so
+these calls never touch a device).  No call here passes valid arguments.
+"""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import exact_tiled_attention_10_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+
+
+def _header_enum():
+    text = open(HEADER).read()
+    return {k: int(v) for k, v in re.findall(r"\b(FA_[A-Z_]+)\s*=\s*(\d+)", text)}
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fa.library_path()):
+        import exact_tiled_attention_10_amd.build as b
+        b.build()
+    return fa.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared_functions()
+    assert set(names) == {"fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_bwd_workspace_size",
+                          "fa_status_string"}
+    for nm in names:
+        assert hasattr(lib, nm), nm
+
+
+def test_status_codes_match_header(lib):
+    enum = _header_enum()
+    for name, val in enum.items():
+        assert getattr(fa, name) == val, name
+        assert fa.fa_status_string(val) not in ("", "unknown status")
+    assert fa.fa_status_string(999) == "unknown status"
+    m = re.search(r"#define FA_MAX_N \(1 << (\d+)\)", open(HEADER).read())
+    assert fa.FA_MAX_N == 1 << int(m.group(1))
+
+
+A = 0x10000          # fake, 16-byte aligned device addresses (never dereferenced)
+MB = 1 << 24
+
+
+def _fwd(lib, q=A, k=A + MB, v=A + 2 * MB, o=A + 3 * MB, lse=A + 4 * MB, B=1, H=2, N=100,
+         d=64, causal=0, scale=0.125, f32=False):
+    fn = lib.fa_fwd_f32 if f32 else lib.fa_fwd
+    return fn(q, k, v, o, lse, B, H, N, d, causal, scale, None)
+
+
+@pytest.mark.parametrize("f32", [False, True])
+def test_forward_rejects_bad_arguments(lib, f32):
+    assert _fwd(lib, d=32, f32=f32) == fa.FA_ERR_HEADDIM
+    assert _fwd(lib, d=0, f32=f32) == fa.FA_ERR_HEADDIM
+    assert _fwd(lib, N=-1, f32=f32) == fa.FA_ERR_SHAPE
+    assert _fwd(lib, B=-2, f32=f32) == fa.FA_ERR_SHAPE
+    assert _fwd(lib, H=-1, f32=f32) == fa.FA_ERR_SHAPE
+    assert _fwd(lib, N=fa.FA_MAX_N + 1, f32=f32) == fa.FA_ERR_SHAPE
+    assert _fwd(lib, B=1 << 20, H=1 << 12, f32=f32) == fa.FA_ERR_SHAPE
+    assert _fwd(lib, scale=math.nan, f32=f32) == fa.FA_ERR_SCALE
+    assert _fwd(lib, scale=math.inf, f32=f32) == fa.FA_ERR_SCALE
+    assert _fwd(lib, q=None, f32=f32) == fa.FA_ERR_NULL
+    assert _fwd(lib, lse=None, f32=f32) == fa.FA_ERR_NULL
+    assert _fwd(lib, v=A + 2 * MB + 2, f32=f32) == fa.FA_ERR_ALIGN
+    assert _fwd(lib, lse=A + 4 * MB + 4, f32=f32) == fa.FA_ERR_ALIGN
+    assert _fwd(lib, o=A + 16, f32=f32) == fa.FA_ERR_ALIAS           # o overlaps q
+    assert _fwd(lib, lse=A + 3 * MB + 64, f32=f32) == fa.FA_ERR_ALIAS  # lse inside o
+    assert _fwd(lib, o=A + 2 * MB, f32=f32) == fa.FA_ERR_ALIAS       # o is v
+
+
+@pytest.mark.parametrize("f32", [False, True])
+def test_forward_empty_is_noop(lib, f32):
+    # B*H*N == 0 returns OK before any pointer check or HIP call
+    assert _fwd(lib, N=0, q=None, k=None, v=None, o=None, lse=None, f32=f32) == fa.FA_OK
+    assert _fwd(lib, B=0, f32=f32) == fa.FA_OK
+    assert _fwd(lib, H=0, f32=f32) == fa.FA_OK
+
+
+def test_workspace_size(lib):
+    assert lib.fa_bwd_workspace_size(1, 2, 100, 32) == 0
+    assert lib.fa_bwd_workspace_size(1, 2, -1, 64) == 0
+    for (B, H, N, d) in ((1, 2, 100, 64), (4, 16, 2048, 64), (1, 8, 32768, 128)):
+        ws = lib.fa_bwd_workspace_size(B, H, N, d)
+        # at least D (fp32 per row) plus the fp32 dQ accumulator
+        assert ws >= B * H * N * 4 + B * H * N * d * 4
+        assert ws % 16 == 0
+
+
+def _bwd(lib, ws_bytes=None, **kw):
+    B, H, N, d = kw.get("B", 1), kw.get("H", 2), kw.get("N", 100), kw.get("d", 64)
+    ptrs = dict(q=A, k=A + MB, v=A + 2 * MB, o=A + 3 * MB, dout=A + 4 * MB, lse=A + 5 * MB,
+                dq=A + 6 * MB, dk=A + 7 * MB, dv=A + 8 * MB, ws=A + 9 * MB)
+    ptrs.update({k: v for k, v in kw.items() if k in ptrs})
+    if ws_bytes is None:
+        ws_bytes = lib.fa_bwd_workspace_size(1, 2, 100, 64)
+    return lib.fa_bwd(ptrs["q"], ptrs["k"], ptrs["v"], ptrs["o"], ptrs["dout"], ptrs["lse"],
+                      ptrs["dq"], ptrs["dk"], ptrs["dv"], ptrs["ws"], ws_bytes, B, H, N, d,
+                      kw.get("causal", 1), kw.get("scale", 0.125), None)
+
+
+def test_backward_rejects_bad_arguments(lib):
+    assert _bwd(lib, d=96) == fa.FA_ERR_HEADDIM
+    assert _bwd(lib, N=-5) == fa.FA_ERR_SHAPE
+    assert _bwd(lib, scale=math.nan) == fa.FA_ERR_SCALE
+    assert _bwd(lib, dout=None) == fa.FA_ERR_NULL
+    assert _bwd(lib, ws=None) == fa.FA_ERR_NULL
+    assert _bwd(lib, dk=A + 7 * MB + 8) == fa.FA_ERR_ALIGN
+    assert _bwd(lib, ws_bytes=16) == fa.FA_ERR_WORKSPACE
+    assert _bwd(lib, dq=A + 3 * MB) == fa.FA_ERR_ALIAS                # dq is o
+    assert _bwd(lib, dv=A + 6 * MB + 32) == fa.FA_ERR_ALIAS           # dv inside dq
+    assert _bwd(lib, ws=A + 8 * MB + 64) == fa.FA_ERR_ALIAS           # ws inside dv
+    assert _bwd(lib, dk=A + 5 * MB) == fa.FA_ERR_ALIAS                # dk over lse
+    assert _bwd(lib, N=0, q=None, ws=None) == fa.FA_OK
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    """The binding has no fallback: a missing libfa.so raises."""
+    monkeypatch.setattr(fa, "_LIB", None)
+    monkeypatch.setattr(fa, "library_path", lambda: str(tmp_path / "libfa.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        fa.load_library()

@@ -348,3 +348,16 @@ def test_empty_sequence():
     assert o.shape == (1, 2, 0, 8) and lse.shape == (1, 2, 0)
     dq, dk, dv = naive_bwd(z, z, z, z, 1.0)
     assert dq.shape == z.shape
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_sampled_rows_match_full_oracle(causal):
+    """The sampled-rows form used for full-size checks equals the full pass."""
+    from oracle import naive_fwd_rows
+    rng = np.random.default_rng(13)
+    q, k, v = rng.standard_normal((3, 70, 8))
+    o, lse = naive_fwd(q, k, v, 0.5, causal)
+    pos = np.array([0, 3, 31, 32, 69])
+    o_r, l_r = naive_fwd_rows(q[pos], k, v, 0.5, causal, pos)
+    np.testing.assert_allclose(o_r, o[pos], atol=1e-14)
+    np.testing.assert_allclose(l_r, lse[pos], atol=1e-14)
