@@ -23,6 +23,7 @@ import torch
 __all__ = [
     "FAError", "library_path", "load_library",
     "fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_bwd_workspace_size", "fa_status_string",
+    "fa_bwd_preprocess", "fa_bwd_main", "fa_bwd_finalize",
     "forward", "backward", "attention",
     "FA_OK", "FA_ERR_NULL", "FA_ERR_SHAPE", "FA_ERR_HEADDIM", "FA_ERR_ALIGN",
     "FA_ERR_ALIAS", "FA_ERR_SCALE", "FA_ERR_HIP", "FA_ERR_WORKSPACE", "FA_MAX_N",
@@ -76,6 +77,13 @@ def load_library():
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
                            i, i, i, i, i, f, vp]
     lib.fa_bwd.restype = i
+    lib.fa_bwd_preprocess.argtypes = [vp, vp, vp, ctypes.c_size_t, i, i, i, i, vp]
+    lib.fa_bwd_preprocess.restype = i
+    lib.fa_bwd_main.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                                i, i, i, i, i, f, vp]
+    lib.fa_bwd_main.restype = i
+    lib.fa_bwd_finalize.argtypes = [vp, vp, ctypes.c_size_t, i, i, i, i, vp]
+    lib.fa_bwd_finalize.restype = i
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
     _LIB = lib
@@ -170,14 +178,54 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, causal: bool, scale: fl
                   (dk, "dk"), (dv, "dv")):
         _check(t, nm, (B, H, N, d), torch.bfloat16, q.device)
     _check(lse, "lse", (B, H, N), torch.float32, q.device)
-    if workspace.device != q.device or not workspace.is_contiguous():
-        raise ValueError("workspace: must be a contiguous tensor on q's device")
-    nbytes = workspace.numel() * workspace.element_size()
+    nbytes = _ws_bytes(workspace, q.device)
     st = load_library().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
                                _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), nbytes,
                                B, H, N, d, int(bool(causal)), float(scale),
                                _stream_handle(q.device, stream))
     _raise(st, "fa_bwd")
+
+
+def _ws_bytes(workspace, device):
+    if workspace.device != device or not workspace.is_contiguous():
+        raise ValueError("workspace: must be a contiguous tensor on q's device")
+    return workspace.numel() * workspace.element_size()
+
+
+def fa_bwd_preprocess(o, dout, workspace, stream=None) -> None:
+    """Backward stage 1: D = rowsum(dO * O) and a zeroed dQ accumulator."""
+    B, H, N, d = _dims(o)
+    for t, nm in ((o, "o"), (dout, "dout")):
+        _check(t, nm, (B, H, N, d), torch.bfloat16, o.device)
+    st = load_library().fa_bwd_preprocess(_ptr(o), _ptr(dout), _ptr(workspace),
+                                          _ws_bytes(workspace, o.device), B, H, N, d,
+                                          _stream_handle(o.device, stream))
+    _raise(st, "fa_bwd_preprocess")
+
+
+def fa_bwd_main(q, k, v, dout, lse, dk, dv, workspace, causal: bool, scale: float,
+                stream=None) -> None:
+    """Backward stage 2: the key-tile kernel (dK, dV, dQ accumulation)."""
+    B, H, N, d = _dims(q)
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout"), (dk, "dk"), (dv, "dv")):
+        _check(t, nm, (B, H, N, d), torch.bfloat16, q.device)
+    _check(lse, "lse", (B, H, N), torch.float32, q.device)
+    st = load_library().fa_bwd_main(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse),
+                                    _ptr(dk), _ptr(dv), _ptr(workspace),
+                                    _ws_bytes(workspace, q.device), B, H, N, d,
+                                    int(bool(causal)), float(scale),
+                                    _stream_handle(q.device, stream))
+    _raise(st, "fa_bwd_main")
+
+
+def fa_bwd_finalize(dq, workspace, stream=None) -> None:
+    """Backward stage 3: dQ = bf16(accumulator)."""
+    B, H, N, d = _dims(dq)
+    _check(dq, "dq", (B, H, N, d), torch.bfloat16, dq.device)
+    st = load_library().fa_bwd_finalize(_ptr(dq), _ptr(workspace),
+                                        _ws_bytes(workspace, dq.device), B, H, N, d,
+                                        _stream_handle(dq.device, stream))
+    _raise(st, "fa_bwd_finalize")
 
 
 # ---------------------------------------------------------------------------

@@ -37,6 +37,8 @@ int check_common(int B, int H, int N, int d, float scale, size_t* tensor_elems,
   if (bh > INT_MAX) return FA_ERR_SHAPE;
   // grid size: one workgroup per (batch*head, 64-row tile) at most
   if (bh * (((long long)N + 63) / 64) > INT_MAX) return FA_ERR_SHAPE;
+  // every elementwise grid (one thread per 8 features of a row) stays < 2^31 blocks
+  if (bh * (long long)N > (1LL << 34)) return FA_ERR_SHAPE;
   if (!isfinite(scale)) return FA_ERR_SCALE;
   *row_elems = (size_t)bh * (size_t)N;
   *tensor_elems = *row_elems * (size_t)d;
@@ -44,6 +46,17 @@ int check_common(int B, int H, int N, int d, float scale, size_t* tensor_elems,
 }
 
 int from_hip(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
+
+// True if any output overlaps an input or another output.
+bool any_alias(const Range* in, int nin, const Range* out, int nout) {
+  for (int i = 0; i < nout; ++i) {
+    for (int j = 0; j < nin; ++j)
+      if (overlaps(out[i], in[j])) return true;
+    for (int j = i + 1; j < nout; ++j)
+      if (overlaps(out[i], out[j])) return true;
+  }
+  return false;
+}
 
 }  // namespace
 
@@ -60,10 +73,8 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
     return FA_ERR_ALIGN;
   const size_t tb = te * 2;
   const Range in[3] = {range_of(q, tb), range_of(k, tb), range_of(v, tb)};
-  const Range ro = range_of(o, tb), rl = range_of(lse, re * 4);
-  for (const Range& r : in)
-    if (overlaps(r, ro) || overlaps(r, rl)) return FA_ERR_ALIAS;
-  if (overlaps(ro, rl)) return FA_ERR_ALIAS;
+  const Range out[2] = {range_of(o, tb), range_of(lse, re * 4)};
+  if (any_alias(in, 3, out, 2)) return FA_ERR_ALIAS;
   return from_hip(fa::launch_fwd_bf16(q, k, v, o, lse, B * H, N, d, causal != 0, scale, stream));
 }
 
@@ -78,10 +89,8 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
     return FA_ERR_ALIGN;
   const size_t tb = te * 4;
   const Range in[3] = {range_of(q, tb), range_of(k, tb), range_of(v, tb)};
-  const Range ro = range_of(o, tb), rl = range_of(lse, re * 4);
-  for (const Range& r : in)
-    if (overlaps(r, ro) || overlaps(r, rl)) return FA_ERR_ALIAS;
-  if (overlaps(ro, rl)) return FA_ERR_ALIAS;
+  const Range out[2] = {range_of(o, tb), range_of(lse, re * 4)};
+  if (any_alias(in, 3, out, 2)) return FA_ERR_ALIAS;
   return from_hip(fa::launch_fwd_f32(q, k, v, o, lse, B * H, N, d, causal != 0, scale, stream));
 }
 
@@ -112,15 +121,69 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
                        range_of(o, tb),    range_of(dout, tb), range_of(lse, re * 4)};
   const Range out[4] = {range_of(dq, tb), range_of(dk, tb), range_of(dv, tb),
                         range_of(workspace, need)};
-  for (const Range& a : out) {
-    for (const Range& b : in)
-      if (overlaps(a, b)) return FA_ERR_ALIAS;
-  }
-  for (int i = 0; i < 4; ++i)
-    for (int j = i + 1; j < 4; ++j)
-      if (overlaps(out[i], out[j])) return FA_ERR_ALIAS;
-  return from_hip(fa::launch_bwd_bf16(q, k, v, o, dout, lse, dq, dk, dv, workspace, B * H, N, d,
+  if (any_alias(in, 6, out, 4)) return FA_ERR_ALIAS;
+  const int BH = B * H;
+  hipError_t e = fa::launch_bwd_pre(o, dout, workspace, BH, N, d, stream);
+  if (e == hipSuccess)
+    e = fa::launch_bwd_main(q, k, v, dout, lse, dk, dv, workspace, BH, N, d, causal != 0, scale,
+                            stream);
+  if (e == hipSuccess) e = fa::launch_bwd_finalize(dq, workspace, BH, N, d, stream);
+  return from_hip(e);
+}
+
+int fa_bwd_preprocess(const void* o, const void* dout, void* workspace, size_t workspace_bytes,
+                      int B, int H, int N, int d, hipStream_t stream) {
+  size_t te = 0, re = 0;
+  int st = check_common(B, H, N, d, 1.0f, &te, &re);
+  if (st != FA_OK) return st;
+  if (re == 0) return FA_OK;
+  if (!o || !dout || !workspace) return FA_ERR_NULL;
+  if (misaligned(o) || misaligned(dout) || misaligned(workspace)) return FA_ERR_ALIGN;
+  const size_t need = fa::bwd_workspace_bytes(B * H, N, d);
+  if (workspace_bytes < need) return FA_ERR_WORKSPACE;
+  const size_t tb = te * 2;
+  const Range in[2] = {range_of(o, tb), range_of(dout, tb)};
+  const Range out[1] = {range_of(workspace, need)};
+  if (any_alias(in, 2, out, 1)) return FA_ERR_ALIAS;
+  return from_hip(fa::launch_bwd_pre(o, dout, workspace, B * H, N, d, stream));
+}
+
+int fa_bwd_main(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                void* dk, void* dv, void* workspace, size_t workspace_bytes, int B, int H, int N,
+                int d, int causal, float scale, hipStream_t stream) {
+  size_t te = 0, re = 0;
+  int st = check_common(B, H, N, d, scale, &te, &re);
+  if (st != FA_OK) return st;
+  if (re == 0) return FA_OK;
+  if (!q || !k || !v || !dout || !lse || !dk || !dv || !workspace) return FA_ERR_NULL;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(dout) || misaligned(lse) ||
+      misaligned(dk) || misaligned(dv) || misaligned(workspace))
+    return FA_ERR_ALIGN;
+  const size_t need = fa::bwd_workspace_bytes(B * H, N, d);
+  if (workspace_bytes < need) return FA_ERR_WORKSPACE;
+  const size_t tb = te * 2;
+  const Range in[5] = {range_of(q, tb), range_of(k, tb), range_of(v, tb), range_of(dout, tb),
+                       range_of(lse, re * 4)};
+  const Range out[3] = {range_of(dk, tb), range_of(dv, tb), range_of(workspace, need)};
+  if (any_alias(in, 5, out, 3)) return FA_ERR_ALIAS;
+  return from_hip(fa::launch_bwd_main(q, k, v, dout, lse, dk, dv, workspace, B * H, N, d,
                                       causal != 0, scale, stream));
+}
+
+int fa_bwd_finalize(void* dq, const void* workspace, size_t workspace_bytes, int B, int H, int N,
+                    int d, hipStream_t stream) {
+  size_t te = 0, re = 0;
+  int st = check_common(B, H, N, d, 1.0f, &te, &re);
+  if (st != FA_OK) return st;
+  if (re == 0) return FA_OK;
+  if (!dq || !workspace) return FA_ERR_NULL;
+  if (misaligned(dq) || misaligned(workspace)) return FA_ERR_ALIGN;
+  const size_t need = fa::bwd_workspace_bytes(B * H, N, d);
+  if (workspace_bytes < need) return FA_ERR_WORKSPACE;
+  const Range in[1] = {range_of(workspace, need)};
+  const Range out[1] = {range_of(dq, te * 2)};
+  if (any_alias(in, 1, out, 1)) return FA_ERR_ALIAS;
+  return from_hip(fa::launch_bwd_finalize(dq, workspace, B * H, N, d, stream));
 }
 
 const char* fa_status_string(int status) {

@@ -64,6 +64,14 @@ __device__ __forceinline__ float wave_xor32(float x) {
   return __shfl_xor(x, 32, 64);
 }
 
+// Position of a 4-row group inside its 16-row chunk in a transposed operand
+// tile (V^T in the forward, Q^T and dO^T in the backward).  A 32x32 MFMA
+// accumulator gives lane half h rows {4h..4h+3, 8+4h..8+4h+3} of each 16-row
+// chunk in registers t = 0..7; storing the groups in the order 0, 2, 1, 3 puts
+// exactly those 8 rows at positions 8h..8h+7, so the matching A operand is one
+// 16-byte LDS read.
+__device__ __forceinline__ int tr_group_pos(int lg) { return ((lg & 1) << 1) | (lg >> 1); }
+
 // Work-tile order for the forward and backward grids.
 //
 // Workgroups are dispatched round-robin over the 8 XCDs (workgroup i lands on

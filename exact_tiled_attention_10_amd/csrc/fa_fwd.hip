@@ -39,12 +39,6 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kBM = 32 * kWaves;  // queries per workgroup
 
-// Position of a 4-key group inside its 16-key chunk in the V^T tile.  The S^T
-// accumulator gives lane half h keys {4h..4h+3, 8+4h..8+4h+3} of each 16-key
-// chunk in registers t = 0..7; storing groups in the order 0, 2, 1, 3 makes
-// those 8 keys contiguous (positions 8h..8h+7).
-__device__ __forceinline__ int vt_group_pos(int lg) { return ((lg & 1) << 1) | (lg >> 1); }
-
 template <int D, int BN>
 struct FwdBf16Cfg {
   static constexpr int KS = D + 8;          // K tile row stride (elements), +16 B pad
@@ -118,7 +112,7 @@ __device__ __forceinline__ void store_tile_bf16(const TileRegs<D, BN>& r, uint16
     const int bi = i * 256 + tid;
     const int kg = bi % (BN / 4);
     const int dg = bi / (BN / 4);
-    const int kpos = 16 * (kg >> 2) + 4 * vt_group_pos(kg & 3);
+    const int kpos = 16 * (kg >> 2) + 4 * tr_group_pos(kg & 3);
     // rows r = keys 4kg..4kg+3; .x = features (4dg, 4dg+1), .y = (4dg+2, 4dg+3)
     const u32x2* v = r.v[i];
     u32x2 c0 = {pack_lo16(v[0].x, v[1].x), pack_lo16(v[2].x, v[3].x)};

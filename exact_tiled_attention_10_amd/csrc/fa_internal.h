@@ -18,9 +18,12 @@ hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float*
 // kernel (dK, dV, atomic dQ), then dQ conversion.  `ws` holds D (BH*N floats,
 // rounded up to 256 bytes) followed by the fp32 dQ accumulator.
 size_t bwd_workspace_bytes(int BH, int N, int d);
-hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
-                           const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                           void* ws, int BH, int N, int d, bool causal, float scale,
-                           hipStream_t stream);
+hipError_t launch_bwd_pre(const void* o, const void* dout, void* ws, int BH, int N, int d,
+                          hipStream_t stream);
+hipError_t launch_bwd_main(const void* q, const void* k, const void* v, const void* dout,
+                           const float* lse, void* dk, void* dv, void* ws, int BH, int N, int d,
+                           bool causal, float scale, hipStream_t stream);
+hipError_t launch_bwd_finalize(void* dq, const void* ws, int BH, int N, int d,
+                               hipStream_t stream);
 
 }  // namespace fa

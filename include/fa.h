@@ -127,6 +127,30 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
            int causal, float scale, hipStream_t stream);
 
+/*
+ * The three stages fa_bwd runs, in order, on the same stream.  Calling them in
+ * sequence with the same arguments is exactly fa_bwd; they exist for callers
+ * that schedule or time the stages separately.  Each validates like fa_bwd
+ * (its own pointers only) and reads/writes the workspace as documented.
+ *
+ * fa_bwd_preprocess -- D = rowsum(dO * O) into the workspace; zeroes the
+ *                      workspace's fp32 dQ accumulator.
+ * fa_bwd_main       -- the key-tile kernel: recomputes P from q, k, lse,
+ *                      writes dk and dv, and adds scale * dS K into the dQ
+ *                      accumulator (float atomics).  Needs the preprocess
+ *                      stage's workspace contents.
+ * fa_bwd_finalize   -- dq = bf16(dQ accumulator).
+ */
+int fa_bwd_preprocess(const void* o, const void* dout, void* workspace,
+                      size_t workspace_bytes, int B, int H, int N, int d,
+                      hipStream_t stream);
+int fa_bwd_main(const void* q, const void* k, const void* v, const void* dout,
+                const float* lse, void* dk, void* dv, void* workspace,
+                size_t workspace_bytes, int B, int H, int N, int d, int causal,
+                float scale, hipStream_t stream);
+int fa_bwd_finalize(void* dq, const void* workspace, size_t workspace_bytes,
+                    int B, int H, int N, int d, hipStream_t stream);
+
 /* fa_status_string -- static, human-readable text for a status code. */
 const char* fa_status_string(int status);
 

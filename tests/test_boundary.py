@@ -40,7 +40,8 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = _declared_functions()
     assert set(names) == {"fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_bwd_workspace_size",
-                          "fa_status_string"}
+                          "fa_status_string", "fa_bwd_preprocess", "fa_bwd_main",
+                          "fa_bwd_finalize"}
     for nm in names:
         assert hasattr(lib, nm), nm
 
@@ -136,3 +137,26 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(fa, "library_path", lambda: str(tmp_path / "libfa.so"))
     with pytest.raises(RuntimeError, match="missing"):
         fa.load_library()
+
+
+def test_backward_stages_reject_bad_arguments(lib):
+    ws = lib.fa_bwd_workspace_size(1, 2, 100, 64)
+    o, g, w = A, A + MB, A + 9 * MB
+    assert lib.fa_bwd_preprocess(o, g, w, 8, 1, 2, 100, 64, None) == fa.FA_ERR_WORKSPACE
+    assert lib.fa_bwd_preprocess(None, g, w, ws, 1, 2, 100, 64, None) == fa.FA_ERR_NULL
+    assert lib.fa_bwd_preprocess(o, g, o + 64, ws, 1, 2, 100, 64, None) == fa.FA_ERR_ALIAS
+    assert lib.fa_bwd_preprocess(o, g, w, ws, 1, 2, 100, 48, None) == fa.FA_ERR_HEADDIM
+    assert lib.fa_bwd_preprocess(o, g, w, ws, 1, 2, 0, 64, None) == fa.FA_OK
+    mk = lambda **kw: lib.fa_bwd_main(  # noqa: E731
+        kw.get("q", A), A + MB, A + 2 * MB, A + 4 * MB, A + 5 * MB, kw.get("dk", A + 7 * MB),
+        A + 8 * MB, kw.get("ws", w), kw.get("wsb", ws), 1, 2, 100, 64, 1,
+        kw.get("scale", 0.125), None)
+    assert mk(q=None) == fa.FA_ERR_NULL
+    assert mk(wsb=4) == fa.FA_ERR_WORKSPACE
+    assert mk(dk=A + 8 * MB + 16) == fa.FA_ERR_ALIAS        # dk overlaps dv
+    assert mk(ws=A + MB) == fa.FA_ERR_ALIAS                 # workspace over k
+    assert mk(scale=math.inf) == fa.FA_ERR_SCALE
+    assert lib.fa_bwd_finalize(A + 6 * MB, w, 4, 1, 2, 100, 64, None) == fa.FA_ERR_WORKSPACE
+    assert lib.fa_bwd_finalize(None, w, ws, 1, 2, 100, 64, None) == fa.FA_ERR_NULL
+    assert lib.fa_bwd_finalize(w + 16, w, ws, 1, 2, 100, 64, None) == fa.FA_ERR_ALIAS
+    assert lib.fa_bwd_finalize(A + 6 * MB + 2, w, ws, 1, 2, 100, 64, None) == fa.FA_ERR_ALIGN

@@ -1,0 +1,153 @@
+"""GPU parity of the backward pass (fa_bwd) against the float64 oracle.
+
+The GPU backward consumes the GPU forward's O and lse (as in training); the
+oracle differentiates the exact definition (softmax Jacobian) on the float64
+upcast of the same bf16 inputs.
+
+Tolerance: max abs error 2e-2 on dQ, dK and dV.  Cases outside the stated
+workloads whose gradients grow past O(1) (large scales, boosted query rows)
+cannot meet an absolute 2e-2 with ANY bf16 output: rounding the exact gradient
+to bf16 already moves it by up to half a unit in the last place, 2^-9 |x|
+(0.027 at |x| = 10).  For those the bar is one bf16 ulp of the largest
+reference magnitude, max(2e-2, 2^-7 * max|ref|), stated per test.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import exact_tiled_attention_10_amd as fa
+from oracle import naive_bwd
+from workloads import WORKLOADS, make_inputs, workload_inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+
+
+def ulp_tol(ref_arrays):
+    """max(2e-2, one bf16 ulp (2^-7 relative) of the largest |reference|)."""
+    top = max(float(np.max(np.abs(r))) if r.size else 0.0 for r in ref_arrays)
+    return max(TOL, top * 2.0 ** -7)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU on this host")
+    fa.load_library()
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _f64(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def _gpu_fwd_bwd(q, k, v, do, causal, scale, prefill_nan=True):
+    qd, kd, vd, dod = (t.cuda() for t in (q, k, v, do))
+    o, lse = fa.forward(qd, kd, vd, causal, scale)
+    dq = torch.empty_like(qd)
+    dk = torch.empty_like(kd)
+    dv = torch.empty_like(vd)
+    if prefill_nan:
+        for t in (dq, dk, dv):
+            t.fill_(float("nan"))
+    B, H, N, d = q.shape
+    ws = torch.full((fa.fa_bwd_workspace_size(B, H, N, d),), 0xFF, dtype=torch.uint8,
+                    device="cuda")
+    fa.fa_bwd(qd, kd, vd, o, dod, lse, dq, dk, dv, ws, causal, scale)
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+def _compare(got, ref, label, tol=TOL):
+    errs = [float(np.max(np.abs(_f64(g) - r))) if r.size else 0.0 for g, r in zip(got, ref)]
+    _say(f"   {label} max|d dQ|={errs[0]:.3e} |d dK|={errs[1]:.3e} |d dV|={errs[2]:.3e}"
+         f" (tol {tol:.3e})")
+    for g in got:
+        assert torch.isfinite(g).all()
+    assert max(errs) <= tol, errs
+    return errs
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 2, 63, 65, 127, 129, 257, 1000])
+def test_bwd_small_and_ragged(N, causal, d):
+    _say(f"[bwd] N={N} d={d} causal={causal}")
+    q, k, v, do = make_inputs(1, 2, N, d, torch.bfloat16, seed=300 + N, with_do=True)
+    scale = 1.0 / math.sqrt(d)
+    got = _gpu_fwd_bwd(q, k, v, do, causal, scale)
+    ref = naive_bwd(_f64(q), _f64(k), _f64(v), _f64(do), scale, causal)
+    _compare(got, ref, f"N={N}")
+
+
+def _heads(w, causal, heads, magnitude_tol=False):
+    q, k, v, do = workload_inputs(w, with_do=True)
+    got = _gpu_fwd_bwd(q, k, v, do, causal, w.scale)
+    worst = 0.0
+    for (b, h) in heads:
+        ref = naive_bwd(_f64(q[b, h]), _f64(k[b, h]), _f64(v[b, h]), _f64(do[b, h]), w.scale,
+                        causal)
+        tol = ulp_tol(ref) if magnitude_tol else TOL
+        errs = _compare([g[b, h] for g in got], ref, f"head ({b},{h})", tol)
+        worst = max(worst, max(errs))
+    _say(f"   worst over {len(heads)} heads: {worst:.3e}")
+
+
+def test_train_step_workload_every_head():
+    """Training-step workload (4 x 16 x 2048 x 64, causal) in the bench's launch
+    configuration: every element of every head against the oracle, 2e-2."""
+    w = WORKLOADS["train_step_n2048"]
+    _say(f"[{w.name}]")
+    _heads(w, True, [(b, h) for b in range(w.B) for h in range(w.H)])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_gpt2_medium_shape_backward_sampled_heads(causal):
+    """Backward at the GPT-2-medium shape with every 7th query row x4 (larger
+    gradients, up to |dK| ~ 8): one bf16 ulp of the largest magnitude."""
+    w = WORKLOADS["gpt2_medium_n1024"]
+    _say(f"[{w.name} backward] causal={causal}")
+    _heads(w, causal, [(0, 0), (3, 7), (7, 15)], magnitude_tol=True)
+
+
+def test_llama8b_shape_backward_sampled_heads():
+    w = WORKLOADS["llama8b_n4096"]
+    _say(f"[{w.name} backward]")
+    _heads(w, True, [(0, 3), (0, 30)])
+
+
+@pytest.mark.parametrize("scale", [-0.2, 0.0, 0.5])
+def test_bwd_unusual_scales(scale):
+    """Negative, zero and large scales (gradients up to ~10 at 0.5): one bf16
+    ulp of the largest magnitude."""
+    q, k, v, do = make_inputs(1, 2, 150, 64, torch.bfloat16, seed=17, with_do=True)
+    for causal in (False, True):
+        got = _gpu_fwd_bwd(q, k, v, do, causal, scale)
+        ref = naive_bwd(_f64(q), _f64(k), _f64(v), _f64(do), scale, causal)
+        _compare(got, ref, f"scale={scale} causal={causal}", ulp_tol(ref))
+
+
+def test_bwd_repeatability():
+    """dK and dV have no atomics: bitwise equal across runs.  dQ sums with
+    float atomics, so runs may differ in the last bits only."""
+    q, k, v, do = make_inputs(2, 4, 700, 128, torch.bfloat16, seed=18, with_do=True)
+    a = _gpu_fwd_bwd(q, k, v, do, True, 0.09)
+    b = _gpu_fwd_bwd(q, k, v, do, True, 0.09)
+    assert torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
+    assert (a[0].float() - b[0].float()).abs().max().item() <= 1e-2
+
+
+def test_autograd_function_matches_oracle():
+    q, k, v, do = make_inputs(1, 2, 200, 64, torch.bfloat16, seed=19, with_do=True)
+    qd, kd, vd = (t.cuda().requires_grad_(True) for t in (q, k, v))
+    o = fa.attention(qd, kd, vd, True, 0.125)
+    o.backward(do.cuda())
+    ref = naive_bwd(_f64(q), _f64(k), _f64(v), _f64(do), 0.125, True)
+    _compare([qd.grad, kd.grad, vd.grad], ref, "autograd")
