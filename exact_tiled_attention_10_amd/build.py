@@ -28,6 +28,8 @@ HIPCC_FLAGS = [
     # no packed fp32 VALU (v_pk_*_f32) anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
+    # the LDS DMA helper clobbers m0 in inline assembly on purpose (fa_common.h)
+    "-Wno-inline-asm",
 ]
 
 

@@ -18,6 +18,7 @@
 namespace fa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -71,6 +72,76 @@ __device__ __forceinline__ float wave_xor32(float x) {
 // exactly those 8 rows at positions 8h..8h+7, so the matching A operand is one
 // 16-byte LDS read.
 __device__ __forceinline__ int tr_group_pos(int lg) { return ((lg & 1) << 1) | (lg >> 1); }
+
+// ---------------------------------------------------------------------------
+// LDS tiles filled by direct global->LDS DMA.
+//
+// global_load_lds_dwordx4 writes lane i's 16 bytes to LDS base + 16*i, so a
+// wave instruction fills 1 KiB contiguously and rows cannot be padded.  Bank
+// conflicts are avoided with an XOR swizzle instead: inside row r of a tile
+// with CPR 16-byte chunks per row, chunk c is stored at position c ^ swz(r).
+//
+// gfx950's LDS serves 256 bytes (64 banks x 4 B) per cycle: 16 lanes of a
+// ds_read_b128, 32 lanes of a ds_read_b64_tr_b16.  A conflict-free access
+// therefore touches 16 distinct 16-byte slots modulo 256 bytes.  Two swizzles
+// cover the two read patterns the kernels use:
+//   SWZ_ROWS  16 consecutive rows read at the same chunk (a row-operand
+//             read: lane n reads row n).  CPR 16: swz = r % 16;
+//             CPR 8 (two rows per 256 B): swz = (r / 2) % 8.
+//   SWZ_TR    transposing reads: rows r0..r0+3 (r0 % 4 == 0) at four
+//             consecutive chunks 4b..4b+3.  CPR 16: swz = 4 (r % 4);
+//             CPR 8: swz = 4 ((r / 2) % 2).
+// ---------------------------------------------------------------------------
+enum { SWZ_ROWS = 0, SWZ_TR = 1 };
+
+template <int CPR, int KIND>
+__device__ __forceinline__ int swz(int r) {
+  static_assert(CPR == 8 || CPR == 16, "rows of 64 or 128 bf16");
+  if (KIND == SWZ_ROWS) return CPR == 16 ? (r & 15) : ((r >> 1) & 7);
+  return CPR == 16 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2);
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Byte offset of element column `col` (a multiple of 4) of row `row`.
+template <int CPR, int KIND>
+__device__ __forceinline__ int tile_off(int row, int col) {
+  return row * CPR * 16 + (((col >> 3) ^ swz<CPR, KIND>(row)) << 4) + ((col & 7) << 1);
+}
+
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return (unsigned)(uintptr_t)(lds_void*)p;
+}
+
+// One 16-byte global -> LDS DMA per lane: global address gbase + voff (gbase
+// wave-uniform), LDS address lds + 16 * lane (lds wave-uniform).
+//
+// Issued as inline assembly on purpose: through the compiler builtin, the
+// waitcnt pass cannot tell that a DMA into one LDS stage does not alias reads
+// of the other stage, and waits for the in-flight prefetch before every LDS
+// read.  Here completion is the caller's job: wait_vmem() and a workgroup
+// barrier before any wave reads the stage.
+__device__ __forceinline__ void dma16(const void* gbase, unsigned voff, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(gbase), "s"(lds)
+               : "memory", "m0");
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each 16-lane group, the
+// lane 4j + c reads 4 bf16 of "row" j; output lane 4c + e receives element e
+// of rows j = 0..3.  So if lane 4j + c points at row (r0 + j), columns
+// (n0 + 4c .. n0 + 4c + 3), output lane i holds column n0 + i of rows
+// r0 .. r0 + 3: a k-contiguous MFMA operand read from an n-contiguous tile.
+__device__ __forceinline__ u32x2 lds_read_tr16(const void* lds_ptr) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)lds_ptr));
+}
+
+// Wait until all of this wave's vector memory operations (including LDS DMA)
+// have completed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Work-tile order for the forward and backward grids.
 //

@@ -24,11 +24,11 @@
 // each probability costs one FMA and one v_exp_f32.  A negative scale is
 // handled by negating the query fragment (exact in bf16/fp32).
 //
-// K and V tiles are double-buffered in LDS: the next tile's global loads are
-// issued before the current tile's math and written to the other buffer after
-// it, with one barrier per tile.  V is stored transposed (V^T[d][key]) so the
-// PV A-operand is a single 16-byte LDS read per lane; the transpose happens in
-// registers on the way in (4x4 bf16 blocks, v_perm_b32).
+// K and V tiles go from HBM straight into LDS by DMA (global_load_lds), two
+// stages deep: tile kt+1 is in flight while tile kt is computed, with one
+// barrier per tile.  Both tiles stay row-major in LDS (XOR-swizzled against
+// bank conflicts); the V^T operand of the PV product is read with the
+// transposing ds_read_b64_tr_b16, so no register shuffling is needed.
 #include "fa_common.h"
 #include "fa_internal.h"
 
@@ -40,91 +40,32 @@ constexpr int kWaves = 4;
 constexpr int kBM = 32 * kWaves;  // queries per workgroup
 
 template <int D, int BN>
-struct FwdBf16Cfg {
-  static constexpr int KS = D + 8;          // K tile row stride (elements), +16 B pad
-  static constexpr int VS = BN + 8;         // V^T tile row stride (elements), +16 B pad
-  static constexpr int K_ELEMS = BN * KS;
-  static constexpr int V_ELEMS = D * VS;
-  static constexpr int STAGE_ELEMS = K_ELEMS + V_ELEMS;
-  static constexpr int SMEM_BYTES = 2 * STAGE_ELEMS * 2;
-  static constexpr int NSB = BN / 32;       // 32-key sub-blocks per tile
-  static constexpr int NKC = BN / 16;       // 16-key chunks per tile
-  static constexpr int NQC = D / 16;        // 16-feature chunks (QK^T k-steps)
-  static constexpr int NDB = D / 32;        // 32-feature output blocks
-  static constexpr int K_LOADS = BN * D / 8 / 256;      // 16-byte K chunks per thread
-  static constexpr int V_LOADS = (BN / 4) * (D / 4) / 256;  // 4x4 V blocks per thread
-  static_assert(K_LOADS * 256 * 8 == BN * D, "K tile split");
-  static_assert(V_LOADS * 256 * 16 == BN * D, "V tile split");
+struct FwdCfg {
+  static constexpr int CPR = D / 8;                 // 16-byte chunks per tile row
+  static constexpr int TILE_BYTES = BN * D * 2;     // one K or V tile (bf16)
+  static constexpr int STAGE_BYTES = 2 * TILE_BYTES;
+  static constexpr int SMEM_BYTES = 2 * STAGE_BYTES;
+  static constexpr int NSB = BN / 32;               // 32-key sub-blocks per tile
+  static constexpr int NKC = BN / 16;               // 16-key chunks per tile
+  static constexpr int NQC = D / 16;                // 16-feature chunks (QK^T k-steps)
+  static constexpr int NDB = D / 32;                // 32-feature output blocks
+  static constexpr int DMA = TILE_BYTES / 16 / 256; // 16-byte DMAs per thread per tensor
+  static constexpr int ROW_BYTES = CPR * 16;
+  static_assert(DMA * 256 * 16 == TILE_BYTES, "tile split");
 };
 
-template <int D, int BN>
-struct TileRegs {
-  u32x4 k[FwdBf16Cfg<D, BN>::K_LOADS];
-  u32x2 v[FwdBf16Cfg<D, BN>::V_LOADS][4];
-};
-
-template <int D, int BN>
-__device__ __forceinline__ void load_tile_bf16(TileRegs<D, BN>& r, const uint16_t* __restrict__ Kh,
-                                               const uint16_t* __restrict__ Vh, int k0, int N,
-                                               int tid) {
-  using C = FwdBf16Cfg<D, BN>;
-#pragma unroll
-  for (int i = 0; i < C::K_LOADS; ++i) {
-    const int ci = i * 256 + tid;
-    const int row = ci / (D / 8);
-    const int col = (ci % (D / 8)) * 8;
-    const int key = k0 + row;
-    if (key < N)
-      r.k[i] = *reinterpret_cast<const u32x4*>(Kh + (size_t)key * D + col);
-    else
-      r.k[i] = u32x4{0u, 0u, 0u, 0u};
-  }
-#pragma unroll
-  for (int i = 0; i < C::V_LOADS; ++i) {
-    const int bi = i * 256 + tid;
-    const int kg = bi % (BN / 4);
-    const int dg = bi / (BN / 4);
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int key = k0 + 4 * kg + rr;
-      if (key < N)
-        r.v[i][rr] = *reinterpret_cast<const u32x2*>(Vh + (size_t)key * D + 4 * dg);
-      else
-        r.v[i][rr] = u32x2{0u, 0u};
-    }
-  }
-}
-
-template <int D, int BN>
-__device__ __forceinline__ void store_tile_bf16(const TileRegs<D, BN>& r, uint16_t* stage, int tid) {
-  using C = FwdBf16Cfg<D, BN>;
-  uint16_t* ks = stage;
-  uint16_t* vs = stage + C::K_ELEMS;
-#pragma unroll
-  for (int i = 0; i < C::K_LOADS; ++i) {
-    const int ci = i * 256 + tid;
-    const int row = ci / (D / 8);
-    const int col = (ci % (D / 8)) * 8;
-    *reinterpret_cast<u32x4*>(ks + row * C::KS + col) = r.k[i];
-  }
-#pragma unroll
-  for (int i = 0; i < C::V_LOADS; ++i) {
-    const int bi = i * 256 + tid;
-    const int kg = bi % (BN / 4);
-    const int dg = bi / (BN / 4);
-    const int kpos = 16 * (kg >> 2) + 4 * tr_group_pos(kg & 3);
-    // rows r = keys 4kg..4kg+3; .x = features (4dg, 4dg+1), .y = (4dg+2, 4dg+3)
-    const u32x2* v = r.v[i];
-    u32x2 c0 = {pack_lo16(v[0].x, v[1].x), pack_lo16(v[2].x, v[3].x)};
-    u32x2 c1 = {pack_hi16(v[0].x, v[1].x), pack_hi16(v[2].x, v[3].x)};
-    u32x2 c2 = {pack_lo16(v[0].y, v[1].y), pack_lo16(v[2].y, v[3].y)};
-    u32x2 c3 = {pack_hi16(v[0].y, v[1].y), pack_hi16(v[2].y, v[3].y)};
-    uint16_t* base = vs + (4 * dg) * C::VS + kpos;
-    *reinterpret_cast<u32x2*>(base + 0 * C::VS) = c0;
-    *reinterpret_cast<u32x2*>(base + 1 * C::VS) = c1;
-    *reinterpret_cast<u32x2*>(base + 2 * C::VS) = c2;
-    *reinterpret_cast<u32x2*>(base + 3 * C::VS) = c3;
-  }
+// Per-lane byte offset (inside one (batch, head) slice, relative to row k0) of
+// the global chunk that lands in this lane's LDS slot of DMA number i.  Rows
+// past N are clamped to row N-1 (finite data; those keys are masked to -inf
+// and their P is 0, so they contribute nothing).
+template <int D, int BN, int KIND>
+__device__ __forceinline__ unsigned dma_src_off(int i, int w, int lane, int k0, int N, bool full) {
+  using C = FwdCfg<D, BN>;
+  const int slot = (i * 4 + w) * 64 + lane;
+  const int row = slot / C::CPR;
+  const int chunk = (slot % C::CPR) ^ swz<C::CPR, KIND>(row);
+  const int src_row = full ? row : min(k0 + row, N - 1) - k0;
+  return (unsigned)((src_row * D + chunk * 8) * 2);
 }
 
 template <int D, int BN, bool CAUSAL>
@@ -132,12 +73,12 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
     int BH, int N, int nqt, float c, int negq) {
-  using C = FwdBf16Cfg<D, BN>;
-  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+  using C = FwdCfg<D, BN>;
+  extern __shared__ __attribute__((aligned(1024))) char smem_raw[];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31;
   const int h = lane >> 5;
 
@@ -145,12 +86,45 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   map_tile(blockIdx.x, BH, nqt, CAUSAL, &bh, &qt);
   const size_t base = (size_t)bh * (size_t)N * D;
   const uint16_t* Qh = Q + base;
-  const uint16_t* Kh = K + base;
-  const uint16_t* Vh = V + base;
+  const char* Kb = reinterpret_cast<const char*>(K + base);
+  const char* Vb = reinterpret_cast<const char*>(V + base);
 
   const int q0 = qt * kBM;
   const int wq0 = q0 + 32 * w;       // this wave's first query
   const int qrow = wq0 + n;          // this lane's query
+
+  const int kend = CAUSAL ? min(N, q0 + kBM) : N;
+  const int nkt = (kend + BN - 1) / BN;
+
+  // DMA bookkeeping: LDS address of this wave's first 1 KiB slot, and the
+  // per-lane source offsets of full tiles (K row-swizzled, V tr-swizzled).
+  // DMA number i covers rows 16i*... further down the tile: with either
+  // swizzle the lane's chunk does not depend on i, so one offset per tensor
+  // plus a uniform stride of 4 KiB per DMA covers the tile.
+  const unsigned lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem_raw)) + w * 1024;
+  const unsigned koff0 = dma_src_off<D, BN, SWZ_ROWS>(0, w, lane, 0, N, true);
+  const unsigned voff0 = dma_src_off<D, BN, SWZ_TR>(0, w, lane, 0, N, true);
+  auto issue = [&](int kt) {
+    const int k0 = kt * BN;
+    const char* kg = Kb + (size_t)k0 * D * 2;
+    const char* vg = Vb + (size_t)k0 * D * 2;
+    const unsigned st = lds0 + (kt & 1) * C::STAGE_BYTES;
+    if (k0 + BN <= N) {
+#pragma unroll
+      for (int i = 0; i < C::DMA; ++i) {
+        dma16(kg + i * 4096, koff0, st + i * 4096);
+        dma16(vg + i * 4096, voff0, st + C::TILE_BYTES + i * 4096);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::DMA; ++i) {
+        dma16(kg, dma_src_off<D, BN, SWZ_ROWS>(i, w, lane, k0, N, false), st + i * 4096);
+        dma16(vg, dma_src_off<D, BN, SWZ_TR>(i, w, lane, k0, N, false),
+              st + C::TILE_BYTES + i * 4096);
+      }
+    }
+  };
+  if (nkt > 0) issue(0);
 
   // Q^T as the B operand: lane holds Q[qrow][16c + 8h .. 16c + 8h + 7].
   bf16x8 qf[C::NQC];
@@ -165,8 +139,19 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     }
   }
 
-  const int kend = CAUSAL ? min(N, q0 + kBM) : N;
-  const int nkt = (kend + BN - 1) / BN;
+  // per-lane LDS operand offsets inside a stage.  K (A operand of S^T): row
+  // 32sb + n, features 16cc + 8h..; the swizzle does not change with sb.
+  int kb[C::NQC];
+#pragma unroll
+  for (int cc = 0; cc < C::NQC; ++cc) kb[cc] = tile_off<C::CPR, SWZ_ROWS>(n, 16 * cc + 8 * h);
+  // V^T (A operand of O^T += V^T P^T) through transposing reads: 16-lane group
+  // g reads key rows 4*(g/2) + j (+16kc, +8 for the second half) and features
+  // 32db + 16*(g%2) + 4*(lane%4); the swizzle does not change with kc.
+  const int vrow0 = 4 * (lane >> 5) + ((lane & 15) >> 2);
+  const int vcol0 = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  int vb[C::NDB];
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db) vb[db] = tile_off<C::CPR, SWZ_TR>(vrow0, 32 * db + vcol0);
 
   f32x16 acc[C::NDB];
 #pragma unroll
@@ -176,20 +161,15 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   float m = kNegInf;   // running max, log2-scaled units
   float lsum = 0.f;    // this lane's share of the running sum
 
-  TileRegs<D, BN> regs;
-  if (nkt > 0) {
-    load_tile_bf16<D, BN>(regs, Kh, Vh, 0, N, tid);
-    store_tile_bf16<D, BN>(regs, smem, tid);
-  }
-  __syncthreads();
-
+  const char* smem_k = smem_raw;
   for (int kt = 0; kt < nkt; ++kt) {
     const int k0 = kt * BN;
-    const bool more = kt + 1 < nkt;
-    if (more) load_tile_bf16<D, BN>(regs, Kh, Vh, k0 + BN, N, tid);
-
-    const uint16_t* ks = smem + (kt & 1) * C::STAGE_ELEMS;
-    const uint16_t* vs = ks + C::K_ELEMS;
+    // tile kt has landed for every lane; every wave is done with tile kt-1
+    wait_vmem();
+    __syncthreads();
+    if (kt + 1 < nkt) issue(kt + 1);
+    const char* ks = smem_k + (kt & 1) * C::STAGE_BYTES;
+    const char* vs = ks + C::TILE_BYTES;
 
     // sub-blocks of 32 keys this wave must compute (wave-uniform)
     int nsb = C::NSB;
@@ -197,88 +177,96 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
       const int lim = wq0 + 31 - k0;          // last visible key offset for the wave
       nsb = lim < 0 ? 0 : min(C::NSB, lim / 32 + 1);
     }
-    if (nsb > 0) {
-      f32x16 s[C::NSB];
-#pragma unroll
-      for (int sb = 0; sb < C::NSB; ++sb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[sb][r] = 0.f;
-        if (sb < nsb) {
-          const uint16_t* krow = ks + (32 * sb + n) * C::KS + 8 * h;
-#pragma unroll
-          for (int cc = 0; cc < C::NQC; ++cc) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + 16 * cc);
-            s[sb] = mfma_32x32x16_bf16(a, qf[cc], s[sb]);
-          }
-        }
-      }
+    if (nsb == 0) continue;
 
-      const bool need_mask = (k0 + BN > N) || (CAUSAL && k0 + BN - 1 > wq0) || (nsb < C::NSB);
-      if (need_mask) {
+    f32x16 s[C::NSB];
 #pragma unroll
-        for (int sb = 0; sb < C::NSB; ++sb)
+    for (int sb = 0; sb < C::NSB; ++sb) {
+      if (sb < nsb) {
+        bf16x8 a[C::NQC];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + 32 * sb + 8 * (r >> 2) + 4 * h + (r & 3);
-            bool dead = key >= N || sb >= nsb;
-            if (CAUSAL) dead = dead || key > qrow;
-            if (dead) s[sb][r] = kNegInf;
-          }
-      }
-
-      float mx = kNegInf;
+        for (int cc = 0; cc < C::NQC; ++cc)
+          a[cc] = *reinterpret_cast<const bf16x8*>(ks + kb[cc] + sb * 32 * C::ROW_BYTES);
+        const f32x16 zero = {};
+        s[sb] = mfma_32x32x16_bf16(a[0], qf[0], zero);
 #pragma unroll
-      for (int sb = 0; sb < C::NSB; ++sb)
+        for (int cc = 1; cc < C::NQC; ++cc) s[sb] = mfma_32x32x16_bf16(a[cc], qf[cc], s[sb]);
+      } else {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sb][r]);
-      mx = fmaxf(mx, wave_xor32(mx));
-      const float m_new = fmaxf(m, mx * c);
-      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-      const float alpha = exp2f(m - m_use);
-
-      float ps = 0.f;
-      uint32_t pk[C::NSB][8];
-#pragma unroll
-      for (int sb = 0; sb < C::NSB; ++sb)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][r], c, -m_use));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][r + 1], c, -m_use));
-          ps += p0 + p1;
-          pk[sb][r >> 1] = pack_bf16x2(p0, p1);
-        }
-      lsum = lsum * alpha + ps;
-      if (__any(alpha != 1.f)) {
-#pragma unroll
-        for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
-      }
-      m = m_new;
-
-      // O^T += V^T P^T over the computed sub-blocks
-#pragma unroll
-      for (int sb = 0; sb < C::NSB; ++sb) {
-        if (sb < nsb) {
-#pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            const int kc = 2 * sb + half;
-            u32x4 bw = {pk[sb][4 * half + 0], pk[sb][4 * half + 1], pk[sb][4 * half + 2],
-                        pk[sb][4 * half + 3]};
-            const bf16x8 b = __builtin_bit_cast(bf16x8, bw);
-#pragma unroll
-            for (int db = 0; db < C::NDB; ++db) {
-              const bf16x8 a =
-                  *reinterpret_cast<const bf16x8*>(vs + (32 * db + n) * C::VS + 16 * kc + 8 * h);
-              acc[db] = mfma_32x32x16_bf16(a, b, acc[db]);
-            }
-          }
-        }
+        for (int r = 0; r < 16; ++r) s[sb][r] = kNegInf;
       }
     }
 
-    if (more) store_tile_bf16<D, BN>(regs, smem + ((kt + 1) & 1) * C::STAGE_ELEMS, tid);
-    __syncthreads();
+    // mask: register r of sub-block sb holds key k0 + 4h + off(sb, r) with
+    // off = 32sb + 8(r/4) + r%4; it is dead past the lane's limit (its own
+    // query under causal masking, and N - 1)
+    if ((k0 + BN > N) || (CAUSAL && k0 + BN - 1 > wq0)) {
+      int lim = N - 1 - k0 - 4 * h;
+      if (CAUSAL) lim = min(lim, qrow - k0 - 4 * h);
+#pragma unroll
+      for (int sb = 0; sb < C::NSB; ++sb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int off = 32 * sb + 8 * (r >> 2) + (r & 3);
+          s[sb][r] = off > lim ? kNegInf : s[sb][r];
+        }
+    }
+
+    float mx = kNegInf;
+#pragma unroll
+    for (int sb = 0; sb < C::NSB; ++sb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sb][r]);
+    mx = fmaxf(mx, wave_xor32(mx));
+    const float m_new = fmaxf(m, mx * c);
+    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+    const float alpha = exp2f(m - m_use);
+
+    // P = exp2(s*c - m), summed in fp32 (the saved lse needs the unrounded
+    // sum: rounding each p to bf16 first moves ln(l) by up to 2^-9 on short
+    // rows), then rounded to bf16 for the PV product
+    uint32_t pk[C::NSB][8];
+    float ps = 0.f;
+#pragma unroll
+    for (int sb = 0; sb < C::NSB; ++sb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][r], c, -m_use));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][r + 1], c, -m_use));
+        pk[sb][r >> 1] = pack_bf16x2(p0, p1);
+        ps += p0 + p1;
+      }
+    lsum = lsum * alpha + ps;
+    if (__any(alpha != 1.f)) {
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+    }
+    m = m_new;
+
+    // O^T += V^T P^T over the computed sub-blocks
+#pragma unroll
+    for (int sb = 0; sb < C::NSB; ++sb) {
+      if (sb < nsb) {
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int kc = 2 * sb + half;
+          const bf16x8 b = __builtin_bit_cast(
+              bf16x8, u32x4{pk[sb][4 * half + 0], pk[sb][4 * half + 1], pk[sb][4 * half + 2],
+                            pk[sb][4 * half + 3]});
+          bf16x8 a[C::NDB];
+#pragma unroll
+          for (int db = 0; db < C::NDB; ++db) {
+            const u32x2 lo = lds_read_tr16(vs + vb[db] + (16 * kc) * C::ROW_BYTES);
+            const u32x2 hi = lds_read_tr16(vs + vb[db] + (16 * kc + 8) * C::ROW_BYTES);
+            a[db] = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+          }
+#pragma unroll
+          for (int db = 0; db < C::NDB; ++db) acc[db] = mfma_32x32x16_bf16(a[db], b, acc[db]);
+        }
+      }
+    }
   }
 
   // epilogue: one deferred division, then O and the log-sum-exp
@@ -490,7 +478,7 @@ inline void split_scale(float scale, float* c, int* negq) {
 template <int D, int BN, bool CAUSAL>
 hipError_t launch_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
                        int N, float scale, hipStream_t stream) {
-  using C = FwdBf16Cfg<D, BN>;
+  using C = FwdCfg<D, BN>;
   const int nqt = (N + kBM - 1) / kBM;
   float c;
   int negq;
