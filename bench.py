@@ -85,10 +85,10 @@ def run_step_bench(steps: int, warmup: int):
         fa.fa_fwd(q, k, v, o, lse, causal, w.scale)
         if ev is not None:
             ev[1].record(stream)
-        fa.fa_bwd_preprocess(o, do, ws)
+        fa.fa_bwd_preprocess(o, do, lse, ws)
         if ev is not None:
             ev[2].record(stream)
-        fa.fa_bwd_main(q, k, v, do, lse, dk, dv, ws, causal, w.scale)
+        fa.fa_bwd_main(q, k, v, do, dk, dv, ws, causal, w.scale)
         if ev is not None:
             ev[3].record(stream)
         fa.fa_bwd_finalize(dq, ws)

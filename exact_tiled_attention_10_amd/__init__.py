@@ -77,9 +77,9 @@ def load_library():
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
                            i, i, i, i, i, f, vp]
     lib.fa_bwd.restype = i
-    lib.fa_bwd_preprocess.argtypes = [vp, vp, vp, ctypes.c_size_t, i, i, i, i, vp]
+    lib.fa_bwd_preprocess.argtypes = [vp, vp, vp, vp, ctypes.c_size_t, i, i, i, i, vp]
     lib.fa_bwd_preprocess.restype = i
-    lib.fa_bwd_main.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+    lib.fa_bwd_main.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
                                 i, i, i, i, i, f, vp]
     lib.fa_bwd_main.restype = i
     lib.fa_bwd_finalize.argtypes = [vp, vp, ctypes.c_size_t, i, i, i, i, vp]
@@ -192,25 +192,25 @@ def _ws_bytes(workspace, device):
     return workspace.numel() * workspace.element_size()
 
 
-def fa_bwd_preprocess(o, dout, workspace, stream=None) -> None:
-    """Backward stage 1: D = rowsum(dO * O) and a zeroed dQ accumulator."""
+def fa_bwd_preprocess(o, dout, lse, workspace, stream=None) -> None:
+    """Backward stage 1: lse*log2(e), D = rowsum(dO * O), zeroed dQ accumulator."""
     B, H, N, d = _dims(o)
     for t, nm in ((o, "o"), (dout, "dout")):
         _check(t, nm, (B, H, N, d), torch.bfloat16, o.device)
-    st = load_library().fa_bwd_preprocess(_ptr(o), _ptr(dout), _ptr(workspace),
+    _check(lse, "lse", (B, H, N), torch.float32, o.device)
+    st = load_library().fa_bwd_preprocess(_ptr(o), _ptr(dout), _ptr(lse), _ptr(workspace),
                                           _ws_bytes(workspace, o.device), B, H, N, d,
                                           _stream_handle(o.device, stream))
     _raise(st, "fa_bwd_preprocess")
 
 
-def fa_bwd_main(q, k, v, dout, lse, dk, dv, workspace, causal: bool, scale: float,
+def fa_bwd_main(q, k, v, dout, dk, dv, workspace, causal: bool, scale: float,
                 stream=None) -> None:
     """Backward stage 2: the key-tile kernel (dK, dV, dQ accumulation)."""
     B, H, N, d = _dims(q)
     for t, nm in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout"), (dk, "dk"), (dv, "dv")):
         _check(t, nm, (B, H, N, d), torch.bfloat16, q.device)
-    _check(lse, "lse", (B, H, N), torch.float32, q.device)
-    st = load_library().fa_bwd_main(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse),
+    st = load_library().fa_bwd_main(_ptr(q), _ptr(k), _ptr(v), _ptr(dout),
                                     _ptr(dk), _ptr(dv), _ptr(workspace),
                                     _ws_bytes(workspace, q.device), B, H, N, d,
                                     int(bool(causal)), float(scale),

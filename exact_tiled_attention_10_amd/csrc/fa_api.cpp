@@ -123,51 +123,51 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
                         range_of(workspace, need)};
   if (any_alias(in, 6, out, 4)) return FA_ERR_ALIAS;
   const int BH = B * H;
-  hipError_t e = fa::launch_bwd_pre(o, dout, workspace, BH, N, d, stream);
+  hipError_t e = fa::launch_bwd_pre(o, dout, lse, workspace, BH, N, d, stream);
   if (e == hipSuccess)
-    e = fa::launch_bwd_main(q, k, v, dout, lse, dk, dv, workspace, BH, N, d, causal != 0, scale,
+    e = fa::launch_bwd_main(q, k, v, dout, dk, dv, workspace, BH, N, d, causal != 0, scale,
                             stream);
   if (e == hipSuccess) e = fa::launch_bwd_finalize(dq, workspace, BH, N, d, stream);
   return from_hip(e);
 }
 
-int fa_bwd_preprocess(const void* o, const void* dout, void* workspace, size_t workspace_bytes,
-                      int B, int H, int N, int d, hipStream_t stream) {
+int fa_bwd_preprocess(const void* o, const void* dout, const float* lse, void* workspace,
+                      size_t workspace_bytes, int B, int H, int N, int d, hipStream_t stream) {
   size_t te = 0, re = 0;
   int st = check_common(B, H, N, d, 1.0f, &te, &re);
   if (st != FA_OK) return st;
   if (re == 0) return FA_OK;
-  if (!o || !dout || !workspace) return FA_ERR_NULL;
-  if (misaligned(o) || misaligned(dout) || misaligned(workspace)) return FA_ERR_ALIGN;
-  const size_t need = fa::bwd_workspace_bytes(B * H, N, d);
-  if (workspace_bytes < need) return FA_ERR_WORKSPACE;
-  const size_t tb = te * 2;
-  const Range in[2] = {range_of(o, tb), range_of(dout, tb)};
-  const Range out[1] = {range_of(workspace, need)};
-  if (any_alias(in, 2, out, 1)) return FA_ERR_ALIAS;
-  return from_hip(fa::launch_bwd_pre(o, dout, workspace, B * H, N, d, stream));
-}
-
-int fa_bwd_main(const void* q, const void* k, const void* v, const void* dout, const float* lse,
-                void* dk, void* dv, void* workspace, size_t workspace_bytes, int B, int H, int N,
-                int d, int causal, float scale, hipStream_t stream) {
-  size_t te = 0, re = 0;
-  int st = check_common(B, H, N, d, scale, &te, &re);
-  if (st != FA_OK) return st;
-  if (re == 0) return FA_OK;
-  if (!q || !k || !v || !dout || !lse || !dk || !dv || !workspace) return FA_ERR_NULL;
-  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(dout) || misaligned(lse) ||
-      misaligned(dk) || misaligned(dv) || misaligned(workspace))
+  if (!o || !dout || !lse || !workspace) return FA_ERR_NULL;
+  if (misaligned(o) || misaligned(dout) || misaligned(lse) || misaligned(workspace))
     return FA_ERR_ALIGN;
   const size_t need = fa::bwd_workspace_bytes(B * H, N, d);
   if (workspace_bytes < need) return FA_ERR_WORKSPACE;
   const size_t tb = te * 2;
-  const Range in[5] = {range_of(q, tb), range_of(k, tb), range_of(v, tb), range_of(dout, tb),
-                       range_of(lse, re * 4)};
+  const Range in[3] = {range_of(o, tb), range_of(dout, tb), range_of(lse, re * 4)};
+  const Range out[1] = {range_of(workspace, need)};
+  if (any_alias(in, 3, out, 1)) return FA_ERR_ALIAS;
+  return from_hip(fa::launch_bwd_pre(o, dout, lse, workspace, B * H, N, d, stream));
+}
+
+int fa_bwd_main(const void* q, const void* k, const void* v, const void* dout, void* dk,
+                void* dv, void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                int causal, float scale, hipStream_t stream) {
+  size_t te = 0, re = 0;
+  int st = check_common(B, H, N, d, scale, &te, &re);
+  if (st != FA_OK) return st;
+  if (re == 0) return FA_OK;
+  if (!q || !k || !v || !dout || !dk || !dv || !workspace) return FA_ERR_NULL;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(dout) || misaligned(dk) ||
+      misaligned(dv) || misaligned(workspace))
+    return FA_ERR_ALIGN;
+  const size_t need = fa::bwd_workspace_bytes(B * H, N, d);
+  if (workspace_bytes < need) return FA_ERR_WORKSPACE;
+  const size_t tb = te * 2;
+  const Range in[4] = {range_of(q, tb), range_of(k, tb), range_of(v, tb), range_of(dout, tb)};
   const Range out[3] = {range_of(dk, tb), range_of(dv, tb), range_of(workspace, need)};
-  if (any_alias(in, 5, out, 3)) return FA_ERR_ALIAS;
-  return from_hip(fa::launch_bwd_main(q, k, v, dout, lse, dk, dv, workspace, B * H, N, d,
-                                      causal != 0, scale, stream));
+  if (any_alias(in, 4, out, 3)) return FA_ERR_ALIAS;
+  return from_hip(fa::launch_bwd_main(q, k, v, dout, dk, dv, workspace, B * H, N, d, causal != 0,
+                                      scale, stream));
 }
 
 int fa_bwd_finalize(void* dq, const void* workspace, size_t workspace_bytes, int B, int H, int N,

@@ -4,31 +4,36 @@
 // scratch", Step 4 and Follow-up questions).
 //
 // Three launches on the caller's stream:
-//   1. bwd_pre:   D_i = sum_c dO_ic * O_ic (fp32) and zero the fp32 dQ
+//   1. bwd_pre:   per row, L2 = lse * log2(e) and D = sum_c dO_c * O_c (fp32),
+//                 into a workspace padded to 64 rows per head; zero the fp32 dQ
 //                 accumulator.
-//   2. bwd_main:  one workgroup per 128-key tile of one (batch, head); each of
-//                 the 4 waves owns 32 keys and keeps K, V (as MFMA operands)
-//                 and its dK, dV accumulators in registers for the whole
-//                 kernel.  Query blocks stream past the resident key tile; per
+//   2. bwd_main:  one workgroup per key tile of one (batch, head); each wave
+//                 owns 32 keys and keeps K, V (as MFMA operands) and its dK, dV
+//                 accumulators in registers for the whole kernel.  Blocks of 64
+//                 queries stream past the resident key tile (Q, dO and the
+//                 block's L2 / D arrive in LDS by DMA, two stages deep); per
 //                 block a wave recomputes
 //                   S  = Q K^T                 (MFMA, lane = key)
-//                   P  = exp(scale*S - L)      (L = saved lse; masked -> 0)
+//                   P  = exp(scale*S - lse)    (masked -> 0)
 //                   dV^T += dO^T P             (MFMA)
 //                   dP = dO V^T                (MFMA)
 //                   dS = P * (dP - D)
 //                   dK^T += Q^T dS             (MFMA)
-//                 then dS goes through LDS so that each wave can form one
-//                 32x32 block of dQ = dS K over all 128 keys (MFMA, K^T kept
-//                 in LDS) and add it, times scale, into the fp32 accumulator
-//                 with hardware float atomics.  Query blocks wholly before the
-//                 key tile are skipped under causal masking ("LLM Architecture
-//                 Refresh [3]", section 7).
+//                 and writes dS (bf16) to LDS.  At the start of the next
+//                 iteration each wave forms a 32x32 block of dQ = dS K from the
+//                 previous block's dS (double-buffered) and the key tile in LDS,
+//                 and adds it, times scale, into the fp32 accumulator with
+//                 hardware float atomics -- a whole iteration of work then hides
+//                 the atomics' latency, and one barrier per block suffices.
+//                 Query blocks wholly before the key tile are skipped under
+//                 causal masking ("LLM Architecture Refresh [3]", section 7).
 //   3. bwd_dq:    dQ = bf16(accumulator).
 //
-// The P and dS registers of the S / dP accumulators are already in the
-// B-operand layout for dV^T and dK^T (keys across lanes, queries across
-// registers); the matching A operands (dO^T, Q^T) are stored transposed in
-// LDS in the same query order, exactly as V^T in the forward.
+// The P and dS registers of the S / dP accumulators are already the B
+// operands of dV^T and dK^T (keys across lanes, queries across registers).
+// Every transposed A/B operand (dO^T, Q^T, K^T, dS with queries across lanes)
+// is read from a row-major LDS tile with ds_read_b64_tr_b16; no tile is ever
+// transposed in registers.
 #include "fa_common.h"
 #include "fa_internal.h"
 
@@ -36,29 +41,38 @@ namespace fa {
 
 namespace {
 
-constexpr int kBKN = 128;  // keys per workgroup (4 waves x 32)
+constexpr int kBQ = 64;  // queries per streamed block
+
+inline size_t round256(size_t b) { return (b + 255) / 256 * 256; }
+inline int pad_rows(int N) { return (N + kBQ - 1) / kBQ * kBQ; }
 
 // ---------------------------------------------------------------------------
-// 1. D = rowsum(dO * O); zero the dQ accumulator
+// 1. L2 = lse*log2(e), D = rowsum(dO * O); zero the dQ accumulator
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict__ O,
                                                       const uint16_t* __restrict__ dO,
+                                                      const float* __restrict__ LSE,
+                                                      float* __restrict__ L2,
                                                       float* __restrict__ Dv,
-                                                      float* __restrict__ dQacc, size_t rows) {
+                                                      float* __restrict__ dQacc, int N, int Npad,
+                                                      size_t prow) {
   constexpr int TPR = D / 8;  // threads per row, 8 features each
   const size_t gid = (size_t)blockIdx.x * 256 + threadIdx.x;
-  const size_t row = gid / TPR;
+  const size_t prow_id = gid / TPR;      // padded row index over all heads
   const int part = (int)(gid % TPR);
   float acc = 0.f;
-  if (row < rows) {
-    const size_t off = row * D + part * 8;
+  const size_t bh = prow_id / Npad;
+  const int i = (int)(prow_id - bh * Npad);
+  const bool live = prow_id < prow && i < N;
+  if (live) {
+    const size_t off = (bh * N + i) * D + part * 8;
     const u32x4 a = *reinterpret_cast<const u32x4*>(O + off);
     const u32x4 b = *reinterpret_cast<const u32x4*>(dO + off);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc += bf16_bits_to_float(a[i] & 0xffffu) * bf16_bits_to_float(b[i] & 0xffffu);
-      acc += bf16_bits_to_float(a[i] >> 16) * bf16_bits_to_float(b[i] >> 16);
+    for (int k = 0; k < 4; ++k) {
+      acc += bf16_bits_to_float(a[k] & 0xffffu) * bf16_bits_to_float(b[k] & 0xffffu);
+      acc += bf16_bits_to_float(a[k] >> 16) * bf16_bits_to_float(b[k] >> 16);
     }
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
     *reinterpret_cast<f32x4*>(dQacc + off) = z;
@@ -66,7 +80,10 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
   }
 #pragma unroll
   for (int s = TPR / 2; s >= 1; s >>= 1) acc += __shfl_xor(acc, s, 64);
-  if (row < rows && part == 0) Dv[row] = acc;
+  if (prow_id < prow && part == 0) {
+    Dv[prow_id] = live ? acc : 0.f;
+    L2[prow_id] = live ? LSE[bh * N + i] * kLog2e : 0.f;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -88,138 +105,103 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(const float* __restrict__ d
 // ---------------------------------------------------------------------------
 template <int D>
 struct BwdCfg {
-  static constexpr int BQ = D == 128 ? 32 : 64;   // queries per streamed block
-  static constexpr int NQS = BQ / 32;             // 32-query sub-blocks
-  static constexpr int RS = D + 8;                // Q / dO row stride (elements)
-  static constexpr int TS = BQ + 8;               // Q^T / dO^T row stride
-  static constexpr int KTS = kBKN + 8;            // K^T row stride
-  static constexpr int DSS = kBKN + 8;            // dS row stride
+  static constexpr int WAVES = D == 64 ? 8 : 4;   // d=64: 2 waves/SIMD; d=128: 1
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int KEYS = 32 * WAVES;         // keys per workgroup
+  static constexpr int CPRD = D / 8;              // 16-byte chunks per Q / dO / K row
+  static constexpr int CPRQ = kBQ / 8;            // 16-byte chunks per dS row
+  static constexpr int RBD = CPRD * 16;           // bytes per Q / dO / K row
+  static constexpr int RBQ = CPRQ * 16;           // bytes per dS row
+  static constexpr int NQS = kBQ / 32;            // 32-query sub-blocks
   static constexpr int NDC = D / 16;              // 16-feature chunks
   static constexpr int NDB = D / 32;              // 32-feature blocks
-  // LDS layout (bf16 elements)
-  static constexpr int OFF_KT = 0;
-  static constexpr int OFF_Q = OFF_KT + D * KTS;
-  static constexpr int OFF_QT = OFF_Q + BQ * RS;
-  static constexpr int OFF_DO = OFF_QT + D * TS;
-  static constexpr int OFF_DOT = OFF_DO + BQ * RS;
-  static constexpr int OFF_DS = OFF_DOT + D * TS;
-  static constexpr int OFF_STAT = OFF_DS + BQ * DSS;   // 2*BQ floats (lse2, D)
-  static constexpr int SMEM_BYTES = OFF_STAT * 2 + 2 * BQ * 4;
-  // 4x4 blocks of one [BQ, D] tile per thread
-  static constexpr int BLK = (BQ / 4) * (D / 4) / 256;
-  static_assert(BLK * 256 * 16 == BQ * D, "query tile split");
-  // waves for dQ: one 32x32 block of [BQ, D] each
-  static_assert(NQS * NDB == 4, "dQ blocks per workgroup");
-  static constexpr int KT_BLK = (kBKN / 4) * (D / 4) / 256;
+  static constexpr int QTILE = kBQ * D * 2;       // Q or dO tile (bytes)
+  static constexpr int STAGE = 2 * QTILE + 2 * kBQ * 4;   // Q, dO, L2, D
+  static constexpr int KTILE = KEYS * D * 2;
+  static constexpr int DSTILE = KEYS * kBQ * 2;
+  static constexpr int OFF_K = 0;
+  static constexpr int OFF_ST = KTILE;                    // two stages
+  static constexpr int OFF_DS = OFF_ST + 2 * STAGE;       // two dS buffers
+  static constexpr int SMEM = OFF_DS + 2 * DSTILE;
+  static constexpr int QDMA = QTILE / 16 / THREADS;       // DMAs per thread per tile
+  static constexpr int KDMA = KTILE / 16 / THREADS;
+  // dQ = dS K: 32x32 output blocks of the [kBQ, D] tile and their owners
+  static constexpr int NBLK = NQS * NDB;
+  static constexpr int KSPLIT = WAVES >= NBLK ? WAVES / NBLK : 1;
+  static constexpr int BPW = WAVES >= NBLK ? 1 : NBLK / WAVES;  // blocks per wave
+  static constexpr int DQKEYS = KEYS / KSPLIT;            // keys per dQ partial
+  static_assert(QDMA * THREADS * 16 == QTILE && KDMA * THREADS * 16 == KTILE, "DMA split");
+  static_assert(SMEM <= 160 * 1024, "LDS budget");
 };
-
-template <int D>
-struct QRegs {
-  u32x2 q[BwdCfg<D>::BLK][4];
-  u32x2 g[BwdCfg<D>::BLK][4];   // dO
-  float lse2, dv;
-};
-
-template <int D>
-__device__ __forceinline__ void load_qblock(QRegs<D>& r, const uint16_t* __restrict__ Qh,
-                                            const uint16_t* __restrict__ dOh,
-                                            const float* __restrict__ lseh,
-                                            const float* __restrict__ Dh, int q0, int N,
-                                            int tid) {
-  using C = BwdCfg<D>;
-#pragma unroll
-  for (int i = 0; i < C::BLK; ++i) {
-    const int bi = i * 256 + tid;
-    const int qg = bi % (C::BQ / 4);
-    const int dg = bi / (C::BQ / 4);
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int qrow = q0 + 4 * qg + rr;
-      if (qrow < N) {
-        r.q[i][rr] = *reinterpret_cast<const u32x2*>(Qh + (size_t)qrow * D + 4 * dg);
-        r.g[i][rr] = *reinterpret_cast<const u32x2*>(dOh + (size_t)qrow * D + 4 * dg);
-      } else {
-        r.q[i][rr] = u32x2{0u, 0u};
-        r.g[i][rr] = u32x2{0u, 0u};
-      }
-    }
-  }
-  r.lse2 = 0.f;
-  r.dv = 0.f;
-  if (tid < C::BQ && q0 + tid < N) {
-    r.lse2 = lseh[q0 + tid] * kLog2e;
-    r.dv = Dh[q0 + tid];
-  }
-}
-
-// Writes one 4x4 block (rows 4g..4g+3, features 4dg..4dg+3) both row-major
-// and transposed (rows permuted by tr_group_pos within 16-row chunks).
-template <int RSTRIDE, int TSTRIDE>
-__device__ __forceinline__ void store_4x4(const u32x2* v, uint16_t* rowmajor, uint16_t* trans,
-                                          int g, int dg) {
-#pragma unroll
-  for (int rr = 0; rr < 4; ++rr)
-    *reinterpret_cast<u32x2*>(rowmajor + (4 * g + rr) * RSTRIDE + 4 * dg) = v[rr];
-  const int pos = 16 * (g >> 2) + 4 * tr_group_pos(g & 3);
-  uint16_t* base = trans + (4 * dg) * TSTRIDE + pos;
-  *reinterpret_cast<u32x2*>(base + 0 * TSTRIDE) =
-      u32x2{pack_lo16(v[0].x, v[1].x), pack_lo16(v[2].x, v[3].x)};
-  *reinterpret_cast<u32x2*>(base + 1 * TSTRIDE) =
-      u32x2{pack_hi16(v[0].x, v[1].x), pack_hi16(v[2].x, v[3].x)};
-  *reinterpret_cast<u32x2*>(base + 2 * TSTRIDE) =
-      u32x2{pack_lo16(v[0].y, v[1].y), pack_lo16(v[2].y, v[3].y)};
-  *reinterpret_cast<u32x2*>(base + 3 * TSTRIDE) =
-      u32x2{pack_hi16(v[0].y, v[1].y), pack_hi16(v[2].y, v[3].y)};
-}
-
-template <int D>
-__device__ __forceinline__ void store_qblock(const QRegs<D>& r, uint16_t* smem, int tid) {
-  using C = BwdCfg<D>;
-#pragma unroll
-  for (int i = 0; i < C::BLK; ++i) {
-    const int bi = i * 256 + tid;
-    const int qg = bi % (C::BQ / 4);
-    const int dg = bi / (C::BQ / 4);
-    store_4x4<C::RS, C::TS>(r.q[i], smem + C::OFF_Q, smem + C::OFF_QT, qg, dg);
-    store_4x4<C::RS, C::TS>(r.g[i], smem + C::OFF_DO, smem + C::OFF_DOT, qg, dg);
-  }
-  float* stat = reinterpret_cast<float*>(smem + C::OFF_STAT);
-  if (tid < C::BQ) {
-    stat[tid] = r.lse2;
-    stat[C::BQ + tid] = r.dv;
-  }
-}
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void bwd_main_kernel(
+__global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_main_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-    const float* __restrict__ LSE, const float* __restrict__ Dv, float* __restrict__ dQacc,
-    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int BH, int N, int nkt, float scale,
-    float c2) {
+    const float* __restrict__ L2, const float* __restrict__ Dv, float* __restrict__ dQacc,
+    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int BH, int N, int Npad, int nkt,
+    float scale, float c2) {
   using C = BwdCfg<D>;
-  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31;
   const int h = lane >> 5;
 
   int bh, kt;
   map_tile(blockIdx.x, BH, nkt, false, &bh, &kt);
   const size_t base = (size_t)bh * (size_t)N * D;
-  const uint16_t* Qh = Q + base;
-  const uint16_t* Kh = K + base;
-  const uint16_t* Vh = V + base;
-  const uint16_t* dOh = dO + base;
-  const float* lseh = LSE + (size_t)bh * N;
-  const float* Dh = Dv + (size_t)bh * N;
+  const char* Qb = reinterpret_cast<const char*>(Q + base);
+  const char* Kb = reinterpret_cast<const char*>(K + base);
+  const char* Vb = reinterpret_cast<const char*>(V + base);
+  const char* dOb = reinterpret_cast<const char*>(dO + base);
+  const float* L2h = L2 + (size_t)bh * Npad;
+  const float* Dh = Dv + (size_t)bh * Npad;
   float* dQh = dQacc + base;
 
-  const int k0 = kt * kBKN;
+  const int k0 = kt * C::KEYS;
   const int wk0 = k0 + 32 * w;   // this wave's first key
   const int key = wk0 + n;       // this lane's key
+  const unsigned lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem));
+
+  // key tile (row-major, transposing-read swizzle) for the K^T operand of dQ
+#pragma unroll
+  for (int j = 0; j < C::KDMA; ++j) {
+    const int slot = (j * C::WAVES + w) * 64 + lane;
+    const int row = slot / C::CPRD;
+    const int chunk = (slot % C::CPRD) ^ swz<C::CPRD, SWZ_TR>(row);
+    const int src = min(k0 + row, N - 1);
+    dma16(Kb, (unsigned)((src * D + chunk * 8) * 2), lds0 + C::OFF_K + (j * C::WAVES + w) * 1024);
+  }
+
+  const int nqb = (N + kBQ - 1) / kBQ;
+  const int qb0 = CAUSAL ? k0 / kBQ : 0;
+  const int nit = nqb - qb0;
+
+  // DMA of query block qb0 + it (Q, dO rows clamped to N-1; L2 and D padded)
+  auto issue = [&](int it) {
+    const int q0 = (qb0 + it) * kBQ;
+    const unsigned st = lds0 + C::OFF_ST + (it & 1) * C::STAGE;
+#pragma unroll
+    for (int j = 0; j < C::QDMA; ++j) {
+      const int slot = (j * C::WAVES + w) * 64 + lane;
+      const int row = slot / C::CPRD;
+      const int chunk = (slot % C::CPRD) ^ swz<C::CPRD, SWZ_BOTH>(row);
+      const int src = min(q0 + row, N - 1);
+      const unsigned off = (unsigned)((src * D + chunk * 8) * 2);
+      dma16(Qb, off, st + (j * C::WAVES + w) * 1024);
+      dma16(dOb, off, st + C::QTILE + (j * C::WAVES + w) * 1024);
+    }
+    if (w == 0) {
+      if (lane < 16)
+        dma16(L2h + q0, lane * 16, st + 2 * C::QTILE);
+      else if (lane < 32)
+        dma16(Dh + q0, (lane - 16) * 16, st + 2 * C::QTILE);
+    }
+  };
+  issue(0);
 
   // K and V as B operands (lane = key, 8 consecutive features per chunk)
   bf16x8 kf[C::NDC], vf[C::NDC];
@@ -227,35 +209,32 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
   for (int cc = 0; cc < C::NDC; ++cc) {
     u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
     if (key < N) {
-      a = *reinterpret_cast<const u32x4*>(Kh + (size_t)key * D + 16 * cc + 8 * h);
-      b = *reinterpret_cast<const u32x4*>(Vh + (size_t)key * D + 16 * cc + 8 * h);
+      a = *reinterpret_cast<const u32x4*>(Kb + ((size_t)key * D + 16 * cc + 8 * h) * 2);
+      b = *reinterpret_cast<const u32x4*>(Vb + ((size_t)key * D + 16 * cc + 8 * h) * 2);
     }
     kf[cc] = __builtin_bit_cast(bf16x8, a);
     vf[cc] = __builtin_bit_cast(bf16x8, b);
   }
-  // K^T of the whole 128-key tile into LDS (natural key order) for dQ
+
+  // per-lane LDS offsets
+  // row-operand reads of Q / dO (A of S and dP): row 32qs + n, features 16cc + 8h
+  int qro[C::NDC];
 #pragma unroll
-  for (int i = 0; i < C::KT_BLK; ++i) {
-    const int bi = i * 256 + tid;
-    const int kg = bi % (kBKN / 4);
-    const int dg = bi / (kBKN / 4);
-    u32x2 v4[4];
+  for (int cc = 0; cc < C::NDC; ++cc) qro[cc] = tile_off<C::CPRD, SWZ_BOTH>(n, 16 * cc + 8 * h);
+  // transposing reads: 16-lane group g reads rows 4*(g/2) + j (+8 for the
+  // second read) and columns 16*(g%2) + 4*(lane%4) of a 32-column block
+  const int trow = 4 * (lane >> 5) + ((lane & 15) >> 2);
+  const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  int qtr[C::NDB][2];   // dO^T / Q^T A operands (rows = queries)
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int kk = k0 + 4 * kg + rr;
-      v4[rr] = kk < N ? *reinterpret_cast<const u32x2*>(Kh + (size_t)kk * D + 4 * dg)
-                      : u32x2{0u, 0u};
-    }
-    uint16_t* tb = smem + C::OFF_KT + (4 * dg) * C::KTS + 4 * kg;
-    *reinterpret_cast<u32x2*>(tb + 0 * C::KTS) =
-        u32x2{pack_lo16(v4[0].x, v4[1].x), pack_lo16(v4[2].x, v4[3].x)};
-    *reinterpret_cast<u32x2*>(tb + 1 * C::KTS) =
-        u32x2{pack_hi16(v4[0].x, v4[1].x), pack_hi16(v4[2].x, v4[3].x)};
-    *reinterpret_cast<u32x2*>(tb + 2 * C::KTS) =
-        u32x2{pack_lo16(v4[0].y, v4[1].y), pack_lo16(v4[2].y, v4[3].y)};
-    *reinterpret_cast<u32x2*>(tb + 3 * C::KTS) =
-        u32x2{pack_hi16(v4[0].y, v4[1].y), pack_hi16(v4[2].y, v4[3].y)};
-  }
+  for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+    for (int rd = 0; rd < 2; ++rd)
+      qtr[db][rd] = tile_off<C::CPRD, SWZ_BOTH>(trow + 8 * rd, 32 * db + tcol);
+  // dS writes: row 32w + n (this lane's key), queries 32qs + 8g + 4h .. +3
+  int dsw[C::NQS];
+#pragma unroll
+  for (int qs = 0; qs < C::NQS; ++qs) dsw[qs] = tile_off<C::CPRQ, SWZ_TR>(32 * w + n, 32 * qs + 4 * h);
 
   f32x16 dk[C::NDB], dv[C::NDB];
 #pragma unroll
@@ -266,136 +245,144 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
       dv[db][r] = 0.f;
     }
 
-  const int nqb = (N + C::BQ - 1) / C::BQ;
-  const int qb0 = CAUSAL ? (k0 / C::BQ) : 0;
+  // dQ = dS K for query block it, from dS buffer it & 1
+  auto dq_step = [&](int it) {
+    const int q0 = (qb0 + it) * kBQ;
+    const char* dsb = smem + C::OFF_DS + (it & 1) * C::DSTILE;
+    const char* kt_lds = smem + C::OFF_K;
+#pragma unroll
+    for (int bi = 0; bi < C::BPW; ++bi) {
+      const int blk = C::BPW == 1 ? (w % C::NBLK) : (w * C::BPW + bi);
+      const int kp = C::BPW == 1 ? (w / C::NBLK) : 0;
+      const int qsq = blk / C::NDB;
+      const int dbq = blk % C::NDB;
+      const int qs0 = q0 + 32 * qsq;
+      const int kb0 = kp * C::DQKEYS;          // first key of this partial (tile-relative)
+      int nkc = C::DQKEYS / 16;
+      if (CAUSAL) {
+        const int lim = qs0 + 31 - (k0 + kb0);  // last key offset that can see a query
+        nkc = lim < 0 ? 0 : min(C::DQKEYS / 16, lim / 16 + 1);
+      }
+      if (nkc == 0) continue;
+      const int aoff = tile_off<C::CPRQ, SWZ_TR>(kb0 + trow, 32 * qsq + tcol);
+      const int boff = tile_off<C::CPRD, SWZ_TR>(kb0 + trow, 32 * dbq + tcol);
+      f32x16 acc = {};
+#pragma unroll
+      for (int kc = 0; kc < C::DQKEYS / 16; ++kc) {
+        if (kc < nkc) {
+          const u32x2 a0 = lds_read_tr16(dsb + aoff + (16 * kc) * C::RBQ);
+          const u32x2 a1 = lds_read_tr16(dsb + aoff + (16 * kc + 8) * C::RBQ);
+          const u32x2 b0 = lds_read_tr16(kt_lds + boff + (16 * kc) * C::RBD);
+          const u32x2 b1 = lds_read_tr16(kt_lds + boff + (16 * kc + 8) * C::RBD);
+          acc = mfma_32x32x16_bf16(__builtin_bit_cast(bf16x8, u32x4{a0.x, a0.y, a1.x, a1.y}),
+                                   __builtin_bit_cast(bf16x8, u32x4{b0.x, b0.y, b1.x, b1.y}),
+                                   acc);
+        }
+      }
+      // acc: lane = feature 32*dbq + n, registers = queries
+      float* dst = dQh + 32 * dbq + n;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qrow = qs0 + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (qrow < N) unsafeAtomicAdd(dst + (size_t)qrow * D, scale * acc[r]);
+      }
+    }
+  };
 
-  QRegs<D> regs;
-  if (qb0 < nqb) {
-    load_qblock<D>(regs, Qh, dOh, lseh, Dh, qb0 * C::BQ, N, tid);
-    store_qblock<D>(regs, smem, tid);
-  }
-  __syncthreads();
+  for (int it = 0; it < nit; ++it) {
+    const int q0 = (qb0 + it) * kBQ;
+    // stage it landed for every lane; every wave is done with iteration it-1
+    wait_vmem();
+    __syncthreads();
+    if (it + 1 < nit) issue(it + 1);
+    if (it > 0) dq_step(it - 1);
 
-  const uint16_t* sQ = smem + C::OFF_Q;
-  const uint16_t* sQT = smem + C::OFF_QT;
-  const uint16_t* sDO = smem + C::OFF_DO;
-  const uint16_t* sDOT = smem + C::OFF_DOT;
-  uint16_t* sDS = smem + C::OFF_DS;
-  const float* sStat = reinterpret_cast<const float*>(smem + C::OFF_STAT);
+    const char* st = smem + C::OFF_ST + (it & 1) * C::STAGE;
+    const char* sQ = st;
+    const char* sdO = st + C::QTILE;
+    const float* sL2 = reinterpret_cast<const float*>(st + 2 * C::QTILE);
+    const float* sD = sL2 + kBQ;
+    char* dsb = smem + C::OFF_DS + (it & 1) * C::DSTILE;
 
-  for (int qb = qb0; qb < nqb; ++qb) {
-    const int q0 = qb * C::BQ;
-    const bool more = qb + 1 < nqb;
-    if (more) load_qblock<D>(regs, Qh, dOh, lseh, Dh, q0 + C::BQ, N, tid);
-
-    // the wave's keys are all after every query of the block: nothing to do
-    const bool wave_dead = CAUSAL && (wk0 > q0 + C::BQ - 1);
 #pragma unroll
     for (int qs = 0; qs < C::NQS; ++qs) {
       const int qs0 = q0 + 32 * qs;
-      // a 32-query sub-block wholly before the wave's keys contributes nothing
-      const bool sub_dead = wave_dead || (CAUSAL && wk0 > qs0 + 31);
-      uint32_t pk[8], sk[8];
-      if (!sub_dead) {
-        f32x16 s, dp;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          s[r] = 0.f;
-          dp[r] = 0.f;
-        }
-        const uint16_t* qrow = sQ + (32 * qs + n) * C::RS + 8 * h;
-        const uint16_t* grow = sDO + (32 * qs + n) * C::RS + 8 * h;
+      uint32_t sk[8];
+      // the wave's keys all come after every query of the sub-block: dS = 0
+      const bool dead = CAUSAL && (wk0 > qs0 + 31);
+      if (!dead) {
+        const f32x16 zero = {};
+        f32x16 s = zero, dp = zero;
 #pragma unroll
         for (int cc = 0; cc < C::NDC; ++cc) {
-          s = mfma_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(qrow + 16 * cc), kf[cc], s);
-          dp = mfma_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(grow + 16 * cc), vf[cc], dp);
+          const bf16x8 aq = *reinterpret_cast<const bf16x8*>(sQ + qro[cc] + 32 * qs * C::RBD);
+          const bf16x8 ag = *reinterpret_cast<const bf16x8*>(sdO + qro[cc] + 32 * qs * C::RBD);
+          s = mfma_32x32x16_bf16(aq, kf[cc], s);
+          dp = mfma_32x32x16_bf16(ag, vf[cc], dp);
         }
-        // registers r: query 32qs + 8(r/4) + 4h + r%4, key = this lane's key
+        // registers r: query qs0 + 4h + off, off = 8(r/4) + r%4; lane = key
+        f32x4 l2v[4], ddv[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          l2v[g] = *reinterpret_cast<const f32x4*>(sL2 + 32 * qs + 8 * g + 4 * h);
+          ddv[g] = *reinterpret_cast<const f32x4*>(sD + 32 * qs + 8 * g + 4 * h);
+        }
+        const bool need_mask = (qs0 + 31 >= N) || (wk0 + 31 >= N) || (CAUSAL && wk0 + 31 > qs0);
+        int lo = -1, hi = 1 << 30;   // live offsets: lo < off+1 ... i.e. off >= lo, off < hi
+        if (need_mask) {
+          if (CAUSAL) lo = key - qs0 - 4 * h;
+          hi = key < N ? N - qs0 - 4 * h : -(1 << 30);
+        }
+        uint32_t pk[8];
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
           float p2[2], ds2[2];
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
-            const int ql = 32 * qs + 8 * ((r + u) >> 2) + 4 * h + ((r + u) & 3);
-            const int qrow_g = q0 + ql;
-            const float l2 = sStat[ql];
-            const float dd = sStat[C::BQ + ql];
-            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r + u], c2, -l2));
-            bool dead = qrow_g >= N || key >= N;
-            if (CAUSAL) dead = dead || key > qrow_g;
-            p = dead ? 0.f : p;
+            const int rr = r + u;
+            const int off = 8 * (rr >> 2) + (rr & 3);
+            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rr], c2, -l2v[rr >> 2][rr & 3]));
+            if (need_mask) p = (off < lo || off >= hi) ? 0.f : p;
             p2[u] = p;
-            ds2[u] = p * (dp[r + u] - dd);
+            ds2[u] = p * (dp[rr] - ddv[rr >> 2][rr & 3]);
           }
           pk[r >> 1] = pack_bf16x2(p2[0], p2[1]);
           sk[r >> 1] = pack_bf16x2(ds2[0], ds2[1]);
         }
-        // dV^T += dO^T P ; dK^T += Q^T dS   (k = queries of this sub-block)
+        // dV^T += dO^T P ; dK^T += Q^T dS  (k = the 16 queries of one half)
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           const bf16x8 bp = __builtin_bit_cast(
               bf16x8, u32x4{pk[4 * half], pk[4 * half + 1], pk[4 * half + 2], pk[4 * half + 3]});
           const bf16x8 bs = __builtin_bit_cast(
               bf16x8, u32x4{sk[4 * half], sk[4 * half + 1], sk[4 * half + 2], sk[4 * half + 3]});
-          const int col = 32 * qs + 16 * half + 8 * h;
+          const int rowoff = (32 * qs + 16 * half) * C::RBD;
 #pragma unroll
           for (int db = 0; db < C::NDB; ++db) {
-            const bf16x8 ag = *reinterpret_cast<const bf16x8*>(sDOT + (32 * db + n) * C::TS + col);
-            const bf16x8 aq = *reinterpret_cast<const bf16x8*>(sQT + (32 * db + n) * C::TS + col);
-            dv[db] = mfma_32x32x16_bf16(ag, bp, dv[db]);
-            dk[db] = mfma_32x32x16_bf16(aq, bs, dk[db]);
+            const u32x2 g0 = lds_read_tr16(sdO + qtr[db][0] + rowoff);
+            const u32x2 g1 = lds_read_tr16(sdO + qtr[db][1] + rowoff);
+            const u32x2 q0v = lds_read_tr16(sQ + qtr[db][0] + rowoff);
+            const u32x2 q1v = lds_read_tr16(sQ + qtr[db][1] + rowoff);
+            dv[db] = mfma_32x32x16_bf16(__builtin_bit_cast(bf16x8, u32x4{g0.x, g0.y, g1.x, g1.y}),
+                                        bp, dv[db]);
+            dk[db] = mfma_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, u32x4{q0v.x, q0v.y, q1v.x, q1v.y}), bs, dk[db]);
           }
         }
       } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i) sk[i] = 0u;
       }
-      // dS (bf16) into LDS as [query][key of the 128-key tile]
+      // dS (bf16) into LDS as [key][query]: registers 4g..4g+3 are queries
+      // 32qs + 8g + 4h .. +3
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int ql = 32 * qs + 8 * (r >> 2) + 4 * h + (r & 3);
-        const uint16_t bits = (r & 1) ? (uint16_t)(sk[r >> 1] >> 16) : (uint16_t)(sk[r >> 1] & 0xffffu);
-        sDS[ql * C::DSS + 32 * w + n] = bits;
-      }
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<u32x2*>(dsb + dsw[qs] + 16 * g) = u32x2{sk[2 * g], sk[2 * g + 1]};
     }
-    __syncthreads();
-
-    // dQ block of this wave: queries 32*qsq.., features 32*dbq..
-    {
-      const int qsq = w / C::NDB;
-      const int dbq = w % C::NDB;
-      const int qs0 = q0 + 32 * qsq;
-      // keys of the tile after every query of the sub-block contribute nothing
-      int nkc = kBKN / 16;
-      if (CAUSAL) {
-        const int lim = qs0 + 31 - k0;
-        nkc = lim < 0 ? 0 : min(kBKN / 16, lim / 16 + 1);
-      }
-      if (nkc > 0) {
-        f32x16 acc;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-        const uint16_t* arow = sDS + (32 * qsq + n) * C::DSS + 8 * h;
-        const uint16_t* brow = smem + C::OFF_KT + (32 * dbq + n) * C::KTS + 8 * h;
-#pragma unroll
-        for (int kc = 0; kc < kBKN / 16; ++kc) {
-          if (kc < nkc)
-            acc = mfma_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(arow + 16 * kc),
-                                     *reinterpret_cast<const bf16x8*>(brow + 16 * kc), acc);
-        }
-        // acc: lane = feature 32*dbq + n, registers = queries
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int qrow_g = qs0 + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (qrow_g < N)
-            unsafeAtomicAdd(dQh + (size_t)qrow_g * D + 32 * dbq + n, scale * acc[r]);
-        }
-      }
-    }
-
-    if (more) store_qblock<D>(regs, smem, tid);
-    __syncthreads();
   }
+  wait_vmem();
+  __syncthreads();
+  if (nit > 0) dq_step(nit - 1);
 
   // epilogue: dK = scale * dK^T acc, dV = dV^T acc (lane = key, registers = features)
   if (key < N) {
@@ -416,69 +403,77 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(
   }
 }
 
-size_t d_bytes(int BH, int N) { return ((size_t)BH * N * 4 + 255) / 256 * 256; }
+// workspace layout: L2 [BH * Npad], D [BH * Npad], dQ accumulator [BH * N * d]
+struct WsLayout {
+  float* l2;
+  float* dv;
+  float* dq;
+};
+inline WsLayout ws_layout(void* ws, int BH, int N) {
+  char* p = reinterpret_cast<char*>(ws);
+  const size_t rows = round256((size_t)BH * pad_rows(N) * 4);
+  return WsLayout{reinterpret_cast<float*>(p), reinterpret_cast<float*>(p + rows),
+                  reinterpret_cast<float*>(p + 2 * rows)};
+}
 
 template <int D, bool CAUSAL>
 hipError_t launch_main(const void* q, const void* k, const void* v, const void* dout,
-                       const float* lse, const float* Dv, float* dqacc, void* dk, void* dv,
-                       int BH, int N, float scale, hipStream_t stream) {
+                       const WsLayout& w, void* dk, void* dv, int BH, int N, float scale,
+                       hipStream_t stream) {
   using C = BwdCfg<D>;
-  const int nkt = (N + kBKN - 1) / kBKN;
+  const int nkt = (N + C::KEYS - 1) / C::KEYS;
   auto kern = bwd_main_kernel<D, CAUSAL>;
-  hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, C::SMEM_BYTES);
+  hipError_t e =
+      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::SMEM);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(BH * nkt), dim3(256), C::SMEM_BYTES, stream, (const uint16_t*)q,
-                     (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, lse, Dv, dqacc,
-                     (uint16_t*)dk, (uint16_t*)dv, BH, N, nkt, scale, scale * kLog2e);
+  hipLaunchKernelGGL(kern, dim3(BH * nkt), dim3(C::THREADS), C::SMEM, stream, (const uint16_t*)q,
+                     (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, w.l2, w.dv,
+                     w.dq, (uint16_t*)dk, (uint16_t*)dv, BH, N, pad_rows(N), nkt, scale,
+                     scale * kLog2e);
   return hipGetLastError();
 }
 
 }  // namespace
 
 size_t bwd_workspace_bytes(int BH, int N, int d) {
-  return d_bytes(BH, N) + (size_t)BH * N * d * 4;
+  return 2 * round256((size_t)BH * pad_rows(N) * 4) + (size_t)BH * N * d * 4;
 }
 
-// Workspace: D (BH*N floats, rounded up to 256 bytes), then the fp32 dQ
-// accumulator (BH*N*d floats).
-hipError_t launch_bwd_pre(const void* o, const void* dout, void* ws, int BH, int N, int d,
-                          hipStream_t stream) {
-  float* Dv = reinterpret_cast<float*>(ws);
-  float* dqacc = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + d_bytes(BH, N));
-  const size_t rows = (size_t)BH * N;
-  const size_t threads = rows * (d / 8);
+hipError_t launch_bwd_pre(const void* o, const void* dout, const float* lse, void* ws, int BH,
+                          int N, int d, hipStream_t stream) {
+  const WsLayout w = ws_layout(ws, BH, N);
+  const int Npad = pad_rows(N);
+  const size_t prow = (size_t)BH * Npad;
+  const size_t threads = prow * (d / 8);
   const unsigned blocks = (unsigned)((threads + 255) / 256);
   if (d == 128)
     hipLaunchKernelGGL(bwd_pre_kernel<128>, dim3(blocks), dim3(256), 0, stream,
-                       (const uint16_t*)o, (const uint16_t*)dout, Dv, dqacc, rows);
+                       (const uint16_t*)o, (const uint16_t*)dout, lse, w.l2, w.dv, w.dq, N, Npad,
+                       prow);
   else
     hipLaunchKernelGGL(bwd_pre_kernel<64>, dim3(blocks), dim3(256), 0, stream,
-                       (const uint16_t*)o, (const uint16_t*)dout, Dv, dqacc, rows);
+                       (const uint16_t*)o, (const uint16_t*)dout, lse, w.l2, w.dv, w.dq, N, Npad,
+                       prow);
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_main(const void* q, const void* k, const void* v, const void* dout,
-                           const float* lse, void* dk, void* dv, void* ws, int BH, int N, int d,
-                           bool causal, float scale, hipStream_t stream) {
-  const float* Dv = reinterpret_cast<const float*>(ws);
-  float* dqacc = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + d_bytes(BH, N));
+                           void* dk, void* dv, void* ws, int BH, int N, int d, bool causal,
+                           float scale, hipStream_t stream) {
+  const WsLayout w = ws_layout(ws, BH, N);
   if (d == 128)
-    return causal
-               ? launch_main<128, true>(q, k, v, dout, lse, Dv, dqacc, dk, dv, BH, N, scale, stream)
-               : launch_main<128, false>(q, k, v, dout, lse, Dv, dqacc, dk, dv, BH, N, scale, stream);
-  return causal
-             ? launch_main<64, true>(q, k, v, dout, lse, Dv, dqacc, dk, dv, BH, N, scale, stream)
-             : launch_main<64, false>(q, k, v, dout, lse, Dv, dqacc, dk, dv, BH, N, scale, stream);
+    return causal ? launch_main<128, true>(q, k, v, dout, w, dk, dv, BH, N, scale, stream)
+                  : launch_main<128, false>(q, k, v, dout, w, dk, dv, BH, N, scale, stream);
+  return causal ? launch_main<64, true>(q, k, v, dout, w, dk, dv, BH, N, scale, stream)
+                : launch_main<64, false>(q, k, v, dout, w, dk, dv, BH, N, scale, stream);
 }
 
 hipError_t launch_bwd_finalize(void* dq, const void* ws, int BH, int N, int d,
                                hipStream_t stream) {
-  const float* dqacc =
-      reinterpret_cast<const float*>(reinterpret_cast<const char*>(ws) + d_bytes(BH, N));
+  const WsLayout w = ws_layout(const_cast<void*>(ws), BH, N);
   const size_t n8 = (size_t)BH * N * d / 8;
   hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream,
-                     dqacc, (uint16_t*)dq, n8);
+                     w.dq, (uint16_t*)dq, n8);
   return hipGetLastError();
 }
 

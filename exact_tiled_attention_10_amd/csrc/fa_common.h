@@ -91,14 +91,17 @@ __device__ __forceinline__ int tr_group_pos(int lg) { return ((lg & 1) << 1) | (
 //   SWZ_TR    transposing reads: rows r0..r0+3 (r0 % 4 == 0) at four
 //             consecutive chunks 4b..4b+3.  CPR 16: swz = 4 (r % 4);
 //             CPR 8: swz = 4 ((r / 2) % 2).
+//   SWZ_BOTH  both patterns on one tile: CPR 16: swz = 4 (r % 4) + (r / 4) % 4;
+//             CPR 8: swz = 4 ((r / 2) % 2) + (r / 4) % 4.
 // ---------------------------------------------------------------------------
-enum { SWZ_ROWS = 0, SWZ_TR = 1 };
+enum { SWZ_ROWS = 0, SWZ_TR = 1, SWZ_BOTH = 2 };
 
 template <int CPR, int KIND>
 __device__ __forceinline__ int swz(int r) {
   static_assert(CPR == 8 || CPR == 16, "rows of 64 or 128 bf16");
   if (KIND == SWZ_ROWS) return CPR == 16 ? (r & 15) : ((r >> 1) & 7);
-  return CPR == 16 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2);
+  if (KIND == SWZ_TR) return CPR == 16 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2);
+  return CPR == 16 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
 }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));

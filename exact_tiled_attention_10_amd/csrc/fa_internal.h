@@ -14,15 +14,16 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                           int BH, int N, int d, bool causal, float scale, hipStream_t stream);
 
-// Backward: D = rowsum(dO * O) and dQ accumulator zeroing, the key-tile
-// kernel (dK, dV, atomic dQ), then dQ conversion.  `ws` holds D (BH*N floats,
-// rounded up to 256 bytes) followed by the fp32 dQ accumulator.
+// Backward: per-row L2 = lse*log2(e) and D = rowsum(dO * O) plus dQ
+// accumulator zeroing, the key-tile kernel (dK, dV, atomic dQ), then dQ
+// conversion.  `ws` holds L2 and D (BH * roundup(N, 64) floats each, 256-byte
+// aligned regions) followed by the fp32 dQ accumulator (BH * N * d floats).
 size_t bwd_workspace_bytes(int BH, int N, int d);
-hipError_t launch_bwd_pre(const void* o, const void* dout, void* ws, int BH, int N, int d,
-                          hipStream_t stream);
+hipError_t launch_bwd_pre(const void* o, const void* dout, const float* lse, void* ws, int BH,
+                          int N, int d, hipStream_t stream);
 hipError_t launch_bwd_main(const void* q, const void* k, const void* v, const void* dout,
-                           const float* lse, void* dk, void* dv, void* ws, int BH, int N, int d,
-                           bool causal, float scale, hipStream_t stream);
+                           void* dk, void* dv, void* ws, int BH, int N, int d, bool causal,
+                           float scale, hipStream_t stream);
 hipError_t launch_bwd_finalize(void* dq, const void* ws, int BH, int N, int d,
                                hipStream_t stream);
 

@@ -98,8 +98,9 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o,
 /*
  * fa_bwd_workspace_size -- bytes of device workspace fa_bwd needs.
  *
- * Returns 0 for invalid shapes.  The workspace holds D = rowsum(dO * O)
- * ([B, H, N] float32) and the float32 dQ accumulator ([B, H, N, d]).
+ * Returns 0 for invalid shapes.  The workspace holds, per row, lse * log2(e)
+ * and D = rowsum(dO * O) (float32, each head padded to a multiple of 64 rows)
+ * and the float32 dQ accumulator ([B, H, N, d]).
  */
 size_t fa_bwd_workspace_size(int B, int H, int N, int d);
 
@@ -133,21 +134,21 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
  * that schedule or time the stages separately.  Each validates like fa_bwd
  * (its own pointers only) and reads/writes the workspace as documented.
  *
- * fa_bwd_preprocess -- D = rowsum(dO * O) into the workspace; zeroes the
- *                      workspace's fp32 dQ accumulator.
- * fa_bwd_main       -- the key-tile kernel: recomputes P from q, k, lse,
- *                      writes dk and dv, and adds scale * dS K into the dQ
- *                      accumulator (float atomics).  Needs the preprocess
- *                      stage's workspace contents.
+ * fa_bwd_preprocess -- lse * log2(e) and D = rowsum(dO * O) into the
+ *                      workspace; zeroes the workspace's fp32 dQ accumulator.
+ * fa_bwd_main       -- the key-tile kernel: recomputes P from q, k and the
+ *                      workspace's log-sum-exp, writes dk and dv, and adds
+ *                      scale * dS K into the dQ accumulator (float atomics).
+ *                      Needs the preprocess stage's workspace contents.
  * fa_bwd_finalize   -- dq = bf16(dQ accumulator).
  */
-int fa_bwd_preprocess(const void* o, const void* dout, void* workspace,
-                      size_t workspace_bytes, int B, int H, int N, int d,
-                      hipStream_t stream);
+int fa_bwd_preprocess(const void* o, const void* dout, const float* lse,
+                      void* workspace, size_t workspace_bytes, int B, int H,
+                      int N, int d, hipStream_t stream);
 int fa_bwd_main(const void* q, const void* k, const void* v, const void* dout,
-                const float* lse, void* dk, void* dv, void* workspace,
-                size_t workspace_bytes, int B, int H, int N, int d, int causal,
-                float scale, hipStream_t stream);
+                void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                int B, int H, int N, int d, int causal, float scale,
+                hipStream_t stream);
 int fa_bwd_finalize(void* dq, const void* workspace, size_t workspace_bytes,
                     int B, int H, int N, int d, hipStream_t stream);
 

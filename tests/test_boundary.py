@@ -141,14 +141,17 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
 
 def test_backward_stages_reject_bad_arguments(lib):
     ws = lib.fa_bwd_workspace_size(1, 2, 100, 64)
-    o, g, w = A, A + MB, A + 9 * MB
-    assert lib.fa_bwd_preprocess(o, g, w, 8, 1, 2, 100, 64, None) == fa.FA_ERR_WORKSPACE
-    assert lib.fa_bwd_preprocess(None, g, w, ws, 1, 2, 100, 64, None) == fa.FA_ERR_NULL
-    assert lib.fa_bwd_preprocess(o, g, o + 64, ws, 1, 2, 100, 64, None) == fa.FA_ERR_ALIAS
-    assert lib.fa_bwd_preprocess(o, g, w, ws, 1, 2, 100, 48, None) == fa.FA_ERR_HEADDIM
-    assert lib.fa_bwd_preprocess(o, g, w, ws, 1, 2, 0, 64, None) == fa.FA_OK
+    o, g, L, w = A, A + MB, A + 5 * MB, A + 9 * MB
+    assert lib.fa_bwd_preprocess(o, g, L, w, 8, 1, 2, 100, 64, None) == fa.FA_ERR_WORKSPACE
+    assert lib.fa_bwd_preprocess(None, g, L, w, ws, 1, 2, 100, 64, None) == fa.FA_ERR_NULL
+    assert lib.fa_bwd_preprocess(o, g, None, w, ws, 1, 2, 100, 64, None) == fa.FA_ERR_NULL
+    assert lib.fa_bwd_preprocess(o, g, L, o + 64, ws, 1, 2, 100, 64, None) == fa.FA_ERR_ALIAS
+    assert lib.fa_bwd_preprocess(o, g, L, L + 16, ws, 1, 2, 100, 64, None) == fa.FA_ERR_ALIAS
+    assert lib.fa_bwd_preprocess(o, g, L + 4, w, ws, 1, 2, 100, 64, None) == fa.FA_ERR_ALIGN
+    assert lib.fa_bwd_preprocess(o, g, L, w, ws, 1, 2, 100, 48, None) == fa.FA_ERR_HEADDIM
+    assert lib.fa_bwd_preprocess(o, g, L, w, ws, 1, 2, 0, 64, None) == fa.FA_OK
     mk = lambda **kw: lib.fa_bwd_main(  # noqa: E731
-        kw.get("q", A), A + MB, A + 2 * MB, A + 4 * MB, A + 5 * MB, kw.get("dk", A + 7 * MB),
+        kw.get("q", A), A + MB, A + 2 * MB, A + 4 * MB, kw.get("dk", A + 7 * MB),
         A + 8 * MB, kw.get("ws", w), kw.get("wsb", ws), 1, 2, 100, 64, 1,
         kw.get("scale", 0.125), None)
     assert mk(q=None) == fa.FA_ERR_NULL
