@@ -125,12 +125,17 @@ struct BwdCfg {
   static constexpr int SMEM = OFF_DS + 2 * DSTILE;
   static constexpr int QDMA = QTILE / 16 / THREADS;       // DMAs per thread per tile
   static constexpr int KDMA = KTILE / 16 / THREADS;
-  // dQ = dS K: 32x32 output blocks of the [kBQ, D] tile and their owners
+  // dQ = dS K.  d = 64 (8 waves): sixteen 16x16 blocks of the [kBQ, 64]
+  // tile, two per wave, each over all the tile's keys -- one owner per dQ
+  // element (two waves adding into the same lines at once cost more than the
+  // rest of the kernel).  d = 128 (4 waves): 32x32 blocks, two per wave.
+  static constexpr bool DQ16 = (D == 64);
   static constexpr int NBLK = NQS * NDB;
   static constexpr int KSPLIT = WAVES >= NBLK ? WAVES / NBLK : 1;
-  static constexpr int BPW = WAVES >= NBLK ? 1 : NBLK / WAVES;  // blocks per wave
-  static constexpr int DQKEYS = KEYS / KSPLIT;            // keys per dQ partial
+  static constexpr int BPW = WAVES >= NBLK ? 1 : NBLK / WAVES;  // 32x32 blocks per wave
   static_assert(QDMA * THREADS * 16 == QTILE && KDMA * THREADS * 16 == KTILE, "DMA split");
+  static_assert(!DQ16 || (kBQ / 16) * (D / 16) == 2 * WAVES, "two 16x16 dQ blocks per wave");
+  static_assert(DQ16 || KSPLIT == 1, "one owner per dQ block");
   static_assert(SMEM <= 160 * 1024, "LDS budget");
 };
 
@@ -159,19 +164,22 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_main_kernel(
   const char* dOb = reinterpret_cast<const char*>(dO + base);
   const float* L2h = L2 + (size_t)bh * Npad;
   const float* Dh = Dv + (size_t)bh * Npad;
-  float* dQh = dQacc + base;
+  // the head's slice of the fp32 dQ accumulator as a buffer resource
+  const __amdgpu_buffer_rsrc_t dq_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      dQacc + base, (short)0, (int)((unsigned)N * (unsigned)D * 4u), 0x00020000);
 
   const int k0 = kt * C::KEYS;
   const int wk0 = k0 + 32 * w;   // this wave's first key
   const int key = wk0 + n;       // this lane's key
   const unsigned lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem));
 
-  // key tile (row-major, transposing-read swizzle) for the K^T operand of dQ
+  // key tile (row-major) for the K^T operand of dQ, read transposing by 16-
+  // and 32-lane groups whose rows lie 8 apart: SWZ_BOTH keeps them apart
 #pragma unroll
   for (int j = 0; j < C::KDMA; ++j) {
     const int slot = (j * C::WAVES + w) * 64 + lane;
     const int row = slot / C::CPRD;
-    const int chunk = (slot % C::CPRD) ^ swz<C::CPRD, SWZ_TR>(row);
+    const int chunk = (slot % C::CPRD) ^ swz<C::CPRD, SWZ_BOTH>(row);
     const int src = min(k0 + row, N - 1);
     dma16(Kb, (unsigned)((src * D + chunk * 8) * 2), lds0 + C::OFF_K + (j * C::WAVES + w) * 1024);
   }
@@ -231,10 +239,15 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_main_kernel(
 #pragma unroll
     for (int rd = 0; rd < 2; ++rd)
       qtr[db][rd] = tile_off<C::CPRD, SWZ_BOTH>(trow + 8 * rd, 32 * db + tcol);
-  // dS writes: row 32w + n (this lane's key), queries 32qs + 8g + 4h .. +3
-  int dsw[C::NQS];
+  // dS writes: row 32w + n (this lane's key), queries 32qs + 8g + 4h .. +3.
+  // The dS tile is row-written and transposing-read, so it uses SWZ_BOTH; its
+  // chunk positions are not affine in g, hence one offset per (qs, g).
+  int dsw[C::NQS][4];
 #pragma unroll
-  for (int qs = 0; qs < C::NQS; ++qs) dsw[qs] = tile_off<C::CPRQ, SWZ_TR>(32 * w + n, 32 * qs + 4 * h);
+  for (int qs = 0; qs < C::NQS; ++qs)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      dsw[qs][g] = tile_off<C::CPRQ, SWZ_BOTH>(32 * w + n, 32 * qs + 8 * g + 4 * h);
 
   f32x16 dk[C::NDB], dv[C::NDB];
 #pragma unroll
@@ -245,46 +258,98 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_main_kernel(
       dv[db][r] = 0.f;
     }
 
-  // dQ = dS K for query block it, from dS buffer it & 1
+  // dQ = dS K for query block it, from dS buffer it & 1, added (times scale)
+  // into the fp32 accumulator with buffer atomics: one per-lane offset, the
+  // register's row as a uniform offset; all rows valid is the common,
+  // branch-free case.  Key chunks past the causal limit hold dS = 0 (masked
+  // P, or zeros written by waves with no visible key), so the k loop is
+  // straight-line and only a block with no visible key at all is skipped.
   auto dq_step = [&](int it) {
     const int q0 = (qb0 + it) * kBQ;
     const char* dsb = smem + C::OFF_DS + (it & 1) * C::DSTILE;
     const char* kt_lds = smem + C::OFF_K;
+    if constexpr (C::DQ16) {
+      const int g = lane >> 4;          // 16-lane group
+      const int rrow = 8 * g + ((lane & 15) >> 2);
+      const int rcol = 4 * (lane & 3);
 #pragma unroll
-    for (int bi = 0; bi < C::BPW; ++bi) {
-      const int blk = C::BPW == 1 ? (w % C::NBLK) : (w * C::BPW + bi);
-      const int kp = C::BPW == 1 ? (w / C::NBLK) : 0;
-      const int qsq = blk / C::NDB;
-      const int dbq = blk % C::NDB;
-      const int qs0 = q0 + 32 * qsq;
-      const int kb0 = kp * C::DQKEYS;          // first key of this partial (tile-relative)
-      int nkc = C::DQKEYS / 16;
-      if (CAUSAL) {
-        const int lim = qs0 + 31 - (k0 + kb0);  // last key offset that can see a query
-        nkc = lim < 0 ? 0 : min(C::DQKEYS / 16, lim / 16 + 1);
+      for (int bi = 0; bi < 2; ++bi) {
+        const int b = 2 * w + bi;
+        const int qbase = 16 * (b / (D / 16));
+        const int dbase = 16 * (b % (D / 16));
+        const int qg0 = q0 + qbase;
+        if (CAUSAL && k0 > qg0 + 15) continue;
+        int aoff[2], boff[2];
+#pragma unroll
+        for (int rd = 0; rd < 2; ++rd) {
+          aoff[rd] = tile_off<C::CPRQ, SWZ_BOTH>(rrow + 4 * rd, qbase + rcol);
+          boff[rd] = tile_off<C::CPRD, SWZ_BOTH>(rrow + 4 * rd, dbase + rcol);
+        }
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < C::KEYS / 32; ++ks) {
+          const u32x2 a0 = lds_read_tr16(dsb + aoff[0] + 32 * ks * C::RBQ);
+          const u32x2 a1 = lds_read_tr16(dsb + aoff[1] + 32 * ks * C::RBQ);
+          const u32x2 b0 = lds_read_tr16(kt_lds + boff[0] + 32 * ks * C::RBD);
+          const u32x2 b1 = lds_read_tr16(kt_lds + boff[1] + 32 * ks * C::RBD);
+          acc = mfma_16x16x32_bf16(__builtin_bit_cast(bf16x8, u32x4{a0.x, a0.y, a1.x, a1.y}),
+                                   __builtin_bit_cast(bf16x8, u32x4{b0.x, b0.y, b1.x, b1.y}), acc);
+        }
+        // acc: lane = feature dbase + lane%16, registers = queries qg0 + 4g + r
+        const int voff = ((qg0 + 4 * g) * D + dbase + (lane & 15)) * 4;
+        if (qg0 + 15 < N) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(scale * acc[r], dq_rsrc, voff,
+                                                            r * D * 4, 0);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (qg0 + 4 * g + r < N)
+              __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(scale * acc[r], dq_rsrc, voff,
+                                                              r * D * 4, 0);
+        }
       }
-      if (nkc == 0) continue;
-      const int aoff = tile_off<C::CPRQ, SWZ_TR>(kb0 + trow, 32 * qsq + tcol);
-      const int boff = tile_off<C::CPRD, SWZ_TR>(kb0 + trow, 32 * dbq + tcol);
-      f32x16 acc = {};
+    } else {
 #pragma unroll
-      for (int kc = 0; kc < C::DQKEYS / 16; ++kc) {
-        if (kc < nkc) {
-          const u32x2 a0 = lds_read_tr16(dsb + aoff + (16 * kc) * C::RBQ);
-          const u32x2 a1 = lds_read_tr16(dsb + aoff + (16 * kc + 8) * C::RBQ);
-          const u32x2 b0 = lds_read_tr16(kt_lds + boff + (16 * kc) * C::RBD);
-          const u32x2 b1 = lds_read_tr16(kt_lds + boff + (16 * kc + 8) * C::RBD);
+      for (int bi = 0; bi < C::BPW; ++bi) {
+        const int blk = w * C::BPW + bi;
+        const int qsq = blk / C::NDB;
+        const int dbq = blk % C::NDB;
+        const int qs0 = q0 + 32 * qsq;
+        if (CAUSAL && k0 > qs0 + 31) continue;
+        // SWZ_BOTH depends on row bits 1..3: the two 8-row halves differ
+        const int aoff0 = tile_off<C::CPRQ, SWZ_BOTH>(trow, 32 * qsq + tcol);
+        const int aoff1 = tile_off<C::CPRQ, SWZ_BOTH>(trow + 8, 32 * qsq + tcol);
+        const int boff0 = tile_off<C::CPRD, SWZ_BOTH>(trow, 32 * dbq + tcol);
+        const int boff1 = tile_off<C::CPRD, SWZ_BOTH>(trow + 8, 32 * dbq + tcol);
+        f32x16 acc = {};
+#pragma unroll
+        for (int kc = 0; kc < C::KEYS / 16; ++kc) {
+          const u32x2 a0 = lds_read_tr16(dsb + aoff0 + (16 * kc) * C::RBQ);
+          const u32x2 a1 = lds_read_tr16(dsb + aoff1 + (16 * kc) * C::RBQ);
+          const u32x2 b0 = lds_read_tr16(kt_lds + boff0 + (16 * kc) * C::RBD);
+          const u32x2 b1 = lds_read_tr16(kt_lds + boff1 + (16 * kc) * C::RBD);
           acc = mfma_32x32x16_bf16(__builtin_bit_cast(bf16x8, u32x4{a0.x, a0.y, a1.x, a1.y}),
                                    __builtin_bit_cast(bf16x8, u32x4{b0.x, b0.y, b1.x, b1.y}),
                                    acc);
         }
-      }
-      // acc: lane = feature 32*dbq + n, registers = queries
-      float* dst = dQh + 32 * dbq + n;
+        // acc: lane = feature 32*dbq + n, registers = queries qs0 + 4h + 8(r/4) + r%4
+        const int voff = ((qs0 + 4 * h) * D + 32 * dbq + n) * 4;
+        if (qs0 + 31 < N) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qrow = qs0 + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (qrow < N) unsafeAtomicAdd(dst + (size_t)qrow * D, scale * acc[r]);
+          for (int r = 0; r < 16; ++r)
+            __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(
+                scale * acc[r], dq_rsrc, voff, (8 * (r >> 2) + (r & 3)) * D * 4, 0);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int qrow = qs0 + 4 * h + 8 * (r >> 2) + (r & 3);
+            if (qrow < N)
+              __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(
+                  scale * acc[r], dq_rsrc, voff, (8 * (r >> 2) + (r & 3)) * D * 4, 0);
+          }
+        }
       }
     }
   };
@@ -377,7 +442,7 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_main_kernel(
       // 32qs + 8g + 4h .. +3
 #pragma unroll
       for (int g = 0; g < 4; ++g)
-        *reinterpret_cast<u32x2*>(dsb + dsw[qs] + 16 * g) = u32x2{sk[2 * g], sk[2 * g + 1]};
+        *reinterpret_cast<u32x2*>(dsb + dsw[qs][g]) = u32x2{sk[2 * g], sk[2 * g + 1]};
     }
   }
   wait_vmem();

@@ -34,17 +34,25 @@ __device__ __forceinline__ f32x16 mfma_32x32x16_bf16(const bf16x8& a,
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+//   v_mfma_f32_16x16x32_bf16: D[16x16] += A[16x32] * B[32x16]; A lane l holds
+//   row l % 16, B lane l column l % 16, both with 8 k-values chosen by
+//   (l / 16, t); D lane l, register r holds D[4*(l/16) + r][l % 16].
+__device__ __forceinline__ f32x4 mfma_16x16x32_bf16(const bf16x8& a, const bf16x8& b,
+                                                   const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 __device__ __forceinline__ f32x16 mfma_32x32x2_f32(float a, float b,
                                                    const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
-// Round-to-nearest-even float -> bf16 pair packed in one dword (lo = a).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Round-to-nearest-even float -> bf16 pair packed in one dword (lo = a); one
+// v_cvt_pk_bf16_f32 (two scalar conversions would cost a shift and an or more).
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  __bf16 x = (__bf16)a;
-  __bf16 y = (__bf16)b;
-  return (uint32_t)__builtin_bit_cast(uint16_t, x) |
-         ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
 // Low (sel = 0x05040100) or high (sel = 0x07060302) 16-bit halves of a and b
