@@ -38,9 +38,14 @@ METRIC = "attention fwd/bwd TFLOP/s and % of bf16 MFMA peak at N=1k-32k, d=64/12
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ["exact_tiled_attention_10_amd/csrc/fa_bwd.hip",
-                  "exact_tiled_attention_10_amd/csrc/fa_fwd.hip",
-                  "exact_tiled_attention_10_amd/csrc/fa_common.h"]
+# sources each kernel is built from: counter-derived traffic is used only while
+# they are unchanged
+KERNEL_SOURCES = {
+    "bwd_main_kernel": ["exact_tiled_attention_10_amd/csrc/fa_bwd.hip",
+                        "exact_tiled_attention_10_amd/csrc/fa_common.h"],
+    "fwd_bf16_kernel": ["exact_tiled_attention_10_amd/csrc/fa_fwd.hip",
+                        "exact_tiled_attention_10_amd/csrc/fa_common.h"],
+}
 STEP_WORKLOAD = "train_step_n2048"
 SWEEP = [("gpt2_medium_n1024", False), ("gpt2_medium_n1024", True),
          ("llama8b_n4096", True), ("long_context_n16384", True),
@@ -52,9 +57,9 @@ def fwd_flops(B, H, N, d, causal):
     return f / 2 if causal else f
 
 
-def source_hash() -> str:
+def source_hash(kernel: str) -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -115,7 +120,7 @@ def run_step_bench(steps: int, warmup: int):
                 fwd_flops=ff, bwd_flops=bf)
 
 
-def run_fwd_sweep(reps: int = 10):
+def run_fwd_sweep(reps: int = 20, warm_s: float = 0.05):
     import torch
     import exact_tiled_attention_10_amd as fa
     from workloads import WORKLOADS, workload_inputs
@@ -126,8 +131,13 @@ def run_fwd_sweep(reps: int = 10):
         q, k, v = (t.cuda() for t in workload_inputs(w, with_do=False))
         o = torch.empty_like(q)
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
-        for _ in range(3):
+        t_end = time.perf_counter() + warm_s
+        n_warm = 0
+        while n_warm < 3 or time.perf_counter() < t_end:
             fa.fa_fwd(q, k, v, o, lse, causal, w.scale)
+            n_warm += 1
+            if n_warm % 16 == 0:
+                torch.cuda.synchronize()
         s = torch.cuda.Event(enable_timing=True)
         e = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
@@ -202,7 +212,7 @@ def load_traffic(kernel_name: str):
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("source_hash") != source_hash() or t.get("kernel") != kernel_name:
+    if t.get("kernel") != kernel_name or t.get("source_hash") != source_hash(kernel_name):
         return None
     return t.get("bytes_per_launch")
 
@@ -238,7 +248,8 @@ def pmc_summary(fetch_csv: str, write_csv: str, copy_mib: float) -> dict:
     name, kf = pick(fetch, "bwd_main_kernel")
     _, kw = pick(write, "bwd_main_kernel")
     bytes_per_launch = kf * 1024.0 * f_scale + kw * 1024.0 * w_scale
-    out = dict(kernel="bwd_main_kernel", kernel_symbol=name, source_hash=source_hash(),
+    out = dict(kernel="bwd_main_kernel", kernel_symbol=name,
+               source_hash=source_hash("bwd_main_kernel"),
                fetch_kib_raw=kf, write_kib_raw=kw, copy_mib=copy_mib,
                copy_fetch_kib_raw=cf, copy_write_kib_raw=cw,
                fetch_scale=f_scale, write_scale=w_scale,
@@ -267,7 +278,9 @@ def main(argv=None):
                                  formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    # The clock settles only after ~0.1 s of sustained matrix-core load, so the
+    # default warm-up is long enough to time the steady state.
+    ap.add_argument("--warmup", type=int, default=400)
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="wall-time budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")

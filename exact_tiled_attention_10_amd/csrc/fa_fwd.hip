@@ -1,34 +1,44 @@
 // Forward kernels: exact attention with online softmax, gfx950.
 //
-// One workgroup owns one tile of 128 queries of one (batch, head) and streams
+// One workgroup owns one tile of 256 queries of one (batch, head) and streams
 // the key/value tiles past it (the flipped loop order of "Flash Attention,
 // From First Principles", "The schedule -- who commutes?": the query block is
-// resident, its output is written once).  Each of the 4 waves owns 32 query
+// resident, its output is written once).  Each of the 8 waves owns 32 query
 // rows.  Per key tile a wave
 //   1. mints the score tile on the matrix cores, transposed: S^T = K Q^T, so
 //      each lane holds the scores of ONE query against 16 keys and its partner
 //      lane (32 away) the other 16 ("The scaffold": S_tile = Q_tile K_tile^T);
 //   2. masks keys past N and, on diagonal tiles, keys after the query;
-//   3. takes the row max (in-lane, then one cross-half exchange) and updates
-//      the running max m; rescales the running sum l and the accumulator by
-//      exp(m_old - m_new) ("LLM Architecture Refresh [3]", sections 2 and 4);
-//   4. forms P = exp(S - m_new) in fp32, adds its row sum to l, rounds P to
-//      bf16 and accumulates O^T += V^T P^T on the matrix cores -- the bf16 P
-//      registers are already in the B-operand layout, no data movement;
+//   3. forms P = exp(S - m) against its running max m, adds the row sums to
+//      the running sum l and rounds P to bf16; when a tile would push some p
+//      past a fixed bound, m first moves to the true running max and l and
+//      the accumulator are rescaled by exp(m_old - m_new) ("LLM Architecture
+//      Refresh [3]", sections 2 and 4);
+//   4. accumulates O^T += V^T P^T on the matrix cores -- the bf16 P registers
+//      are already in the B-operand layout, no data movement;
 // and after the last tile divides once by l and stores O and the
 // log-sum-exp ("FlashAttention from scratch", Step 3 and Follow-up questions).
-// Key tiles lying wholly after a wave's last query are skipped
+// Key tiles lying wholly after the workgroup's last query are skipped
 // ("LLM Architecture Refresh [3]", section 7).
+//
+// Schedule: the waves form two groups of four, one wave of each group per
+// SIMD.  In every round one group issues only matrix-core work (the value
+// product of the previous tile and the scores of the current one) while the
+// other runs the softmax of its scores on the vector ALUs, then the groups
+// swap; a workgroup barrier separates the halves.  So each SIMD keeps its
+// matrix core and its vector ALU busy with two waves whose own instruction
+// streams need not interleave the two kinds of work.
 //
 // Scores are kept in log2 units: t = s * c - m with c = |scale| * log2(e), so
 // each probability costs one FMA and one v_exp_f32.  A negative scale is
 // handled by negating the query fragment (exact in bf16/fp32).
 //
 // K and V tiles go from HBM straight into LDS by DMA (global_load_lds), two
-// stages deep: tile kt+1 is in flight while tile kt is computed, with one
-// barrier per tile.  Both tiles stay row-major in LDS (XOR-swizzled against
-// bank conflicts); the V^T operand of the PV product is read with the
-// transposing ds_read_b64_tr_b16, so no register shuffling is needed.
+// stages deep.  Both tiles stay row-major in LDS (XOR-swizzled against bank
+// conflicts); the V^T operand of the PV product is read with the transposing
+// ds_read_b64_tr_b16, so no register shuffling is needed.
+#include <type_traits>
+
 #include "fa_common.h"
 #include "fa_internal.h"
 
@@ -36,49 +46,70 @@ namespace fa {
 
 namespace {
 
-constexpr int kWaves = 4;
+// Eight waves in two groups of four; the hardware places wave w on SIMD
+// w % 4, so every SIMD runs one wave of each group.
+constexpr int kWaves = 8;
 constexpr int kBM = 32 * kWaves;  // queries per workgroup
+// The fp32 kernel keeps the 4-wave, 128-query tiling.
+constexpr int kWavesF32 = 4;
+constexpr int kBMF32 = 32 * kWavesF32;
+
+// A tile's probabilities are accepted against the running max m as it stands
+// as long as every lane's sum of p stays <= kSumBound (so every p <= 2^8);
+// otherwise the tile rebases m to the true running max first.
+constexpr float kSumBound = 256.f;
+// Start value of the running max (log2 units): finite, so exp2(t - m) is +inf
+// (never NaN) for every finite score of the first tile, which forces a rebase.
+constexpr float kMInit = -1e30f;
 
 template <int D, int BN>
 struct FwdCfg {
   static constexpr int CPR = D / 8;                 // 16-byte chunks per tile row
   static constexpr int TILE_BYTES = BN * D * 2;     // one K or V tile (bf16)
-  static constexpr int STAGE_BYTES = 2 * TILE_BYTES;
-  static constexpr int SMEM_BYTES = 2 * STAGE_BYTES;
+  static constexpr int SMEM_BYTES = 4 * TILE_BYTES; // K[2], V[2]
+  static constexpr int OFF_V = 2 * TILE_BYTES;
   static constexpr int NSB = BN / 32;               // 32-key sub-blocks per tile
-  static constexpr int NKC = BN / 16;               // 16-key chunks per tile
   static constexpr int NQC = D / 16;                // 16-feature chunks (QK^T k-steps)
   static constexpr int NDB = D / 32;                // 32-feature output blocks
-  static constexpr int DMA = TILE_BYTES / 16 / 256; // 16-byte DMAs per thread per tensor
+  static constexpr int DMA = TILE_BYTES / (16 * 64 * kWaves);  // DMAs per lane per tile
+  static constexpr int DMA_STRIDE = 16 * 64 * kWaves;          // bytes between them
   static constexpr int ROW_BYTES = CPR * 16;
-  static_assert(DMA * 256 * 16 == TILE_BYTES, "tile split");
+  static_assert(DMA * DMA_STRIDE == TILE_BYTES, "tile split");
 };
 
 // Per-lane byte offset (inside one (batch, head) slice, relative to row k0) of
 // the global chunk that lands in this lane's LDS slot of DMA number i.  Rows
 // past N are clamped to row N-1 (finite data; those keys are masked to -inf
-// and their P is 0, so they contribute nothing).
+// and their P is 0, so they contribute nothing).  Both the LDS tile and the
+// global rows are D * 2 bytes long, so with either swizzle DMA i + 1 is DMA i
+// shifted by DMA_STRIDE bytes on both sides (for a full tile).
 template <int D, int BN, int KIND>
 __device__ __forceinline__ unsigned dma_src_off(int i, int w, int lane, int k0, int N, bool full) {
   using C = FwdCfg<D, BN>;
-  const int slot = (i * 4 + w) * 64 + lane;
+  const int slot = (i * kWaves + w) * 64 + lane;
   const int row = slot / C::CPR;
   const int chunk = (slot % C::CPR) ^ swz<C::CPR, KIND>(row);
   const int src_row = full ? row : min(k0 + row, N - 1) - k0;
   return (unsigned)((src_row * D + chunk * 8) * 2);
 }
 
+// Workgroup barrier that orders the compiler's memory operations but adds no
+// wait for outstanding memory transfers (prefetch DMAs stay in flight).
+__device__ __forceinline__ void phase_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
 template <int D, int BN, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
+__global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
     int BH, int N, int nqt, float c, int negq) {
   using C = FwdCfg<D, BN>;
+  constexpr int NSB = C::NSB;
   extern __shared__ __attribute__((aligned(1024))) char smem_raw[];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = w >> 2;            // 0: matrix phase first; 1: softmax phase first
   const int n = lane & 31;
   const int h = lane >> 5;
 
@@ -89,42 +120,52 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   const char* Kb = reinterpret_cast<const char*>(K + base);
   const char* Vb = reinterpret_cast<const char*>(V + base);
 
+  // 32-query blocks alternate between the groups so both see the same share
+  // of the causal diagonal.
   const int q0 = qt * kBM;
-  const int wq0 = q0 + 32 * w;       // this wave's first query
-  const int qrow = wq0 + n;          // this lane's query
+  const int wq0 = q0 + 32 * (2 * (w & 3) + grp);   // this wave's first query
+  const int qrow = wq0 + n;                        // this lane's query
 
   const int kend = CAUSAL ? min(N, q0 + kBM) : N;
   const int nkt = (kend + BN - 1) / BN;
 
-  // DMA bookkeeping: LDS address of this wave's first 1 KiB slot, and the
-  // per-lane source offsets of full tiles (K row-swizzled, V tr-swizzled).
-  // DMA number i covers rows 16i*... further down the tile: with either
-  // swizzle the lane's chunk does not depend on i, so one offset per tensor
-  // plus a uniform stride of 4 KiB per DMA covers the tile.
-  const unsigned lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem_raw)) + w * 1024;
-  const unsigned koff0 = dma_src_off<D, BN, SWZ_ROWS>(0, w, lane, 0, N, true);
-  const unsigned voff0 = dma_src_off<D, BN, SWZ_TR>(0, w, lane, 0, N, true);
-  auto issue = [&](int kt) {
-    const int k0 = kt * BN;
-    const char* kg = Kb + (size_t)k0 * D * 2;
-    const char* vg = Vb + (size_t)k0 * D * 2;
-    const unsigned st = lds0 + (kt & 1) * C::STAGE_BYTES;
+  // DMA: tile t of K (V) goes to K (V) stage t & 1.  Round j issues K tile
+  // j + 1 and V tile j; they land by the end of round j and are read in round
+  // j + 1 (K by the scores of tile j + 1, V by the value product of tile j).
+  // Only the group that starts a round with its softmax phase issues them
+  // (each of its waves two 1 KiB slots per DMA step): a DMA instruction costs
+  // about 16 cycles at the CU's address unit, and a burst of them would
+  // otherwise hold back the start of the other group's matrix phase.
+  const unsigned ldsb = __builtin_amdgcn_readfirstlane(lds_addr(smem_raw));
+  const int ws0 = w & 3, ws1 = ws0 + 4;   // the two DMA slots a group-1 wave fills
+  const unsigned koffA = dma_src_off<D, BN, SWZ_ROWS>(0, ws0, lane, 0, N, true);
+  const unsigned voffA = dma_src_off<D, BN, SWZ_TR>(0, ws0, lane, 0, N, true);
+  const unsigned koffB = dma_src_off<D, BN, SWZ_ROWS>(0, ws1, lane, 0, N, true);
+  const unsigned voffB = dma_src_off<D, BN, SWZ_TR>(0, ws1, lane, 0, N, true);
+  auto issue_slot = [&](int t, int ws, unsigned lds_tensor, const char* gsrc, unsigned off0,
+                        auto kind) __attribute__((always_inline)) {
+    constexpr int KIND = decltype(kind)::value;
+    const int k0 = t * BN;
+    const char* g = gsrc + (size_t)k0 * D * 2;
+    const unsigned st = ldsb + ws * 1024 + lds_tensor + (t & 1) * C::TILE_BYTES;
     if (k0 + BN <= N) {
 #pragma unroll
-      for (int i = 0; i < C::DMA; ++i) {
-        dma16(kg + i * 4096, koff0, st + i * 4096);
-        dma16(vg + i * 4096, voff0, st + C::TILE_BYTES + i * 4096);
-      }
+      for (int i = 0; i < C::DMA; ++i)
+        dma16(g + i * C::DMA_STRIDE, off0, st + i * C::DMA_STRIDE);
     } else {
 #pragma unroll
-      for (int i = 0; i < C::DMA; ++i) {
-        dma16(kg, dma_src_off<D, BN, SWZ_ROWS>(i, w, lane, k0, N, false), st + i * 4096);
-        dma16(vg, dma_src_off<D, BN, SWZ_TR>(i, w, lane, k0, N, false),
-              st + C::TILE_BYTES + i * 4096);
-      }
+      for (int i = 0; i < C::DMA; ++i)
+        dma16(g, dma_src_off<D, BN, KIND>(i, ws, lane, k0, N, false), st + i * C::DMA_STRIDE);
     }
   };
-  if (nkt > 0) issue(0);
+  auto issue = [&](int t, unsigned lds_tensor, const char* gsrc, unsigned offA, unsigned offB,
+                   auto kind) __attribute__((always_inline)) {
+    issue_slot(t, ws0, lds_tensor, gsrc, offA, kind);
+    issue_slot(t, ws1, lds_tensor, gsrc, offB, kind);
+  };
+  using rows_t = std::integral_constant<int, SWZ_ROWS>;
+  using tr_t = std::integral_constant<int, SWZ_TR>;
+  if (nkt > 0 && grp == 1) issue(0, 0u, Kb, koffA, koffB, rows_t{});
 
   // Q^T as the B operand: lane holds Q[qrow][16c + 8h .. 16c + 8h + 7].
   bf16x8 qf[C::NQC];
@@ -139,134 +180,226 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     }
   }
 
-  // per-lane LDS operand offsets inside a stage.  K (A operand of S^T): row
-  // 32sb + n, features 16cc + 8h..; the swizzle does not change with sb.
-  int kb[C::NQC];
-#pragma unroll
-  for (int cc = 0; cc < C::NQC; ++cc) kb[cc] = tile_off<C::CPR, SWZ_ROWS>(n, 16 * cc + 8 * h);
+  // Per-lane LDS operand addresses inside a stage, one register per tensor.
+  // K (A operand of S^T): row 32sb + n, features 16cc + 8h..  With the row
+  // swizzle the chunk is (2cc + h) ^ (n % 16), so the byte offset is
+  // ka ^ (32 cc) with ka the cc = 0 offset: the XOR only touches bits 5..7,
+  // the sub-block and stage offsets are added as immediates.
+  const int ka = tile_off<C::CPR, SWZ_ROWS>(n, 8 * h);
   // V^T (A operand of O^T += V^T P^T) through transposing reads: 16-lane group
   // g reads key rows 4*(g/2) + j (+16kc, +8 for the second half) and features
-  // 32db + 16*(g%2) + 4*(lane%4); the swizzle does not change with kc.
+  // 32db + 16*(g%2) + 4*(lane%4).  With the transposing swizzle (chunk ^ 4(r%4))
+  // the db = 0 offset va gives block db at va ^ (64 db) (CPR 16) or va ^ (64 db)
+  // with db < 2 (CPR 8: swz 4((r/2)%2) touches bit 2 of the chunk as well).
   const int vrow0 = 4 * (lane >> 5) + ((lane & 15) >> 2);
   const int vcol0 = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  int vb[C::NDB];
-#pragma unroll
-  for (int db = 0; db < C::NDB; ++db) vb[db] = tile_off<C::CPR, SWZ_TR>(vrow0, 32 * db + vcol0);
+  const int va = tile_off<C::CPR, SWZ_TR>(vrow0, vcol0);
+  auto kaddr = [&](int cc) __attribute__((always_inline)) { return ka ^ (32 * cc); };
+  auto vaddr = [&](int db) __attribute__((always_inline)) { return va ^ (64 * db); };
 
   f32x16 acc[C::NDB];
 #pragma unroll
   for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
-  float m = kNegInf;   // running max, log2-scaled units
+  float m = kMInit;    // running max, log2-scaled units (same in both lane halves)
   float lsum = 0.f;    // this lane's share of the running sum
+  f32x16 s[NSB];       // scores of the tile between its matrix and softmax phases
+  uint32_t pk[NSB][8]; // bf16 probabilities between the softmax and value phases
 
-  const char* smem_k = smem_raw;
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int k0 = kt * BN;
-    // tile kt has landed for every lane; every wave is done with tile kt-1
-    wait_vmem();
-    __syncthreads();
-    if (kt + 1 < nkt) issue(kt + 1);
-    const char* ks = smem_k + (kt & 1) * C::STAGE_BYTES;
-    const char* vs = ks + C::TILE_BYTES;
-
-    // sub-blocks of 32 keys this wave must compute (wave-uniform)
-    int nsb = C::NSB;
-    if (CAUSAL) {
-      const int lim = wq0 + 31 - k0;          // last visible key offset for the wave
-      nsb = lim < 0 ? 0 : min(C::NSB, lim / 32 + 1);
-    }
-    if (nsb == 0) continue;
-
-    f32x16 s[C::NSB];
+  // Matrix phase of round j: O^T += V^T P^T for tile j - 1 (skipped in the
+  // first round) and the scores S^T = K Q^T of tile j (skipped in the last),
+  // in steps of two value-product MFMAs (one 16-key chunk, two 32-feature
+  // blocks) and two score MFMAs (two 16-feature k-steps).  The operands of
+  // step t + 1 are read from LDS (into the other half of a double buffer)
+  // before the MFMAs of step t are issued, so the LDS latency hides behind
+  // the matrix work; scheduling barriers keep that order.
+  //
+  // Every wave computes whole tiles, also on the causal diagonal where some
+  // of its sub-blocks are masked entirely: the groups advance in lock step,
+  // so a phase lasts as long as its busiest wave and skipping work in one
+  // wave would not shorten it.  The softmax phase masks those scores.
+  struct StepOps {
+    bf16x8 v[2];   // V^T blocks
+    bf16x8 k[2];   // K rows
+  };
+  enum { FIRST = 0, MID = 1, LAST = 2 };
+  auto matrix_phase = [&](auto parity, auto kind) __attribute__((always_inline)) {
+    constexpr int P = decltype(parity)::value;   // j & 1
+    constexpr int KIND = decltype(kind)::value;
+    constexpr bool DO_PV = KIND != FIRST;
+    constexpr bool DO_S = KIND != LAST;
+    constexpr int SUB = C::NDB / 2;              // steps per 16-key chunk
+    constexpr int NSTEP = 2 * NSB * SUB;
+    static_assert(C::NQC / 2 == 2 * SUB, "two score k-steps per step");
+    const char* vs = smem_raw + C::OFF_V + (P ^ 1) * C::TILE_BYTES;
+    const char* ks = smem_raw + P * C::TILE_BYTES;
+    // step t: chunk kc = t / SUB (sub-block kc / 2, half kc % 2), part u = t % SUB
+    auto load = [&](StepOps& o, int t) __attribute__((always_inline)) {
+      const int kc = t / SUB, u = t % SUB, sb = kc >> 1, half = kc & 1;
+      if constexpr (DO_PV) {
 #pragma unroll
-    for (int sb = 0; sb < C::NSB; ++sb) {
-      if (sb < nsb) {
-        bf16x8 a[C::NQC];
-#pragma unroll
-        for (int cc = 0; cc < C::NQC; ++cc)
-          a[cc] = *reinterpret_cast<const bf16x8*>(ks + kb[cc] + sb * 32 * C::ROW_BYTES);
-        const f32x16 zero = {};
-        s[sb] = mfma_32x32x16_bf16(a[0], qf[0], zero);
-#pragma unroll
-        for (int cc = 1; cc < C::NQC; ++cc) s[sb] = mfma_32x32x16_bf16(a[cc], qf[cc], s[sb]);
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[sb][r] = kNegInf;
+        for (int i = 0; i < 2; ++i) {
+          const int db = 2 * u + i;
+          const u32x2 lo = lds_read_tr16(vs + vaddr(db) + (16 * kc) * C::ROW_BYTES);
+          const u32x2 hi = lds_read_tr16(vs + vaddr(db) + (16 * kc + 8) * C::ROW_BYTES);
+          o.v[i] = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+        }
       }
+      if constexpr (DO_S) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          o.k[i] = *reinterpret_cast<const bf16x8*>(
+              ks + kaddr(half * (C::NQC / 2) + 2 * u + i) + sb * 32 * C::ROW_BYTES);
+      }
+    };
+    auto compute = [&](const StepOps& o, int t) __attribute__((always_inline)) {
+      const int kc = t / SUB, u = t % SUB, sb = kc >> 1, half = kc & 1;
+      if constexpr (DO_PV) {
+        const bf16x8 b = __builtin_bit_cast(
+            bf16x8, u32x4{pk[sb][4 * half + 0], pk[sb][4 * half + 1], pk[sb][4 * half + 2],
+                          pk[sb][4 * half + 3]});
+#pragma unroll
+        for (int i = 0; i < 2; ++i) acc[2 * u + i] = mfma_32x32x16_bf16(o.v[i], b, acc[2 * u + i]);
+      }
+      if constexpr (DO_S) {
+        if (half == 0 && u == 0) {
+          const f32x16 zero = {};
+          s[sb] = zero;
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          s[sb] = mfma_32x32x16_bf16(o.k[i], qf[half * (C::NQC / 2) + 2 * u + i], s[sb]);
+      }
+    };
+    __builtin_amdgcn_s_setprio(1);
+    StepOps ops[2];
+    load(ops[0], 0);
+#pragma unroll
+    for (int t = 0; t < NSTEP; ++t) {
+      if (t + 1 < NSTEP) load(ops[(t + 1) & 1], t + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(ops[t & 1], t);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_s_setprio(0);
+  };
 
-    // mask: register r of sub-block sb holds key k0 + 4h + off(sb, r) with
-    // off = 32sb + 8(r/4) + r%4; it is dead past the lane's limit (its own
-    // query under causal masking, and N - 1)
+  // P = exp2(s*c - m), rounded to bf16 into pk; returns this lane's fp32 sum
+  // of the unrounded p (the saved lse needs the unrounded sum: rounding each p
+  // to bf16 first moves ln(l) by up to 2^-9 on short rows).
+  auto probs = [&]() __attribute__((always_inline)) {
+    float part[4] = {0.f, 0.f, 0.f, 0.f};   // four partial sums: no serial add chain
+#pragma unroll
+    for (int sb = 0; sb < NSB; ++sb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][r], c, -m));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][r + 1], c, -m));
+        pk[sb][r >> 1] = pack_bf16x2(p0, p1);
+        part[(r >> 1) & 3] += p0 + p1;
+      }
+    return (part[0] + part[1]) + (part[2] + part[3]);
+  };
+
+  // Softmax phase of round j for tile j: mask, probabilities against the
+  // current m; if some lane's sum passed the bound, move m to the true running
+  // max (both halves of a query agree on it), rescale the accumulator and the
+  // running sum by exp2(m_old - m_new) ("LLM Architecture Refresh [3]",
+  // sections 2 and 4) and form the probabilities again.
+  auto softmax_phase = [&](int j) __attribute__((always_inline)) {
+    if (j < 0 || j >= nkt) return;
+    const int k0 = j * BN;
     if ((k0 + BN > N) || (CAUSAL && k0 + BN - 1 > wq0)) {
+      // register r of sub-block sb holds key k0 + 4h + off(sb, r) with
+      // off = 32sb + 8(r/4) + r%4; it is dead past the lane's limit (its own
+      // query under causal masking, and N - 1).  A tile wholly after the
+      // wave's queries gives p = 0 everywhere (m is finite from tile 0 on,
+      // which holds key 0).
       int lim = N - 1 - k0 - 4 * h;
       if (CAUSAL) lim = min(lim, qrow - k0 - 4 * h);
 #pragma unroll
-      for (int sb = 0; sb < C::NSB; ++sb)
+      for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int off = 32 * sb + 8 * (r >> 2) + (r & 3);
           s[sb][r] = off > lim ? kNegInf : s[sb][r];
         }
     }
-
-    float mx = kNegInf;
+    float ps = probs();
+    if (__any(ps > kSumBound)) {
+      float mx = kNegInf;
 #pragma unroll
-    for (int sb = 0; sb < C::NSB; ++sb)
+      for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sb][r]);
-    mx = fmaxf(mx, wave_xor32(mx));
-    const float m_new = fmaxf(m, mx * c);
-    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-    const float alpha = exp2f(m - m_use);
-
-    // P = exp2(s*c - m), summed in fp32 (the saved lse needs the unrounded
-    // sum: rounding each p to bf16 first moves ln(l) by up to 2^-9 on short
-    // rows), then rounded to bf16 for the PV product
-    uint32_t pk[C::NSB][8];
-    float ps = 0.f;
-#pragma unroll
-    for (int sb = 0; sb < C::NSB; ++sb)
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][r], c, -m_use));
-        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][r + 1], c, -m_use));
-        pk[sb][r >> 1] = pack_bf16x2(p0, p1);
-        ps += p0 + p1;
-      }
-    lsum = lsum * alpha + ps;
-    if (__any(alpha != 1.f)) {
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sb][r]);
+      mx = fmaxf(mx, wave_xor32(mx));
+      const float m_new = fmaxf(m, mx * c);
+      const float alpha = __builtin_amdgcn_exp2f(m - m_new);
 #pragma unroll
       for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+      lsum *= alpha;
+      m = m_new;
+      ps = probs();
     }
-    m = m_new;
+    lsum += ps;
+  };
 
-    // O^T += V^T P^T over the computed sub-blocks
-#pragma unroll
-    for (int sb = 0; sb < C::NSB; ++sb) {
-      if (sb < nsb) {
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int kc = 2 * sb + half;
-          const bf16x8 b = __builtin_bit_cast(
-              bf16x8, u32x4{pk[sb][4 * half + 0], pk[sb][4 * half + 1], pk[sb][4 * half + 2],
-                            pk[sb][4 * half + 3]});
-          bf16x8 a[C::NDB];
-#pragma unroll
-          for (int db = 0; db < C::NDB; ++db) {
-            const u32x2 lo = lds_read_tr16(vs + vb[db] + (16 * kc) * C::ROW_BYTES);
-            const u32x2 hi = lds_read_tr16(vs + vb[db] + (16 * kc + 8) * C::ROW_BYTES);
-            a[db] = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
-          }
-#pragma unroll
-          for (int db = 0; db < C::NDB; ++db) acc[db] = mfma_32x32x16_bf16(a[db], b, acc[db]);
-        }
-      }
+  // Rounds j = 0 .. nkt.  Group 0: matrix phase j, softmax phase j; group 1:
+  // softmax phase j - 1, matrix phase j.  At any time one wave of each SIMD
+  // issues matrix-core work and the other vector work.  The tiles a round
+  // reads were issued one round earlier and waited for at its end.
+  // The two groups run separate loops (the same number of barriers): inside
+  // one loop the scores are live across the back edge for one group and the
+  // probabilities for the other, and merging the two would keep both live.
+  auto round = [&](int j, auto parity, auto group, auto kind) __attribute__((always_inline)) {
+    if constexpr (decltype(group)::value == 1) {
+      if (j + 1 < nkt) issue(j + 1, 0u, Kb, koffA, koffB, rows_t{});
+      if (j < nkt) issue(j, (unsigned)C::OFF_V, Vb, voffA, voffB, tr_t{});
     }
+    if constexpr (decltype(group)::value == 0) {
+      matrix_phase(parity, kind);
+      phase_barrier();
+      softmax_phase(j);
+    } else {
+      softmax_phase(j - 1);
+      phase_barrier();
+      matrix_phase(parity, kind);
+    }
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's DMAs landed, its LDS reads done
+    phase_barrier();
+  };
+  using even = std::integral_constant<int, 0>;
+  using odd = std::integral_constant<int, 1>;
+  using first = std::integral_constant<int, FIRST>;
+  using mid = std::integral_constant<int, MID>;
+  using last = std::integral_constant<int, LAST>;
+  // rounds: 0 (scores only), 1 .. nkt-1, nkt (value product only)
+  auto run = [&](auto group) __attribute__((always_inline)) {
+    round(0, even{}, group, first{});
+    int j = 1;
+    for (; j + 1 < nkt; j += 2) {
+      round(j, odd{}, group, mid{});
+      round(j + 1, even{}, group, mid{});
+    }
+    if (j < nkt) {
+      round(j, odd{}, group, mid{});
+      ++j;
+    }
+    if (j & 1)
+      round(j, odd{}, group, last{});
+    else
+      round(j, even{}, group, last{});
+  };
+  wait_vmem();
+  phase_barrier();
+  if (nkt > 0) {
+    if (grp == 0)
+      run(std::integral_constant<int, 0>{});
+    else
+      run(std::integral_constant<int, 1>{});
   }
 
   // epilogue: one deferred division, then O and the log-sum-exp
@@ -361,7 +494,7 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_kernel(
   const float* Qh = Q + base;
   const float* Kh = K + base;
   const float* Vh = V + base;
-  const int q0 = qt * kBM;
+  const int q0 = qt * kBMF32;
   const int wq0 = q0 + 32 * w;
   const int qrow = wq0 + n;
 
@@ -373,7 +506,7 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_kernel(
     qf[i] = negq ? -x : x;
   }
 
-  const int kend = CAUSAL ? min(N, q0 + kBM) : N;
+  const int kend = CAUSAL ? min(N, q0 + kBMF32) : N;
   const int nkt = (kend + C::BN - 1) / C::BN;
 
   f32x16 acc[C::NDB];
@@ -487,7 +620,7 @@ hipError_t launch_bf16(const void* q, const void* k, const void* v, void* o, flo
   hipError_t e = hipFuncSetAttribute((const void*)kern,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, C::SMEM_BYTES);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(BH * nqt), dim3(256), C::SMEM_BYTES, stream,
+  hipLaunchKernelGGL(kern, dim3(BH * nqt), dim3(64 * kWaves), C::SMEM_BYTES, stream,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse,
                      BH, N, nqt, c, negq);
   return hipGetLastError();
@@ -497,7 +630,7 @@ template <int D, bool CAUSAL>
 hipError_t launch_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                       int BH, int N, float scale, hipStream_t stream) {
   using C = FwdF32Cfg<D>;
-  const int nqt = (N + kBM - 1) / kBM;
+  const int nqt = (N + kBMF32 - 1) / kBMF32;
   float c;
   int negq;
   split_scale(scale, &c, &negq);
@@ -517,8 +650,8 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
   if (d == 128)
     return causal ? launch_bf16<128, 64, true>(q, k, v, o, lse, BH, N, scale, stream)
                   : launch_bf16<128, 64, false>(q, k, v, o, lse, BH, N, scale, stream);
-  return causal ? launch_bf16<64, 128, true>(q, k, v, o, lse, BH, N, scale, stream)
-                : launch_bf16<64, 128, false>(q, k, v, o, lse, BH, N, scale, stream);
+  return causal ? launch_bf16<64, 64, true>(q, k, v, o, lse, BH, N, scale, stream)
+                : launch_bf16<64, 64, false>(q, k, v, o, lse, BH, N, scale, stream);
 }
 
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
