@@ -20,11 +20,14 @@
 //                   dS = P * (dP - D)
 //                   dK^T += Q^T dS             (MFMA)
 //                 and writes dS (bf16) to LDS.  At the start of the next
-//                 iteration each wave forms a 32x32 block of dQ = dS K from the
-//                 previous block's dS (double-buffered) and the key tile in LDS,
-//                 and adds it, times scale, into the fp32 accumulator with
-//                 hardware float atomics -- a whole iteration of work then hides
-//                 the atomics' latency, and one barrier per block suffices.
+//                 iteration each wave forms its share of dQ = dS K from the
+//                 previous block's dS (double-buffered) and the key tile in LDS
+//                 -- two 16x16 blocks over all the tile's keys at d = 64, two
+//                 32x32 blocks at d = 128, so every dQ element has one writer
+//                 per key tile -- and adds it, times scale, into the fp32
+//                 accumulator with hardware float atomics.  A whole iteration
+//                 of work then hides the atomics' latency, and one barrier per
+//                 block suffices.
 //                 Query blocks wholly before the key tile are skipped under
 //                 causal masking ("LLM Architecture Refresh [3]", section 7).
 //   3. bwd_dq:    dQ = bf16(accumulator).

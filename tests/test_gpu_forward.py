@@ -188,6 +188,27 @@ def test_large_scores_finite():
     assert np.max(np.abs(lse - rl)) <= TOL_LSE
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_running_max_grows_every_tile(causal, d):
+    """Key blocks of 64 with growing norm: the running max rises by ~10 natural
+    units per tile, so the rescale by exp(m_old - m_new) fires tile after tile
+    (P2 section 2), and the last block jumps by thousands of units (a
+    probability formed against the old max would overflow fp32)."""
+    N = 700
+    q, k, v = make_inputs(1, 2, N, d, torch.bfloat16, seed=15)
+    grow = torch.tensor([1.0 + 0.5 * (j // 64) for j in range(N)])
+    grow[640:] *= 20.0
+    k = (k.float() * grow[None, None, :, None]).to(torch.bfloat16)
+    o, lse = _run(q, k, v, causal, 1.0)
+    ro, rl = naive_fwd(_f64(q), _f64(k), _f64(v), 1.0, causal)
+    jumps = np.diff(rl[0, 0, ::64])
+    _say(f"   lse at every 64th row: {np.round(rl[0, 0, ::64], 1)}")
+    assert np.max(rl) > 1000
+    assert np.max(np.abs(o - ro)) <= TOL_BF16
+    assert np.max(np.abs(lse - rl)) <= TOL_LSE * max(1.0, np.max(np.abs(rl)) / 1000)
+
+
 @pytest.mark.parametrize("scale", [-0.2, 0.0, 2.0])
 def test_unusual_scales(scale):
     q, k, v = make_inputs(1, 2, 200, 64, torch.bfloat16, seed=13)
