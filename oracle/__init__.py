@@ -24,6 +24,9 @@ from .attention import (
     naive_fwd_rows,
     naive_bwd,
     visible_mask,
+    kv_head_of,
+    naive_fwd_gqa,
+    naive_bwd_gqa,
 )
 from .tiled import (
     online_normaliser,
@@ -39,6 +42,9 @@ __all__ = [
     "naive_fwd_rows",
     "naive_bwd",
     "visible_mask",
+    "kv_head_of",
+    "naive_fwd_gqa",
+    "naive_bwd_gqa",
     "online_normaliser",
     "tiled_fwd",
     "tiled_bwd",

@@ -187,3 +187,74 @@ def naive_bwd(q, k, v, do, scale: float, causal: bool = False,
         dq[idx], dk[idx], dv[idx] = _bwd_head(q[idx], k[idx], v[idx], do[idx],
                                               scale, causal, row_chunk)
     return dq, dk, dv
+
+
+# ---------------------------------------------------------------------------
+# Grouped-query attention
+#
+# The pages name multi-query and grouped-query attention as the fix for the
+# key/value cache ("LLM Architecture Refresh [3]", section 6, the table that
+# sets the KV cache against the score matrix; "Flash Attention, From First
+# Principles", "Honesty time", item 6) without defining them further.  The
+# reading taken: H query heads share Hkv key/value heads, H a multiple of Hkv,
+# and query head h uses key/value head h // (H // Hkv) (consecutive query
+# heads form a group).  Per query head the operation is exactly the one above.
+# ---------------------------------------------------------------------------
+
+def kv_head_of(h: int, H: int, Hkv: int) -> int:
+    """Key/value head serving query head h (groups of H // Hkv consecutive heads)."""
+    if Hkv < 1 or H % Hkv:
+        raise ValueError(f"H={H} is not a multiple of Hkv={Hkv}")
+    return h // (H // Hkv)
+
+
+def naive_fwd_gqa(q, k, v, scale: float, causal: bool = False,
+                  row_chunk: int = _DEFAULT_ROW_CHUNK):
+    """Exact attention with shared key/value heads.  Returns (O, lse), float64.
+
+    q: [B, H, N, d]; k, v: [B, Hkv, N, d].  Query head h attends with
+    key/value head kv_head_of(h, H, Hkv).
+    """
+    q = _as_f64(q)
+    k = _as_f64(k)
+    v = _as_f64(v)
+    B, H, n, _ = q.shape
+    Hkv = k.shape[1]
+    o = np.empty(q.shape[:-1] + (v.shape[-1],), dtype=np.float64)
+    lse = np.empty(q.shape[:-1], dtype=np.float64)
+    if n == 0:
+        return o, lse
+    for b in range(B):
+        for h in range(H):
+            g = kv_head_of(h, H, Hkv)
+            o[b, h], lse[b, h] = _fwd_head(q[b, h], k[b, g], v[b, g], float(scale),
+                                           causal, row_chunk)
+    return o, lse
+
+
+def naive_bwd_gqa(q, k, v, do, scale: float, causal: bool = False,
+                  row_chunk: int = _DEFAULT_ROW_CHUNK):
+    """Gradients of sum(O * dO) for O = naive_fwd_gqa(q, k, v).
+
+    A shared key/value head receives the sum of the gradients of every query
+    head that reads it (the chain rule through a shared input).
+    """
+    q = _as_f64(q)
+    k = _as_f64(k)
+    v = _as_f64(v)
+    do = _as_f64(do)
+    B, H, n, _ = q.shape
+    Hkv = k.shape[1]
+    dq = np.empty_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    if n == 0:
+        return dq, dk, dv
+    for b in range(B):
+        for h in range(H):
+            g = kv_head_of(h, H, Hkv)
+            dq[b, h], dk_h, dv_h = _bwd_head(q[b, h], k[b, g], v[b, g], do[b, h],
+                                             float(scale), causal, row_chunk)
+            dk[b, g] += dk_h
+            dv[b, g] += dv_h
+    return dq, dk, dv

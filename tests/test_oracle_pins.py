@@ -361,3 +361,45 @@ def test_sampled_rows_match_full_oracle(causal):
     o_r, l_r = naive_fwd_rows(q[pos], k, v, 0.5, causal, pos)
     np.testing.assert_allclose(o_r, o[pos], atol=1e-14)
     np.testing.assert_allclose(l_r, lse[pos], atol=1e-14)
+
+
+# --- grouped-query attention -------------------------------------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("H,Hkv", [(4, 2), (6, 1), (8, 4)])
+def test_gqa_matches_library_sdpa_and_autograd_float64(causal, H, Hkv):
+    """torch's float64 SDPA with enable_gqa (a library routine that repeats each
+    key/value head over consecutive query heads) and its autograd pin the
+    head map h -> h // (H // Hkv) and the summed dK, dV of a shared head."""
+    from oracle import naive_bwd_gqa, naive_fwd_gqa
+    rng = np.random.default_rng(21)
+    q = rng.standard_normal((2, H, 29, 8))
+    k, v = (rng.standard_normal((2, Hkv, 29, 8)) for _ in range(2))
+    do = rng.standard_normal(q.shape)
+    o, _ = naive_fwd_gqa(q, k, v, 0.35, causal)
+    dq, dk, dv = naive_bwd_gqa(q, k, v, do, 0.35, causal)
+    tq, tk, tv = (torch.from_numpy(x).requires_grad_(True) for x in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        tq, tk, tv, is_causal=causal, scale=0.35, enable_gqa=True)
+    ref.backward(torch.from_numpy(do))
+    assert np.max(np.abs(o - ref.detach().numpy())) < 1e-13
+    for mine, r in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+        assert np.max(np.abs(mine - r.numpy())) < 1e-12
+
+
+def test_gqa_with_one_query_head_per_kv_head_is_plain_attention():
+    from oracle import naive_bwd_gqa, naive_fwd_gqa
+    rng = np.random.default_rng(22)
+    q, k, v, do = (rng.standard_normal((1, 3, 20, 8)) for _ in range(4))
+    for a, b in zip(naive_fwd_gqa(q, k, v, 0.5, True), naive_fwd(q, k, v, 0.5, True)):
+        assert np.array_equal(a, b)
+    for a, b in zip(naive_bwd_gqa(q, k, v, do, 0.5, True),
+                    naive_bwd(q, k, v, do, 0.5, True)):
+        assert np.array_equal(a, b)
+
+
+def test_gqa_rejects_a_head_count_the_kv_heads_do_not_divide():
+    from oracle import naive_fwd_gqa
+    z = np.zeros((1, 3, 4, 8))
+    with pytest.raises(ValueError):
+        naive_fwd_gqa(z, np.zeros((1, 2, 4, 8)), np.zeros((1, 2, 4, 8)), 1.0)

@@ -93,3 +93,21 @@ def workload_inputs(w: Workload, with_do: bool = None):
         with_do = w.backward
     return make_inputs(w.B, w.H, w.N, w.d, w.torch_dtype, w.seed, with_do,
                        w.boost_every, w.boost)
+
+
+def make_gqa_inputs(B: int, H: int, Hkv: int, N: int, d: int, dtype=torch.bfloat16,
+                    seed: int = 0, with_do: bool = False):
+    """Grouped-query inputs: q (and dO) [B, H, N, d], k and v [B, Hkv, N, d].
+
+    Same recipe as ``make_inputs`` (torch.randn float32 in the order q, k, v,
+    dO, then the cast), with the key/value tensors drawn at their own head count.
+    """
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    q = torch.randn((B, H, N, d), generator=g, dtype=torch.float32)
+    k = torch.randn((B, Hkv, N, d), generator=g, dtype=torch.float32)
+    v = torch.randn((B, Hkv, N, d), generator=g, dtype=torch.float32)
+    out = [q.to(dtype), k.to(dtype), v.to(dtype)]
+    if with_do:
+        out.append(torch.randn((B, H, N, d), generator=g, dtype=torch.float32).to(dtype))
+    return tuple(out)
