@@ -6,9 +6,12 @@ kernels; this module only checks tensor metadata, allocates outputs with torch
 and passes raw device pointers and the current HIP stream.  There is no CPU
 fallback: if the library is missing, every call raises.
 
-Low-level entry points carry the C names (``fa_fwd``, ``fa_fwd_f32``,
-``fa_bwd``, ``fa_bwd_workspace_size``, ``fa_status_string``) and take
-preallocated tensors; ``forward``/``backward``/``attention`` allocate.
+Low-level entry points carry the C names (``fa_fwd``, ``fa_fwd_gqa``,
+``fa_fwd_f32``, ``fa_bwd``, ``fa_bwd_gqa``, ``fa_bwd_workspace_size``,
+``fa_status_string``) and take preallocated tensors;
+``forward``/``backward``/``attention`` allocate, and take key / value tensors
+with fewer heads than the queries (grouped-query attention) when the dtype is
+bf16.
 """
 
 from __future__ import annotations
@@ -22,7 +25,8 @@ import torch
 
 __all__ = [
     "FAError", "library_path", "load_library",
-    "fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_bwd_workspace_size", "fa_status_string",
+    "fa_fwd", "fa_fwd_gqa", "fa_fwd_f32", "fa_bwd", "fa_bwd_gqa", "fa_bwd_workspace_size",
+    "fa_status_string",
     "fa_bwd_preprocess", "fa_bwd_main", "fa_bwd_finalize",
     "forward", "backward", "attention",
     "FA_OK", "FA_ERR_NULL", "FA_ERR_SHAPE", "FA_ERR_HEADDIM", "FA_ERR_ALIGN",
@@ -70,6 +74,8 @@ def load_library():
     vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
     lib.fa_fwd.restype = i
+    lib.fa_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
+    lib.fa_fwd_gqa.restype = i
     lib.fa_fwd_f32.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
     lib.fa_fwd_f32.restype = i
     lib.fa_bwd_workspace_size.argtypes = [i, i, i, i]
@@ -77,6 +83,9 @@ def load_library():
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
                            i, i, i, i, i, f, vp]
     lib.fa_bwd.restype = i
+    lib.fa_bwd_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                               i, i, i, i, i, i, f, vp]
+    lib.fa_bwd_gqa.restype = i
     lib.fa_bwd_preprocess.argtypes = [vp, vp, vp, vp, ctypes.c_size_t, i, i, i, i, vp]
     lib.fa_bwd_preprocess.restype = i
     lib.fa_bwd_main.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
@@ -153,6 +162,33 @@ def fa_fwd(q, k, v, o, lse, causal: bool, scale: float, stream=None) -> None:
     _raise(st, "fa_fwd")
 
 
+def _kv_heads(q, k) -> int:
+    """Key / value head count of ``k`` against ``q`` [B, H, N, d]."""
+    B, H, N, d = _dims(q)
+    kd = _dims(k)
+    if kd[0] != B or kd[2:] != (N, d):
+        raise ValueError(f"k: shape {kd} does not match q {(B, H, N, d)} in B, N or d")
+    Hkv = kd[1]
+    if Hkv < 1 or Hkv > H or H % Hkv:
+        raise ValueError(f"query heads {H} are not a multiple of key/value heads {Hkv}")
+    return Hkv
+
+
+def fa_fwd_gqa(q, k, v, o, lse, causal: bool, scale: float, stream=None) -> None:
+    """bf16 forward with grouped-query attention: q, o [B,H,N,d]; k, v [B,Hkv,N,d]."""
+    B, H, N, d = _dims(q)
+    Hkv = _kv_heads(q, k) if H else k.shape[1]
+    for t, nm in ((q, "q"), (o, "o")):
+        _check(t, nm, (B, H, N, d), torch.bfloat16, q.device)
+    for t, nm in ((k, "k"), (v, "v")):
+        _check(t, nm, (B, Hkv, N, d), torch.bfloat16, q.device)
+    _check(lse, "lse", (B, H, N), torch.float32, q.device)
+    st = load_library().fa_fwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Hkv,
+                                   N, d, int(bool(causal)), float(scale),
+                                   _stream_handle(q.device, stream))
+    _raise(st, "fa_fwd_gqa")
+
+
 def fa_fwd_f32(q, k, v, o, lse, causal: bool, scale: float, stream=None) -> None:
     """fp32 forward into preallocated ``o`` [B,H,N,d] f32 and ``lse`` [B,H,N] f32."""
     B, H, N, d = _dims(q)
@@ -184,6 +220,25 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, causal: bool, scale: fl
                                B, H, N, d, int(bool(causal)), float(scale),
                                _stream_handle(q.device, stream))
     _raise(st, "fa_bwd")
+
+
+def fa_bwd_gqa(q, k, v, o, dout, lse, dq, dk, dv, workspace, causal: bool, scale: float,
+               stream=None) -> None:
+    """bf16 backward with grouped-query attention: q, o, dout, dq [B,H,N,d];
+    k, v, dk, dv [B,Hkv,N,d]; dk and dv sum over the query heads of a group."""
+    B, H, N, d = _dims(q)
+    Hkv = _kv_heads(q, k) if H else k.shape[1]
+    for t, nm in ((q, "q"), (o, "o"), (dout, "dout"), (dq, "dq")):
+        _check(t, nm, (B, H, N, d), torch.bfloat16, q.device)
+    for t, nm in ((k, "k"), (v, "v"), (dk, "dk"), (dv, "dv")):
+        _check(t, nm, (B, Hkv, N, d), torch.bfloat16, q.device)
+    _check(lse, "lse", (B, H, N), torch.float32, q.device)
+    nbytes = _ws_bytes(workspace, q.device)
+    st = load_library().fa_bwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+                                   _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), nbytes,
+                                   B, H, Hkv, N, d, int(bool(causal)), float(scale),
+                                   _stream_handle(q.device, stream))
+    _raise(st, "fa_bwd_gqa")
 
 
 def _ws_bytes(workspace, device):
@@ -234,13 +289,18 @@ def fa_bwd_finalize(dq, workspace, stream=None) -> None:
 
 def forward(q, k, v, causal: bool = False, scale: Optional[float] = None,
             stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """O, lse = exact attention of [B,H,N,d] bf16 or fp32 tensors on the GPU."""
+    """O, lse = exact attention of [B,H,N,d] bf16 or fp32 tensors on the GPU.
+
+    bf16 ``k`` and ``v`` may have fewer heads than ``q`` (grouped-query
+    attention, H a multiple of their head count)."""
     B, H, N, d = _dims(q)
     s = _default_scale(d, scale)
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     if q.dtype == torch.float32:
         fa_fwd_f32(q, k, v, o, lse, causal, s, stream)
+    elif k.dim() == 4 and k.shape[1] != H:
+        fa_fwd_gqa(q, k, v, o, lse, causal, s, stream)
     else:
         fa_fwd(q, k, v, o, lse, causal, s, stream)
     return o, lse
@@ -256,7 +316,10 @@ def backward(q, k, v, o, lse, do, causal: bool = False, scale: Optional[float] =
     dv = torch.empty_like(v)
     ws = torch.empty(max(1, fa_bwd_workspace_size(B, H, N, d)), dtype=torch.uint8,
                      device=q.device)
-    fa_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, causal, s, stream)
+    if k.dim() == 4 and k.shape[1] != H:
+        fa_bwd_gqa(q, k, v, o, do, lse, dq, dk, dv, ws, causal, s, stream)
+    else:
+        fa_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, causal, s, stream)
     return dq, dk, dv
 
 

@@ -58,24 +58,80 @@ bool any_alias(const Range* in, int nin, const Range* out, int nout) {
   return false;
 }
 
-}  // namespace
+// Grouped-query head counts: H query heads share Hkv key / value heads, each
+// key / value head serving H / Hkv consecutive query heads.
+int check_heads(int H, int Hkv) {
+  if (H == 0) return Hkv >= 0 ? FA_OK : FA_ERR_SHAPE;
+  if (Hkv < 1 || Hkv > H || H % Hkv != 0) return FA_ERR_SHAPE;
+  return FA_OK;
+}
 
-extern "C" {
-
-int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
-           int d, int causal, float scale, hipStream_t stream) {
+int fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+             int Hkv, int N, int d, int causal, float scale, hipStream_t stream) {
   size_t te = 0, re = 0;
   int st = check_common(B, H, N, d, scale, &te, &re);
+  if (st != FA_OK) return st;
+  st = check_heads(H, Hkv);
   if (st != FA_OK) return st;
   if (re == 0) return FA_OK;
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(lse))
     return FA_ERR_ALIGN;
   const size_t tb = te * 2;
-  const Range in[3] = {range_of(q, tb), range_of(k, tb), range_of(v, tb)};
+  const size_t kvb = tb / (size_t)(H / Hkv);
+  const Range in[3] = {range_of(q, tb), range_of(k, kvb), range_of(v, kvb)};
   const Range out[2] = {range_of(o, tb), range_of(lse, re * 4)};
   if (any_alias(in, 3, out, 2)) return FA_ERR_ALIAS;
-  return from_hip(fa::launch_fwd_bf16(q, k, v, o, lse, B * H, N, d, causal != 0, scale, stream));
+  return from_hip(
+      fa::launch_fwd_bf16(q, k, v, o, lse, B * H, N, d, H / Hkv, causal != 0, scale, stream));
+}
+
+int bwd_bf16(const void* q, const void* k, const void* v, const void* o, const void* dout,
+             const float* lse, void* dq, void* dk, void* dv, void* workspace,
+             size_t workspace_bytes, int B, int H, int Hkv, int N, int d, int causal, float scale,
+             hipStream_t stream) {
+  size_t te = 0, re = 0;
+  int st = check_common(B, H, N, d, scale, &te, &re);
+  if (st != FA_OK) return st;
+  st = check_heads(H, Hkv);
+  if (st != FA_OK) return st;
+  if (re == 0) return FA_OK;
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace)
+    return FA_ERR_NULL;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(dout) ||
+      misaligned(lse) || misaligned(dq) || misaligned(dk) || misaligned(dv) ||
+      misaligned(workspace))
+    return FA_ERR_ALIGN;
+  const size_t need = fa::bwd_workspace_bytes(B * H, N, d);
+  if (workspace_bytes < need) return FA_ERR_WORKSPACE;
+  const size_t tb = te * 2;
+  const size_t kvb = tb / (size_t)(H / Hkv);
+  const Range in[6] = {range_of(q, tb),    range_of(k, kvb),   range_of(v, kvb),
+                       range_of(o, tb),    range_of(dout, tb), range_of(lse, re * 4)};
+  const Range out[4] = {range_of(dq, tb), range_of(dk, kvb), range_of(dv, kvb),
+                        range_of(workspace, need)};
+  if (any_alias(in, 6, out, 4)) return FA_ERR_ALIAS;
+  const int BH = B * H;
+  hipError_t e = fa::launch_bwd_pre(o, dout, lse, workspace, BH, N, d, stream);
+  if (e == hipSuccess)
+    e = fa::launch_bwd_main(q, k, v, dout, dk, dv, workspace, BH, N, d, H / Hkv, causal != 0,
+                            scale, stream);
+  if (e == hipSuccess) e = fa::launch_bwd_finalize(dq, workspace, BH, N, d, stream);
+  return from_hip(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+           int d, int causal, float scale, hipStream_t stream) {
+  return fwd_bf16(q, k, v, o, lse, B, H, H, N, d, causal, scale, stream);
+}
+
+int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+               int Hkv, int N, int d, int causal, float scale, hipStream_t stream) {
+  return fwd_bf16(q, k, v, o, lse, B, H, Hkv, N, d, causal, scale, stream);
 }
 
 int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H,
@@ -104,31 +160,16 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
            const float* lse, void* dq, void* dk, void* dv, void* workspace,
            size_t workspace_bytes, int B, int H, int N, int d, int causal, float scale,
            hipStream_t stream) {
-  size_t te = 0, re = 0;
-  int st = check_common(B, H, N, d, scale, &te, &re);
-  if (st != FA_OK) return st;
-  if (re == 0) return FA_OK;
-  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace)
-    return FA_ERR_NULL;
-  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(dout) ||
-      misaligned(lse) || misaligned(dq) || misaligned(dk) || misaligned(dv) ||
-      misaligned(workspace))
-    return FA_ERR_ALIGN;
-  const size_t need = fa::bwd_workspace_bytes(B * H, N, d);
-  if (workspace_bytes < need) return FA_ERR_WORKSPACE;
-  const size_t tb = te * 2;
-  const Range in[6] = {range_of(q, tb),    range_of(k, tb),    range_of(v, tb),
-                       range_of(o, tb),    range_of(dout, tb), range_of(lse, re * 4)};
-  const Range out[4] = {range_of(dq, tb), range_of(dk, tb), range_of(dv, tb),
-                        range_of(workspace, need)};
-  if (any_alias(in, 6, out, 4)) return FA_ERR_ALIAS;
-  const int BH = B * H;
-  hipError_t e = fa::launch_bwd_pre(o, dout, lse, workspace, BH, N, d, stream);
-  if (e == hipSuccess)
-    e = fa::launch_bwd_main(q, k, v, dout, dk, dv, workspace, BH, N, d, causal != 0, scale,
-                            stream);
-  if (e == hipSuccess) e = fa::launch_bwd_finalize(dq, workspace, BH, N, d, stream);
-  return from_hip(e);
+  return bwd_bf16(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, H, N, d,
+                  causal, scale, stream);
+}
+
+int fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const void* dout,
+               const float* lse, void* dq, void* dk, void* dv, void* workspace,
+               size_t workspace_bytes, int B, int H, int Hkv, int N, int d, int causal,
+               float scale, hipStream_t stream) {
+  return bwd_bf16(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, Hkv, N, d,
+                  causal, scale, stream);
 }
 
 int fa_bwd_preprocess(const void* o, const void* dout, const float* lse, void* workspace,
@@ -166,8 +207,8 @@ int fa_bwd_main(const void* q, const void* k, const void* v, const void* dout, v
   const Range in[4] = {range_of(q, tb), range_of(k, tb), range_of(v, tb), range_of(dout, tb)};
   const Range out[3] = {range_of(dk, tb), range_of(dv, tb), range_of(workspace, need)};
   if (any_alias(in, 4, out, 3)) return FA_ERR_ALIAS;
-  return from_hip(fa::launch_bwd_main(q, k, v, dout, dk, dv, workspace, B * H, N, d, causal != 0,
-                                      scale, stream));
+  return from_hip(fa::launch_bwd_main(q, k, v, dout, dk, dv, workspace, B * H, N, d, 1,
+                                      causal != 0, scale, stream));
 }
 
 int fa_bwd_finalize(void* dq, const void* workspace, size_t workspace_bytes, int B, int H, int N,
@@ -190,7 +231,9 @@ const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "ok";
     case FA_ERR_NULL: return "a required pointer is NULL";
-    case FA_ERR_SHAPE: return "invalid shape (B, H or N negative, N too large, or size overflow)";
+    case FA_ERR_SHAPE:
+      return "invalid shape (B, H or N negative, N too large, size overflow, or H not a "
+             "multiple of Hkv)";
     case FA_ERR_HEADDIM: return "unsupported head dimension (must be 64 or 128)";
     case FA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
     case FA_ERR_ALIAS: return "an output overlaps an input or another output";

@@ -147,8 +147,8 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_main_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ L2, const float* __restrict__ Dv, float* __restrict__ dQacc,
-    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int BH, int N, int Npad, int nkt,
-    float scale, float c2) {
+    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int BHkv, int N, int Npad, int nkt,
+    int group, float scale, float c2) {
   using C = BwdCfg<D>;
   extern __shared__ __attribute__((aligned(1024))) char smem[];
 
@@ -158,18 +158,27 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_main_kernel(
   const int n = lane & 31;
   const int h = lane >> 5;
 
-  int bh, kt;
-  map_tile(blockIdx.x, BH, nkt, false, &bh, &kt);
-  const size_t base = (size_t)bh * (size_t)N * D;
-  const char* Qb = reinterpret_cast<const char*>(Q + base);
-  const char* Kb = reinterpret_cast<const char*>(K + base);
-  const char* Vb = reinterpret_cast<const char*>(V + base);
-  const char* dOb = reinterpret_cast<const char*>(dO + base);
-  const float* L2h = L2 + (size_t)bh * Npad;
-  const float* Dh = Dv + (size_t)bh * Npad;
-  // the head's slice of the fp32 dQ accumulator as a buffer resource
-  const __amdgpu_buffer_rsrc_t dq_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      dQacc + base, (short)0, (int)((unsigned)N * (unsigned)D * 4u), 0x00020000);
+  // The workgroup owns a key tile of one key / value head; with grouped-query
+  // attention the `group` query heads sharing it are processed one after the
+  // other, so dK and dV sum over them in registers (group = 1: plain
+  // multi-head attention).
+  int kvh, kt;
+  map_tile(blockIdx.x, BHkv, nkt, false, &kvh, &kt);
+  const size_t kvbase = (size_t)kvh * (size_t)N * D;
+  const char* Kb = reinterpret_cast<const char*>(K + kvbase);
+  const char* Vb = reinterpret_cast<const char*>(V + kvbase);
+  // per query head g of the group: its Q, dO, L2, D and dQ accumulator slice
+  auto qhead = [&](int g) { return (size_t)kvh * group + g; };
+  auto Qb_of = [&](int g) {
+    return reinterpret_cast<const char*>(Q + qhead(g) * (size_t)N * D);
+  };
+  auto dOb_of = [&](int g) {
+    return reinterpret_cast<const char*>(dO + qhead(g) * (size_t)N * D);
+  };
+  auto dq_rsrc_of = [&](int g) {
+    return __builtin_amdgcn_make_buffer_rsrc(dQacc + qhead(g) * (size_t)N * D, (short)0,
+                                             (int)((unsigned)N * (unsigned)D * 4u), 0x00020000);
+  };
 
   const int k0 = kt * C::KEYS;
   const int wk0 = k0 + 32 * w;   // this wave's first key
@@ -189,12 +198,19 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_main_kernel(
 
   const int nqb = (N + kBQ - 1) / kBQ;
   const int qb0 = CAUSAL ? k0 / kBQ : 0;
-  const int nit = nqb - qb0;
+  const int nit = nqb - qb0;       // query blocks per query head
+  const int ntot = group * nit;    // iterations: (query head, query block)
 
-  // DMA of query block qb0 + it (Q, dO rows clamped to N-1; L2 and D padded)
-  auto issue = [&](int it) {
-    const int q0 = (qb0 + it) * kBQ;
-    const unsigned st = lds0 + C::OFF_ST + (it & 1) * C::STAGE;
+  // DMA of iteration t: query block qb0 + t % nit of query head t / nit (Q, dO
+  // rows clamped to N-1; L2 and D padded)
+  auto issue = [&](int t) {
+    const int g = t / nit;
+    const int q0 = (qb0 + (t - g * nit)) * kBQ;
+    const char* Qb = Qb_of(g);
+    const char* dOb = dOb_of(g);
+    const float* L2h = L2 + qhead(g) * Npad;
+    const float* Dh = Dv + qhead(g) * Npad;
+    const unsigned st = lds0 + C::OFF_ST + (t & 1) * C::STAGE;
 #pragma unroll
     for (int j = 0; j < C::QDMA; ++j) {
       const int slot = (j * C::WAVES + w) * 64 + lane;
@@ -212,7 +228,7 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_main_kernel(
         dma16(Dh + q0, (lane - 16) * 16, st + 2 * C::QTILE);
     }
   };
-  issue(0);
+  if (ntot > 0) issue(0);
 
   // K and V as B operands (lane = key, 8 consecutive features per chunk)
   bf16x8 kf[C::NDC], vf[C::NDC];
@@ -267,9 +283,11 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_main_kernel(
   // branch-free case.  Key chunks past the causal limit hold dS = 0 (masked
   // P, or zeros written by waves with no visible key), so the k loop is
   // straight-line and only a block with no visible key at all is skipped.
-  auto dq_step = [&](int it) {
-    const int q0 = (qb0 + it) * kBQ;
-    const char* dsb = smem + C::OFF_DS + (it & 1) * C::DSTILE;
+  auto dq_step = [&](int t) {
+    const int gq = t / nit;
+    const int q0 = (qb0 + (t - gq * nit)) * kBQ;
+    const __amdgpu_buffer_rsrc_t dq_rsrc = dq_rsrc_of(gq);
+    const char* dsb = smem + C::OFF_DS + (t & 1) * C::DSTILE;
     const char* kt_lds = smem + C::OFF_K;
     if constexpr (C::DQ16) {
       const int g = lane >> 4;          // 16-lane group
@@ -357,20 +375,20 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_main_kernel(
     }
   };
 
-  for (int it = 0; it < nit; ++it) {
-    const int q0 = (qb0 + it) * kBQ;
-    // stage it landed for every lane; every wave is done with iteration it-1
+  for (int t = 0; t < ntot; ++t) {
+    const int q0 = (qb0 + (t % nit)) * kBQ;
+    // stage t landed for every lane; every wave is done with iteration t-1
     wait_vmem();
     __syncthreads();
-    if (it + 1 < nit) issue(it + 1);
-    if (it > 0) dq_step(it - 1);
+    if (t + 1 < ntot) issue(t + 1);
+    if (t > 0) dq_step(t - 1);
 
-    const char* st = smem + C::OFF_ST + (it & 1) * C::STAGE;
+    const char* st = smem + C::OFF_ST + (t & 1) * C::STAGE;
     const char* sQ = st;
     const char* sdO = st + C::QTILE;
     const float* sL2 = reinterpret_cast<const float*>(st + 2 * C::QTILE);
     const float* sD = sL2 + kBQ;
-    char* dsb = smem + C::OFF_DS + (it & 1) * C::DSTILE;
+    char* dsb = smem + C::OFF_DS + (t & 1) * C::DSTILE;
 
 #pragma unroll
     for (int qs = 0; qs < C::NQS; ++qs) {
@@ -450,12 +468,12 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_main_kernel(
   }
   wait_vmem();
   __syncthreads();
-  if (nit > 0) dq_step(nit - 1);
+  if (ntot > 0) dq_step(ntot - 1);
 
   // epilogue: dK = scale * dK^T acc, dV = dV^T acc (lane = key, registers = features)
   if (key < N) {
-    uint16_t* dkrow = dK + base + (size_t)key * D;
-    uint16_t* dvrow = dV + base + (size_t)key * D;
+    uint16_t* dkrow = dK + kvbase + (size_t)key * D;
+    uint16_t* dvrow = dV + kvbase + (size_t)key * D;
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
@@ -486,18 +504,19 @@ inline WsLayout ws_layout(void* ws, int BH, int N) {
 
 template <int D, bool CAUSAL>
 hipError_t launch_main(const void* q, const void* k, const void* v, const void* dout,
-                       const WsLayout& w, void* dk, void* dv, int BH, int N, float scale,
-                       hipStream_t stream) {
+                       const WsLayout& w, void* dk, void* dv, int BH, int N, int group,
+                       float scale, hipStream_t stream) {
   using C = BwdCfg<D>;
   const int nkt = (N + C::KEYS - 1) / C::KEYS;
+  const int BHkv = BH / group;
   auto kern = bwd_main_kernel<D, CAUSAL>;
   hipError_t e =
       hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::SMEM);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(BH * nkt), dim3(C::THREADS), C::SMEM, stream, (const uint16_t*)q,
-                     (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, w.l2, w.dv,
-                     w.dq, (uint16_t*)dk, (uint16_t*)dv, BH, N, pad_rows(N), nkt, scale,
-                     scale * kLog2e);
+  hipLaunchKernelGGL(kern, dim3(BHkv * nkt), dim3(C::THREADS), C::SMEM, stream,
+                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
+                     (const uint16_t*)dout, w.l2, w.dv, w.dq, (uint16_t*)dk, (uint16_t*)dv, BHkv, N,
+                     pad_rows(N), nkt, group, scale, scale * kLog2e);
   return hipGetLastError();
 }
 
@@ -526,14 +545,14 @@ hipError_t launch_bwd_pre(const void* o, const void* dout, const float* lse, voi
 }
 
 hipError_t launch_bwd_main(const void* q, const void* k, const void* v, const void* dout,
-                           void* dk, void* dv, void* ws, int BH, int N, int d, bool causal,
-                           float scale, hipStream_t stream) {
+                           void* dk, void* dv, void* ws, int BH, int N, int d, int group,
+                           bool causal, float scale, hipStream_t stream) {
   const WsLayout w = ws_layout(ws, BH, N);
   if (d == 128)
-    return causal ? launch_main<128, true>(q, k, v, dout, w, dk, dv, BH, N, scale, stream)
-                  : launch_main<128, false>(q, k, v, dout, w, dk, dv, BH, N, scale, stream);
-  return causal ? launch_main<64, true>(q, k, v, dout, w, dk, dv, BH, N, scale, stream)
-                : launch_main<64, false>(q, k, v, dout, w, dk, dv, BH, N, scale, stream);
+    return causal ? launch_main<128, true>(q, k, v, dout, w, dk, dv, BH, N, group, scale, stream)
+                  : launch_main<128, false>(q, k, v, dout, w, dk, dv, BH, N, group, scale, stream);
+  return causal ? launch_main<64, true>(q, k, v, dout, w, dk, dv, BH, N, group, scale, stream)
+                : launch_main<64, false>(q, k, v, dout, w, dk, dv, BH, N, group, scale, stream);
 }
 
 hipError_t launch_bwd_finalize(void* dq, const void* ws, int BH, int N, int d,

@@ -101,7 +101,7 @@ template <int D, int BN, bool CAUSAL>
 __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
-    int BH, int N, int nqt, float c, int negq) {
+    int BH, int N, int nqt, float c, int negq, int group) {
   using C = FwdCfg<D, BN>;
   constexpr int NSB = C::NSB;
   extern __shared__ __attribute__((aligned(1024))) char smem_raw[];
@@ -116,9 +116,13 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(
   int bh, qt;
   map_tile(blockIdx.x, BH, nqt, CAUSAL, &bh, &qt);
   const size_t base = (size_t)bh * (size_t)N * D;
+  // grouped-query attention: `group` consecutive query heads share one key /
+  // value head (1 for plain multi-head attention); the grid order keeps the
+  // query heads of a group on one XCD whenever the heads per XCD allow
+  const size_t kvbase = (size_t)(bh / group) * (size_t)N * D;
   const uint16_t* Qh = Q + base;
-  const char* Kb = reinterpret_cast<const char*>(K + base);
-  const char* Vb = reinterpret_cast<const char*>(V + base);
+  const char* Kb = reinterpret_cast<const char*>(K + kvbase);
+  const char* Vb = reinterpret_cast<const char*>(V + kvbase);
 
   // 32-query blocks alternate between the groups so both see the same share
   // of the causal diagonal.
@@ -610,7 +614,7 @@ inline void split_scale(float scale, float* c, int* negq) {
 
 template <int D, int BN, bool CAUSAL>
 hipError_t launch_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
-                       int N, float scale, hipStream_t stream) {
+                       int N, int group, float scale, hipStream_t stream) {
   using C = FwdCfg<D, BN>;
   const int nqt = (N + kBM - 1) / kBM;
   float c;
@@ -622,7 +626,7 @@ hipError_t launch_bf16(const void* q, const void* k, const void* v, void* o, flo
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(BH * nqt), dim3(64 * kWaves), C::SMEM_BYTES, stream,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse,
-                     BH, N, nqt, c, negq);
+                     BH, N, nqt, c, negq, group);
   return hipGetLastError();
 }
 
@@ -646,12 +650,13 @@ hipError_t launch_f32(const float* q, const float* k, const float* v, float* o, 
 }  // namespace
 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
-                           int BH, int N, int d, bool causal, float scale, hipStream_t stream) {
+                           int BH, int N, int d, int group, bool causal, float scale,
+                           hipStream_t stream) {
   if (d == 128)
-    return causal ? launch_bf16<128, 64, true>(q, k, v, o, lse, BH, N, scale, stream)
-                  : launch_bf16<128, 64, false>(q, k, v, o, lse, BH, N, scale, stream);
-  return causal ? launch_bf16<64, 64, true>(q, k, v, o, lse, BH, N, scale, stream)
-                : launch_bf16<64, 64, false>(q, k, v, o, lse, BH, N, scale, stream);
+    return causal ? launch_bf16<128, 64, true>(q, k, v, o, lse, BH, N, group, scale, stream)
+                  : launch_bf16<128, 64, false>(q, k, v, o, lse, BH, N, group, scale, stream);
+  return causal ? launch_bf16<64, 64, true>(q, k, v, o, lse, BH, N, group, scale, stream)
+                : launch_bf16<64, 64, false>(q, k, v, o, lse, BH, N, group, scale, stream);
 }
 
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,

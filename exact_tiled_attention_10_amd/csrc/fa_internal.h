@@ -8,8 +8,11 @@
 
 namespace fa {
 
+// BH = batch * query heads; `group` consecutive query heads share one key /
+// value head (K and V hold BH / group heads).
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
-                           int BH, int N, int d, bool causal, float scale, hipStream_t stream);
+                           int BH, int N, int d, int group, bool causal, float scale,
+                           hipStream_t stream);
 
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                           int BH, int N, int d, bool causal, float scale, hipStream_t stream);
@@ -21,9 +24,10 @@ hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float*
 size_t bwd_workspace_bytes(int BH, int N, int d);
 hipError_t launch_bwd_pre(const void* o, const void* dout, const float* lse, void* ws, int BH,
                           int N, int d, hipStream_t stream);
+// BH = batch * query heads; `group` query heads share each key / value head.
 hipError_t launch_bwd_main(const void* q, const void* k, const void* v, const void* dout,
-                           void* dk, void* dv, void* ws, int BH, int N, int d, bool causal,
-                           float scale, hipStream_t stream);
+                           void* dk, void* dv, void* ws, int BH, int N, int d, int group,
+                           bool causal, float scale, hipStream_t stream);
 hipError_t launch_bwd_finalize(void* dq, const void* ws, int BH, int N, int d,
                                hipStream_t stream);
 

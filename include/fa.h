@@ -54,7 +54,8 @@ extern "C" {
 enum {
   FA_OK = 0,
   FA_ERR_NULL = 1,      /* a required pointer is NULL                        */
-  FA_ERR_SHAPE = 2,     /* B, H or N negative, or N > FA_MAX_N, or overflow   */
+  FA_ERR_SHAPE = 2,     /* B, H or N negative, N > FA_MAX_N, overflow, or a
+                           head count H that Hkv does not divide             */
   FA_ERR_HEADDIM = 3,   /* d is not 64 or 128                                 */
   FA_ERR_ALIGN = 4,     /* a tensor pointer is not 16-byte aligned            */
   FA_ERR_ALIAS = 5,     /* an output overlaps an input or another output      */
@@ -84,6 +85,25 @@ enum {
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int H, int N, int d, int causal, float scale,
            hipStream_t stream);
+
+/*
+ * fa_fwd_gqa -- forward pass with grouped-query attention, bfloat16 tensors.
+ *
+ *   q, o        [B, H, N, d];  k, v  [B, Hkv, N, d];  lse [B, H, N].
+ *   Hkv         key / value heads, 1 <= Hkv <= H with H a multiple of Hkv
+ *               (Hkv = 1: multi-query attention; Hkv = H: same as fa_fwd).
+ *
+ * Query head h attends with key / value head h / (H / Hkv): each key / value
+ * head serves H / Hkv consecutive query heads.  The pages only name
+ * multi-query and grouped-query attention ("Flash Attention, From First
+ * Principles", "Honesty time -- the confession list", item 6; "LLM
+ * Architecture Refresh [3]", section 6, the KV-cache vs score-matrix table);
+ * the grouping is the usual consecutive one.  Otherwise exactly fa_fwd: same
+ * operation per head, rules, rounding and errors.
+ */
+int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int Hkv, int N, int d, int causal, float scale,
+               hipStream_t stream);
 
 /*
  * fa_fwd_f32 -- forward pass, float32 tensors end to end.
@@ -127,6 +147,24 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            const void* dout, const float* lse, void* dq, void* dk, void* dv,
            void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
            int causal, float scale, hipStream_t stream);
+
+/*
+ * fa_bwd_gqa -- backward pass with grouped-query attention, bfloat16 tensors.
+ *
+ *   q, o, dout, dq  [B, H, N, d];  k, v, dk, dv  [B, Hkv, N, d];  lse [B, H, N].
+ *   workspace       at least fa_bwd_workspace_size(B, H, N, d) bytes (it is
+ *                   sized by the query heads).
+ *
+ * The gradient of fa_fwd_gqa: dK and dV of a key / value head sum the
+ * contributions of the H / Hkv query heads that share it (the chain rule
+ * through the shared head); each workgroup owns a key tile of one key / value
+ * head and walks its query heads in turn, so the sum stays in registers.
+ * Otherwise exactly fa_bwd.
+ */
+int fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o,
+               const void* dout, const float* lse, void* dq, void* dk, void* dv,
+               void* workspace, size_t workspace_bytes, int B, int H, int Hkv,
+               int N, int d, int causal, float scale, hipStream_t stream);
 
 /*
  * The three stages fa_bwd runs, in order, on the same stream.  Calling them in

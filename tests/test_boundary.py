@@ -39,9 +39,9 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared_functions()
-    assert set(names) == {"fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_bwd_workspace_size",
-                          "fa_status_string", "fa_bwd_preprocess", "fa_bwd_main",
-                          "fa_bwd_finalize"}
+    assert set(names) == {"fa_fwd", "fa_fwd_gqa", "fa_fwd_f32", "fa_bwd", "fa_bwd_gqa",
+                          "fa_bwd_workspace_size", "fa_status_string", "fa_bwd_preprocess",
+                          "fa_bwd_main", "fa_bwd_finalize"}
     for nm in names:
         assert hasattr(lib, nm), nm
 
@@ -163,3 +163,30 @@ def test_backward_stages_reject_bad_arguments(lib):
     assert lib.fa_bwd_finalize(None, w, ws, 1, 2, 100, 64, None) == fa.FA_ERR_NULL
     assert lib.fa_bwd_finalize(w + 16, w, ws, 1, 2, 100, 64, None) == fa.FA_ERR_ALIAS
     assert lib.fa_bwd_finalize(A + 6 * MB + 2, w, ws, 1, 2, 100, 64, None) == fa.FA_ERR_ALIGN
+
+
+def test_gqa_entry_points_reject_bad_head_counts(lib):
+    f = lambda H, Hkv, **kw: lib.fa_fwd_gqa(  # noqa: E731
+        kw.get("q", A), kw.get("k", A + MB), A + 2 * MB, kw.get("o", A + 3 * MB), A + 4 * MB,
+        1, H, Hkv, 100, 64, 1, 0.125, None)
+    assert f(4, 0) == fa.FA_ERR_SHAPE
+    assert f(4, 3) == fa.FA_ERR_SHAPE            # 4 query heads do not split over 3
+    assert f(4, 8) == fa.FA_ERR_SHAPE            # more key/value heads than query heads
+    assert f(4, -1) == fa.FA_ERR_SHAPE
+    assert f(0, 1) == fa.FA_OK                   # no query heads: nothing to do
+    assert f(4, 2, q=None) == fa.FA_ERR_NULL
+    assert f(4, 2, o=A + 16) == fa.FA_ERR_ALIAS  # o over q
+    # k holds 2 heads of 100 x 64 bf16 (25.6 KB): an o just past it is fine,
+    # an o inside it is not
+    assert f(4, 2, k=A + 3 * MB - 2 * 100 * 64 * 2) != fa.FA_ERR_ALIAS
+    assert f(4, 2, k=A + 3 * MB - 2 * 100 * 64 * 2 + 16) == fa.FA_ERR_ALIAS
+    ws = lib.fa_bwd_workspace_size(1, 4, 100, 64)
+    b = lambda H, Hkv, **kw: lib.fa_bwd_gqa(  # noqa: E731
+        A, A + MB, A + 2 * MB, A + 3 * MB, A + 4 * MB, A + 5 * MB, A + 6 * MB,
+        kw.get("dk", A + 7 * MB), A + 8 * MB, A + 9 * MB, kw.get("wsb", ws), 1, H, Hkv, 100, 64,
+        1, 0.125, None)
+    assert b(4, 3) == fa.FA_ERR_SHAPE
+    assert b(4, 0) == fa.FA_ERR_SHAPE
+    assert b(4, 2, wsb=16) == fa.FA_ERR_WORKSPACE
+    assert b(4, 2, dk=A + 8 * MB - 16) == fa.FA_ERR_ALIAS   # dk runs into dv
+    assert b(0, 2) == fa.FA_OK
