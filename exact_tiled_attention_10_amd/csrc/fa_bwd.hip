@@ -22,12 +22,15 @@
 //                 and writes dS (bf16) to LDS.  At the start of the next
 //                 iteration each wave forms its share of dQ = dS K from the
 //                 previous block's dS (double-buffered) and the key tile in LDS
-//                 -- two 16x16 blocks over all the tile's keys at d = 64, two
-//                 32x32 blocks at d = 128, so every dQ element has one writer
-//                 per key tile -- and adds it, times scale, into the fp32
-//                 accumulator with hardware float atomics.  A whole iteration
-//                 of work then hides the atomics' latency, and one barrier per
-//                 block suffices.
+//                 -- 32x32 blocks over all the tile's keys (one per wave on
+//                 waves 0..3 at d = 64, two per wave at d = 128), so every dQ
+//                 element has one writer per key tile -- and adds it, times
+//                 scale, into the fp32 accumulator with hardware float
+//                 atomics; one barrier per block suffices.  The atomics are
+//                 the kernel's scarcest resource (measured: removing them
+//                 takes a quarter off its time at d = 64, half at d = 128):
+//                 their count, one per dQ element per key tile, is why the
+//                 key tiles are as large as the registers allow.
 //                 Query blocks wholly before the key tile are skipped under
 //                 causal masking ("LLM Architecture Refresh [3]", section 7).
 //   3. bwd_dq:    dQ = bf16(accumulator).
@@ -37,6 +40,8 @@
 // Every transposed A/B operand (dO^T, Q^T, K^T, dS with queries across lanes)
 // is read from a row-major LDS tile with ds_read_b64_tr_b16; no tile is ever
 // transposed in registers.
+#include <type_traits>
+
 #include "fa_common.h"
 #include "fa_internal.h"
 
@@ -128,17 +133,16 @@ struct BwdCfg {
   static constexpr int SMEM = OFF_DS + 2 * DSTILE;
   static constexpr int QDMA = QTILE / 16 / THREADS;       // DMAs per thread per tile
   static constexpr int KDMA = KTILE / 16 / THREADS;
-  // dQ = dS K.  d = 64 (8 waves): sixteen 16x16 blocks of the [kBQ, 64]
-  // tile, two per wave, each over all the tile's keys -- one owner per dQ
-  // element (two waves adding into the same lines at once cost more than the
-  // rest of the kernel).  d = 128 (4 waves): 32x32 blocks, two per wave.
-  static constexpr bool DQ16 = (D == 64);
+  // dQ = dS K in 32x32 blocks of the [kBQ, D] tile, each over all the tile's
+  // keys, so every dQ element has one owner (two waves adding into the same
+  // lines at once cost more than the rest of the kernel).  d = 64: the four
+  // blocks go to waves 0..3, one per SIMD (16x16 blocks on all eight waves
+  // read twice the LDS bytes per product); d = 128: two blocks per wave.
   static constexpr int NBLK = NQS * NDB;
-  static constexpr int KSPLIT = WAVES >= NBLK ? WAVES / NBLK : 1;
-  static constexpr int BPW = WAVES >= NBLK ? 1 : NBLK / WAVES;  // 32x32 blocks per wave
+  static constexpr int DQW = WAVES >= NBLK ? NBLK : WAVES;   // waves owning dQ blocks
+  static constexpr int BPW = NBLK / DQW;                     // blocks per owner
   static_assert(QDMA * THREADS * 16 == QTILE && KDMA * THREADS * 16 == KTILE, "DMA split");
-  static_assert(!DQ16 || (kBQ / 16) * (D / 16) == 2 * WAVES, "two 16x16 dQ blocks per wave");
-  static_assert(DQ16 || KSPLIT == 1, "one owner per dQ block");
+  static_assert(BPW * DQW == NBLK, "dQ block split");
   static_assert(SMEM <= 160 * 1024, "LDS budget");
 };
 
@@ -284,92 +288,49 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_main_kernel(
   // P, or zeros written by waves with no visible key), so the k loop is
   // straight-line and only a block with no visible key at all is skipped.
   auto dq_step = [&](int t) {
+    if (w >= C::DQW) return;
     const int gq = t / nit;
     const int q0 = (qb0 + (t - gq * nit)) * kBQ;
     const __amdgpu_buffer_rsrc_t dq_rsrc = dq_rsrc_of(gq);
     const char* dsb = smem + C::OFF_DS + (t & 1) * C::DSTILE;
     const char* kt_lds = smem + C::OFF_K;
-    if constexpr (C::DQ16) {
-      const int g = lane >> 4;          // 16-lane group
-      const int rrow = 8 * g + ((lane & 15) >> 2);
-      const int rcol = 4 * (lane & 3);
 #pragma unroll
-      for (int bi = 0; bi < 2; ++bi) {
-        const int b = 2 * w + bi;
-        const int qbase = 16 * (b / (D / 16));
-        const int dbase = 16 * (b % (D / 16));
-        const int qg0 = q0 + qbase;
-        if (CAUSAL && k0 > qg0 + 15) continue;
-        int aoff[2], boff[2];
+    for (int bi = 0; bi < C::BPW; ++bi) {
+      const int blk = w * C::BPW + bi;
+      const int qsq = blk / C::NDB;
+      const int dbq = blk % C::NDB;
+      const int qs0 = q0 + 32 * qsq;
+      if (CAUSAL && k0 > qs0 + 31) continue;
+      // SWZ_BOTH depends on row bits 1..3: the two 8-row halves differ
+      const int aoff0 = tile_off<C::CPRQ, SWZ_BOTH>(trow, 32 * qsq + tcol);
+      const int aoff1 = tile_off<C::CPRQ, SWZ_BOTH>(trow + 8, 32 * qsq + tcol);
+      const int boff0 = tile_off<C::CPRD, SWZ_BOTH>(trow, 32 * dbq + tcol);
+      const int boff1 = tile_off<C::CPRD, SWZ_BOTH>(trow + 8, 32 * dbq + tcol);
+      f32x16 acc = {};
 #pragma unroll
-        for (int rd = 0; rd < 2; ++rd) {
-          aoff[rd] = tile_off<C::CPRQ, SWZ_BOTH>(rrow + 4 * rd, qbase + rcol);
-          boff[rd] = tile_off<C::CPRD, SWZ_BOTH>(rrow + 4 * rd, dbase + rcol);
-        }
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < C::KEYS / 32; ++ks) {
-          const u32x2 a0 = lds_read_tr16(dsb + aoff[0] + 32 * ks * C::RBQ);
-          const u32x2 a1 = lds_read_tr16(dsb + aoff[1] + 32 * ks * C::RBQ);
-          const u32x2 b0 = lds_read_tr16(kt_lds + boff[0] + 32 * ks * C::RBD);
-          const u32x2 b1 = lds_read_tr16(kt_lds + boff[1] + 32 * ks * C::RBD);
-          acc = mfma_16x16x32_bf16(__builtin_bit_cast(bf16x8, u32x4{a0.x, a0.y, a1.x, a1.y}),
-                                   __builtin_bit_cast(bf16x8, u32x4{b0.x, b0.y, b1.x, b1.y}), acc);
-        }
-        // acc: lane = feature dbase + lane%16, registers = queries qg0 + 4g + r
-        const int voff = ((qg0 + 4 * g) * D + dbase + (lane & 15)) * 4;
-        if (qg0 + 15 < N) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(scale * acc[r], dq_rsrc, voff,
-                                                            r * D * 4, 0);
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (qg0 + 4 * g + r < N)
-              __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(scale * acc[r], dq_rsrc, voff,
-                                                              r * D * 4, 0);
-        }
+      for (int kc = 0; kc < C::KEYS / 16; ++kc) {
+        const u32x2 a0 = lds_read_tr16(dsb + aoff0 + (16 * kc) * C::RBQ);
+        const u32x2 a1 = lds_read_tr16(dsb + aoff1 + (16 * kc) * C::RBQ);
+        const u32x2 b0 = lds_read_tr16(kt_lds + boff0 + (16 * kc) * C::RBD);
+        const u32x2 b1 = lds_read_tr16(kt_lds + boff1 + (16 * kc) * C::RBD);
+        acc = mfma_32x32x16_bf16(__builtin_bit_cast(bf16x8, u32x4{a0.x, a0.y, a1.x, a1.y}),
+                                 __builtin_bit_cast(bf16x8, u32x4{b0.x, b0.y, b1.x, b1.y}),
+                                 acc);
       }
-    } else {
+      // acc: lane = feature 32*dbq + n, registers = queries qs0 + 4h + 8(r/4) + r%4
+      const int voff = ((qs0 + 4 * h) * D + 32 * dbq + n) * 4;
+      if (qs0 + 31 < N) {
 #pragma unroll
-      for (int bi = 0; bi < C::BPW; ++bi) {
-        const int blk = w * C::BPW + bi;
-        const int qsq = blk / C::NDB;
-        const int dbq = blk % C::NDB;
-        const int qs0 = q0 + 32 * qsq;
-        if (CAUSAL && k0 > qs0 + 31) continue;
-        // SWZ_BOTH depends on row bits 1..3: the two 8-row halves differ
-        const int aoff0 = tile_off<C::CPRQ, SWZ_BOTH>(trow, 32 * qsq + tcol);
-        const int aoff1 = tile_off<C::CPRQ, SWZ_BOTH>(trow + 8, 32 * qsq + tcol);
-        const int boff0 = tile_off<C::CPRD, SWZ_BOTH>(trow, 32 * dbq + tcol);
-        const int boff1 = tile_off<C::CPRD, SWZ_BOTH>(trow + 8, 32 * dbq + tcol);
-        f32x16 acc = {};
+        for (int r = 0; r < 16; ++r)
+          __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(
+              scale * acc[r], dq_rsrc, voff, (8 * (r >> 2) + (r & 3)) * D * 4, 0);
+      } else {
 #pragma unroll
-        for (int kc = 0; kc < C::KEYS / 16; ++kc) {
-          const u32x2 a0 = lds_read_tr16(dsb + aoff0 + (16 * kc) * C::RBQ);
-          const u32x2 a1 = lds_read_tr16(dsb + aoff1 + (16 * kc) * C::RBQ);
-          const u32x2 b0 = lds_read_tr16(kt_lds + boff0 + (16 * kc) * C::RBD);
-          const u32x2 b1 = lds_read_tr16(kt_lds + boff1 + (16 * kc) * C::RBD);
-          acc = mfma_32x32x16_bf16(__builtin_bit_cast(bf16x8, u32x4{a0.x, a0.y, a1.x, a1.y}),
-                                   __builtin_bit_cast(bf16x8, u32x4{b0.x, b0.y, b1.x, b1.y}),
-                                   acc);
-        }
-        // acc: lane = feature 32*dbq + n, registers = queries qs0 + 4h + 8(r/4) + r%4
-        const int voff = ((qs0 + 4 * h) * D + 32 * dbq + n) * 4;
-        if (qs0 + 31 < N) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
+        for (int r = 0; r < 16; ++r) {
+          const int qrow = qs0 + 4 * h + 8 * (r >> 2) + (r & 3);
+          if (qrow < N)
             __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(
                 scale * acc[r], dq_rsrc, voff, (8 * (r >> 2) + (r & 3)) * D * 4, 0);
-        } else {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int qrow = qs0 + 4 * h + 8 * (r >> 2) + (r & 3);
-            if (qrow < N)
-              __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(
-                  scale * acc[r], dq_rsrc, voff, (8 * (r >> 2) + (r & 3)) * D * 4, 0);
-          }
         }
       }
     }
@@ -420,21 +381,29 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_main_kernel(
           hi = key < N ? N - qs0 - 4 * h : -(1 << 30);
         }
         uint32_t pk[8];
+        // P and dS; the mask compares exist only in the masked instance (a
+        // branch-free select in every sub-block cost 4 VALU ops per score)
+        auto probs = [&](auto masked) __attribute__((always_inline)) {
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          float p2[2], ds2[2];
+          for (int r = 0; r < 16; r += 2) {
+            float p2[2], ds2[2];
 #pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int rr = r + u;
-            const int off = 8 * (rr >> 2) + (rr & 3);
-            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rr], c2, -l2v[rr >> 2][rr & 3]));
-            if (need_mask) p = (off < lo || off >= hi) ? 0.f : p;
-            p2[u] = p;
-            ds2[u] = p * (dp[rr] - ddv[rr >> 2][rr & 3]);
+            for (int u = 0; u < 2; ++u) {
+              const int rr = r + u;
+              const int off = 8 * (rr >> 2) + (rr & 3);
+              float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rr], c2, -l2v[rr >> 2][rr & 3]));
+              if constexpr (decltype(masked)::value) p = (off < lo || off >= hi) ? 0.f : p;
+              p2[u] = p;
+              ds2[u] = p * (dp[rr] - ddv[rr >> 2][rr & 3]);
+            }
+            pk[r >> 1] = pack_bf16x2(p2[0], p2[1]);
+            sk[r >> 1] = pack_bf16x2(ds2[0], ds2[1]);
           }
-          pk[r >> 1] = pack_bf16x2(p2[0], p2[1]);
-          sk[r >> 1] = pack_bf16x2(ds2[0], ds2[1]);
-        }
+        };
+        if (need_mask)
+          probs(std::true_type{});
+        else
+          probs(std::false_type{});
         // dV^T += dO^T P ; dK^T += Q^T dS  (k = the 16 queries of one half)
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
