@@ -27,6 +27,9 @@ from .attention import (
     kv_head_of,
     naive_fwd_gqa,
     naive_bwd_gqa,
+    visible_mask_kv,
+    naive_fwd_kv,
+    naive_bwd_kv,
 )
 from .tiled import (
     online_normaliser,
@@ -45,6 +48,9 @@ __all__ = [
     "kv_head_of",
     "naive_fwd_gqa",
     "naive_bwd_gqa",
+    "visible_mask_kv",
+    "naive_fwd_kv",
+    "naive_bwd_kv",
     "online_normaliser",
     "tiled_fwd",
     "tiled_bwd",

@@ -258,3 +258,93 @@ def naive_bwd_gqa(q, k, v, do, scale: float, causal: bool = False,
             dk[b, g] += dk_h
             dv[b, g] += dv_h
     return dq, dk, dv
+
+
+# ---------------------------------------------------------------------------
+# Queries and keys of different lengths (cross-attention, decode against a
+# key/value cache)
+#
+# The pages treat one length n for queries and keys ("LLM Architecture
+# Refresh [3]", the notes before the references: one forward pass over n
+# tokens, so the score matrix is square) and note that generation splits a
+# sequence into a prompt and generated tokens.  The reading taken for Nq query
+# rows against Nk keys: the queries are the LAST Nq positions of the
+# sequence, so with causal masking query i (0-based) sees key j iff
+# j <= i + (Nk - Nq) (bottom-right alignment; for Nq = Nk this is the j <= i
+# rule of section 5).  A query with no visible key (only possible when
+# Nq > Nk) has no probability mass: its output row is 0 and its log-sum-exp
+# is -inf, the identity of the block-merge law ("Flash Attention, From First
+# Principles", "The scaffold").
+# ---------------------------------------------------------------------------
+
+def visible_mask_kv(n_q: int, n_k: int, causal: bool) -> np.ndarray:
+    """Boolean [n_q, n_k] mask: key j visible to query i (bottom-right causal)."""
+    if not causal:
+        return np.ones((n_q, n_k), dtype=bool)
+    i = np.arange(n_q)[:, None]
+    j = np.arange(n_k)[None, :]
+    return j <= i + (n_k - n_q)
+
+
+def naive_fwd_kv(q, k, v, scale: float, causal: bool = False):
+    """Exact attention of Nq queries against Nk keys.  Returns (O, lse), float64.
+
+    q: [B, H, Nq, d]; k, v: [B, Hkv, Nk, d] with H a multiple of Hkv (query
+    head h reads key/value head h // (H // Hkv)).  Rows without a visible key
+    give O = 0 and lse = -inf.
+    """
+    q = _as_f64(q)
+    k = _as_f64(k)
+    v = _as_f64(v)
+    B, H, nq, _ = q.shape
+    Hkv, nk = k.shape[1], k.shape[2]
+    o = np.zeros(q.shape[:-1] + (v.shape[-1],), dtype=np.float64)
+    lse = np.full(q.shape[:-1], -np.inf, dtype=np.float64)
+    if nq == 0 or nk == 0:
+        return o, lse
+    mask = visible_mask_kv(nq, nk, causal)
+    live = mask.any(axis=1)
+    for b in range(B):
+        for h in range(H):
+            g = kv_head_of(h, H, Hkv)
+            s = float(scale) * (q[b, h] @ k[b, g].T)             # S = s Q K^T
+            s = np.where(mask, s, -np.inf)
+            m = np.max(s, axis=1, keepdims=True)
+            m = np.where(np.isfinite(m), m, 0.0)
+            e = np.exp(s - m)                                    # masked -> 0
+            l = np.sum(e, axis=1, keepdims=True)
+            l_safe = np.where(l > 0, l, 1.0)
+            o[b, h] = (e / l_safe) @ v[b, g]
+            lse[b, h] = np.where(live, (m + np.log(l_safe))[:, 0], -np.inf)
+    return o, lse
+
+
+def naive_bwd_kv(q, k, v, do, scale: float, causal: bool = False):
+    """Gradients of sum(O * dO) for O = naive_fwd_kv(q, k, v).
+
+    The softmax Jacobian per row as in ``naive_bwd``; rows with no visible key
+    contribute nothing.  Shared key/value heads sum their query heads' parts.
+    """
+    q = _as_f64(q)
+    k = _as_f64(k)
+    v = _as_f64(v)
+    do = _as_f64(do)
+    B, H, nq, _ = q.shape
+    Hkv, nk = k.shape[1], k.shape[2]
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    if nq == 0 or nk == 0:
+        return dq, dk, dv
+    mask = visible_mask_kv(nq, nk, causal)
+    for b in range(B):
+        for h in range(H):
+            g = kv_head_of(h, H, Hkv)
+            s = float(scale) * (q[b, h] @ k[b, g].T)
+            p = softmax_rows(np.where(mask, s, -np.inf))         # empty rows -> 0
+            dv[b, g] += p.T @ do[b, h]                           # dV = P^T dO
+            dp = do[b, h] @ v[b, g].T                            # dP = dO V^T
+            ds = p * (dp - np.sum(p * dp, axis=1, keepdims=True))
+            dq[b, h] = float(scale) * (ds @ k[b, g])             # dQ = s dS K
+            dk[b, g] += float(scale) * (ds.T @ q[b, h])          # dK = s dS^T Q
+    return dq, dk, dv

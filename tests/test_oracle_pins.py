@@ -403,3 +403,94 @@ def test_gqa_rejects_a_head_count_the_kv_heads_do_not_divide():
     z = np.zeros((1, 3, 4, 8))
     with pytest.raises(ValueError):
         naive_fwd_gqa(z, np.zeros((1, 2, 4, 8)), np.zeros((1, 2, 4, 8)), 1.0)
+
+
+# --- queries and keys of different lengths (bottom-right causal) -----------------
+
+def _sdpa_lower_right(q, k, v, do, scale, causal):
+    from torch.nn.attention.bias import causal_lower_right
+    import warnings
+    tq, tk, tv = (torch.from_numpy(x).requires_grad_(True) for x in (q, k, v))
+    with warnings.catch_warnings():
+        warnings.simplefilter("ignore")   # the library warns about rows with no key
+        mask = causal_lower_right(q.shape[-2], k.shape[-2]) if causal else None
+        o = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask,
+                                                             scale=scale)
+    o.backward(torch.from_numpy(do))
+    return o.detach().numpy(), tq.grad.numpy(), tk.grad.numpy(), tv.grad.numpy()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("nq,nk", [(1, 37), (5, 37), (16, 64), (37, 37), (40, 19)])
+def test_kv_matches_library_sdpa_lower_right_float64(nq, nk, causal):
+    """torch's float64 SDPA with its lower-right causal bias (a library routine)
+    pins the alignment j <= i + (Nk - Nq), forward and gradients."""
+    from oracle import naive_bwd_kv, naive_fwd_kv, visible_mask_kv
+    rng = np.random.default_rng(31)
+    q = rng.standard_normal((2, 3, nq, 8))
+    k, v = (rng.standard_normal((2, 3, nk, 8)) for _ in range(2))
+    do = rng.standard_normal(q.shape)
+    o, lse = naive_fwd_kv(q, k, v, 0.45, causal)
+    dq, dk, dv = naive_bwd_kv(q, k, v, do, 0.45, causal)
+    ro, rdq, rdk, rdv = _sdpa_lower_right(q, k, v, do, 0.45, causal)
+    live = visible_mask_kv(nq, nk, causal).any(axis=1)
+    # rows with visible keys agree with the library; empty rows are 0 / -inf
+    assert np.max(np.abs(o[..., live, :] - ro[..., live, :])) < 1e-13
+    assert np.all(o[..., ~live, :] == 0) and np.all(lse[..., ~live] == -np.inf)
+    assert np.all(np.isfinite(lse[..., live]))
+    for mine, ref in ((dq, rdq), (dk, rdk), (dv, rdv)):
+        ref = np.nan_to_num(ref)
+        assert np.max(np.abs(mine - ref)) < 1e-12
+
+
+def test_kv_with_equal_lengths_is_plain_attention():
+    from oracle import naive_bwd_kv, naive_fwd_kv
+    rng = np.random.default_rng(32)
+    q, k, v, do = (rng.standard_normal((1, 2, 23, 8)) for _ in range(4))
+    for causal in (False, True):
+        for a, b in zip(naive_fwd_kv(q, k, v, 0.3, causal), naive_fwd(q, k, v, 0.3, causal)):
+            assert np.max(np.abs(a - b)) < 1e-14
+        for a, b in zip(naive_bwd_kv(q, k, v, do, 0.3, causal),
+                        naive_bwd(q, k, v, do, 0.3, causal)):
+            assert np.max(np.abs(a - b)) < 1e-13
+
+
+def test_kv_gqa_matches_library_on_repeated_heads():
+    from oracle import naive_fwd_kv
+    rng = np.random.default_rng(33)
+    q = rng.standard_normal((1, 6, 9, 8))
+    k, v = (rng.standard_normal((1, 2, 30, 8)) for _ in range(2))
+    o, _ = naive_fwd_kv(q, k, v, 0.5, True)
+    kr, vr = (np.repeat(x, 3, axis=1) for x in (k, v))
+    ro, _, _, _ = _sdpa_lower_right(q, kr, vr, np.zeros_like(q), 0.5, True)
+    assert np.max(np.abs(o - ro)) < 1e-13
+
+
+def test_kv_block_merge_law():
+    """Attention over all keys equals the merge of two disjoint key blocks by
+    their log-sum-exps ("Flash Attention, From First Principles", "The
+    scaffold"): lse = log(e^lse1 + e^lse2), O = (e^lse1 O1 + e^lse2 O2) / e^lse.
+    This pins lse as the natural log-sum-exp of the scaled scores."""
+    from oracle import naive_fwd_kv
+    rng = np.random.default_rng(34)
+    q = rng.standard_normal((1, 1, 4, 8)) * 3
+    k, v = (rng.standard_normal((1, 1, 50, 8)) for _ in range(2))
+    o, lse = naive_fwd_kv(q, k, v, 0.7, False)
+    o1, l1 = naive_fwd_kv(q, k[:, :, :21], v[:, :, :21], 0.7, False)
+    o2, l2 = naive_fwd_kv(q, k[:, :, 21:], v[:, :, 21:], 0.7, False)
+    lm = np.logaddexp(l1, l2)
+    om = (np.exp(l1 - lm)[..., None] * o1 + np.exp(l2 - lm)[..., None] * o2)
+    assert np.max(np.abs(lm - lse)) < 1e-13
+    assert np.max(np.abs(om - o)) < 1e-13
+    # a single query row: lse is log sum_j exp(scale q.k_j), computed directly
+    direct = np.log(np.sum(np.exp(0.7 * (k[0, 0] @ q[0, 0, 2]))))
+    assert abs(direct - lse[0, 0, 2]) < 1e-12
+
+
+def test_kv_decode_row_sees_every_key():
+    from oracle import naive_fwd_kv
+    rng = np.random.default_rng(35)
+    q = rng.standard_normal((1, 2, 1, 8))
+    k, v = (rng.standard_normal((1, 2, 40, 8)) for _ in range(2))
+    for a, b in zip(naive_fwd_kv(q, k, v, 0.5, True), naive_fwd_kv(q, k, v, 0.5, False)):
+        assert np.array_equal(a, b)
