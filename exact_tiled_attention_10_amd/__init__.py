@@ -7,8 +7,9 @@ and passes raw device pointers and the current HIP stream.  There is no CPU
 fallback: if the library is missing, every call raises.
 
 Low-level entry points carry the C names (``fa_fwd``, ``fa_fwd_gqa``,
-``fa_fwd_f32``, ``fa_bwd``, ``fa_bwd_gqa``, ``fa_bwd_workspace_size``,
-``fa_status_string``) and take preallocated tensors;
+``fa_fwd_kv``, ``fa_fwd_kv_workspace_size``, ``fa_fwd_f32``, ``fa_bwd``,
+``fa_bwd_gqa``, ``fa_bwd_workspace_size``, ``fa_status_string``) and take
+preallocated tensors;
 ``forward``/``backward``/``attention`` allocate, and take key / value tensors
 with fewer heads than the queries (grouped-query attention) when the dtype is
 bf16.
@@ -25,8 +26,8 @@ import torch
 
 __all__ = [
     "FAError", "library_path", "load_library",
-    "fa_fwd", "fa_fwd_gqa", "fa_fwd_f32", "fa_bwd", "fa_bwd_gqa", "fa_bwd_workspace_size",
-    "fa_status_string",
+    "fa_fwd", "fa_fwd_gqa", "fa_fwd_kv", "fa_fwd_kv_workspace_size", "fa_fwd_f32",
+    "fa_bwd", "fa_bwd_gqa", "fa_bwd_workspace_size", "fa_status_string",
     "fa_bwd_preprocess", "fa_bwd_main", "fa_bwd_finalize",
     "forward", "backward", "attention",
     "FA_OK", "FA_ERR_NULL", "FA_ERR_SHAPE", "FA_ERR_HEADDIM", "FA_ERR_ALIGN",
@@ -76,6 +77,11 @@ def load_library():
     lib.fa_fwd.restype = i
     lib.fa_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
     lib.fa_fwd_gqa.restype = i
+    lib.fa_fwd_kv_workspace_size.argtypes = [i, i, i, i, i]
+    lib.fa_fwd_kv_workspace_size.restype = ctypes.c_size_t
+    lib.fa_fwd_kv.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i, i, i, i, i, i, i, f,
+                              vp]
+    lib.fa_fwd_kv.restype = i
     lib.fa_fwd_f32.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
     lib.fa_fwd_f32.restype = i
     lib.fa_bwd_workspace_size.argtypes = [i, i, i, i]
@@ -189,6 +195,35 @@ def fa_fwd_gqa(q, k, v, o, lse, causal: bool, scale: float, stream=None) -> None
     _raise(st, "fa_fwd_gqa")
 
 
+def fa_fwd_kv_workspace_size(B: int, H: int, Nq: int, Nk: int, d: int) -> int:
+    return int(load_library().fa_fwd_kv_workspace_size(B, H, Nq, Nk, d))
+
+
+def fa_fwd_kv(q, k, v, o, lse, workspace, causal: bool, scale: float, stream=None) -> None:
+    """bf16 forward of Nq queries against Nk keys (bottom-right causal):
+    q, o [B,H,Nq,d]; k, v [B,Hkv,Nk,d]; lse [B,H,Nq]; ``workspace`` a uint8
+    device tensor of at least ``fa_fwd_kv_workspace_size`` bytes (or None when
+    that is 0)."""
+    B, H, Nq, d = _dims(q)
+    kd = _dims(k)
+    Hkv, Nk = kd[1], kd[2]
+    if kd[0] != B or kd[3] != d:
+        raise ValueError(f"k: shape {kd} does not match q {(B, H, Nq, d)} in B or d")
+    if H and (Hkv < 1 or Hkv > H or H % Hkv):
+        raise ValueError(f"query heads {H} are not a multiple of key/value heads {Hkv}")
+    for t, nm in ((q, "q"), (o, "o")):
+        _check(t, nm, (B, H, Nq, d), torch.bfloat16, q.device)
+    for t, nm in ((k, "k"), (v, "v")):
+        _check(t, nm, (B, Hkv, Nk, d), torch.bfloat16, q.device)
+    _check(lse, "lse", (B, H, Nq), torch.float32, q.device)
+    nbytes = 0 if workspace is None else _ws_bytes(workspace, q.device)
+    st = load_library().fa_fwd_kv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                  _ptr(workspace), nbytes, B, H, Hkv, Nq, Nk, d,
+                                  int(bool(causal)), float(scale),
+                                  _stream_handle(q.device, stream))
+    _raise(st, "fa_fwd_kv")
+
+
 def fa_fwd_f32(q, k, v, o, lse, causal: bool, scale: float, stream=None) -> None:
     """fp32 forward into preallocated ``o`` [B,H,N,d] f32 and ``lse`` [B,H,N] f32."""
     B, H, N, d = _dims(q)
@@ -292,12 +327,17 @@ def forward(q, k, v, causal: bool = False, scale: Optional[float] = None,
     """O, lse = exact attention of [B,H,N,d] bf16 or fp32 tensors on the GPU.
 
     bf16 ``k`` and ``v`` may have fewer heads than ``q`` (grouped-query
-    attention, H a multiple of their head count)."""
+    attention, H a multiple of their head count) and another length than the
+    queries (the queries are then the last positions: bottom-right causal)."""
     B, H, N, d = _dims(q)
     s = _default_scale(d, scale)
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    if q.dtype == torch.float32:
+    if q.dtype != torch.float32 and k.dim() == 4 and k.shape[2] != N:
+        nb = fa_fwd_kv_workspace_size(B, H, N, k.shape[2], d)
+        ws = torch.empty(nb, dtype=torch.uint8, device=q.device) if nb else None
+        fa_fwd_kv(q, k, v, o, lse, ws, causal, s, stream)
+    elif q.dtype == torch.float32:
         fa_fwd_f32(q, k, v, o, lse, causal, s, stream)
     elif k.dim() == 4 and k.shape[1] != H:
         fa_fwd_gqa(q, k, v, o, lse, causal, s, stream)

@@ -120,9 +120,54 @@ int bwd_bf16(const void* q, const void* k, const void* v, const void* o, const v
   return from_hip(e);
 }
 
+// Nq query rows against Nk keys: sizes of q / o ([B, H, Nq, d]), k / v
+// ([B, Hkv, Nk, d]) and lse ([B, H, Nq]) in elements.
+int check_kv(int B, int H, int Hkv, int Nq, int Nk, int d, float scale, size_t* q_elems,
+             size_t* kv_elems, size_t* rows) {
+  size_t te = 0, re = 0;
+  int st = check_common(B, H, Nq, d, scale, &te, &re);
+  if (st != FA_OK) return st;
+  if (Nk < 0 || Nk > FA_MAX_N) return FA_ERR_SHAPE;
+  st = check_heads(H, Hkv);
+  if (st != FA_OK) return st;
+  *q_elems = te;
+  *rows = re;
+  *kv_elems = H > 0 ? (size_t)B * (size_t)Hkv * (size_t)Nk * (size_t)d : 0;
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t fa_fwd_kv_workspace_size(int B, int H, int Nq, int Nk, int d) {
+  size_t te = 0, re = 0;
+  if (check_common(B, H, Nq, d, 1.f, &te, &re) != FA_OK) return 0;
+  if (Nk < 0 || Nk > FA_MAX_N || re == 0) return 0;
+  return fa::fwd_workspace_bytes(B * H, Nq, Nk, d);
+}
+
+int fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
+              size_t workspace_bytes, int B, int H, int Hkv, int Nq, int Nk, int d, int causal,
+              float scale, hipStream_t stream) {
+  size_t qe = 0, kve = 0, re = 0;
+  int st = check_kv(B, H, Hkv, Nq, Nk, d, scale, &qe, &kve, &re);
+  if (st != FA_OK) return st;
+  if (re == 0) return FA_OK;
+  if (!q || !o || !lse || (Nk > 0 && (!k || !v))) return FA_ERR_NULL;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(lse) ||
+      misaligned(workspace))
+    return FA_ERR_ALIGN;
+  const size_t need = fa::fwd_workspace_bytes(B * H, Nq, Nk, d);
+  if (need > 0 && workspace_bytes < need) return FA_ERR_WORKSPACE;
+  if (need > 0 && !workspace) return FA_ERR_NULL;
+  const Range in[3] = {range_of(q, qe * 2), range_of(k, kve * 2), range_of(v, kve * 2)};
+  const Range out[3] = {range_of(o, qe * 2), range_of(lse, re * 4),
+                        range_of(workspace, need)};
+  if (any_alias(in, 3, out, 3)) return FA_ERR_ALIAS;
+  return from_hip(fa::launch_fwd_bf16_kv(q, k, v, o, lse, need > 0 ? workspace : nullptr, B * H,
+                                         Nq, Nk, d, H / Hkv, causal != 0, scale, stream));
+}
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
            int d, int causal, float scale, hipStream_t stream) {

@@ -8,7 +8,8 @@
 //   1. mints the score tile on the matrix cores, transposed: S^T = K Q^T, so
 //      each lane holds the scores of ONE query against 16 keys and its partner
 //      lane (32 away) the other 16 ("The scaffold": S_tile = Q_tile K_tile^T);
-//   2. masks keys past N and, on diagonal tiles, keys after the query;
+//   2. masks keys past the end and, on diagonal tiles, keys after the
+//      query's last visible key;
 //   3. forms P = exp(S - m) against its running max m, adds the row sums to
 //      the running sum l and rounds P to bf16; when a tile would push some p
 //      past a fixed bound, m first moves to the true running max and l and
@@ -37,6 +38,7 @@
 // stages deep.  Both tiles stay row-major in LDS (XOR-swizzled against bank
 // conflicts); the V^T operand of the PV product is read with the transposing
 // ds_read_b64_tr_b16, so no register shuffling is needed.
+#include <algorithm>
 #include <type_traits>
 
 #include "fa_common.h"
@@ -97,11 +99,30 @@ __device__ __forceinline__ unsigned dma_src_off(int i, int w, int lane, int k0, 
 // wait for outstanding memory transfers (prefetch DMAs stay in flight).
 __device__ __forceinline__ void phase_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
+// Problem of one launch.  Nq query rows against Nk keys per head; with causal
+// masking query i sees key j iff j <= i + koff (koff = Nk - Nq: the queries
+// are the last Nq positions).  The keys may be split into nsplit ranges of
+// klen keys, one workgroup per (query tile, range); each range's normalised
+// output and log-sum-exp go to Opart / Lpart (fp32) for fwd_merge_kernel.
+struct FwdArgs {
+  const uint16_t* Q;
+  const uint16_t* K;
+  const uint16_t* V;
+  uint16_t* O;
+  float* LSE;
+  float* Opart;   // [nsplit, BH, Nq, D] when nsplit > 1
+  float* Lpart;   // [nsplit, BH, Nq]
+  int BH, Nq, Nk, koff, nqt, nsplit, klen, group, negq;
+  float c;
+};
+
 template <int D, int BN, bool CAUSAL>
-__global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(
-    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-    const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
-    int BH, int N, int nqt, float c, int negq, int group) {
+__global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(const FwdArgs a) {
+  const uint16_t* __restrict__ Q = a.Q;
+  const uint16_t* __restrict__ K = a.K;
+  const uint16_t* __restrict__ V = a.V;
+  const int BH = a.BH, Nq = a.Nq, Nk = a.Nk, koff = a.koff, group = a.group;
+  const float c = a.c;
   using C = FwdCfg<D, BN>;
   constexpr int NSB = C::NSB;
   extern __shared__ __attribute__((aligned(1024))) char smem_raw[];
@@ -113,13 +134,20 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(
   const int n = lane & 31;
   const int h = lane >> 5;
 
-  int bh, qt;
-  map_tile(blockIdx.x, BH, nqt, CAUSAL, &bh, &qt);
-  const size_t base = (size_t)bh * (size_t)N * D;
+  int bh, qt, sp = 0;
+  {
+    int bid = blockIdx.x;
+    if (a.nsplit > 1) {
+      sp = bid % a.nsplit;
+      bid /= a.nsplit;
+    }
+    map_tile(bid, BH, a.nqt, CAUSAL, &bh, &qt);
+  }
+  const size_t base = (size_t)bh * (size_t)Nq * D;
   // grouped-query attention: `group` consecutive query heads share one key /
   // value head (1 for plain multi-head attention); the grid order keeps the
   // query heads of a group on one XCD whenever the heads per XCD allow
-  const size_t kvbase = (size_t)(bh / group) * (size_t)N * D;
+  const size_t kvbase = (size_t)(bh / group) * (size_t)Nk * D;
   const uint16_t* Qh = Q + base;
   const char* Kb = reinterpret_cast<const char*>(K + kvbase);
   const char* Vb = reinterpret_cast<const char*>(V + kvbase);
@@ -130,8 +158,11 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(
   const int wq0 = q0 + 32 * (2 * (w & 3) + grp);   // this wave's first query
   const int qrow = wq0 + n;                        // this lane's query
 
-  const int kend = CAUSAL ? min(N, q0 + kBM) : N;
-  const int nkt = (kend + BN - 1) / BN;
+  // this workgroup's keys: [kb, ke), cut at the tile's last visible key
+  const int kb = sp * a.klen;
+  int ke = min(Nk, kb + a.klen);
+  if (CAUSAL) ke = min(ke, q0 + kBM + koff);
+  const int nkt = ke > kb ? (ke - kb + BN - 1) / BN : 0;
 
   // DMA: tile t of K (V) goes to K (V) stage t & 1.  Round j issues K tile
   // j + 1 and V tile j; they land by the end of round j and are read in round
@@ -142,24 +173,24 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(
   // otherwise hold back the start of the other group's matrix phase.
   const unsigned ldsb = __builtin_amdgcn_readfirstlane(lds_addr(smem_raw));
   const int ws0 = w & 3, ws1 = ws0 + 4;   // the two DMA slots a group-1 wave fills
-  const unsigned koffA = dma_src_off<D, BN, SWZ_ROWS>(0, ws0, lane, 0, N, true);
-  const unsigned voffA = dma_src_off<D, BN, SWZ_TR>(0, ws0, lane, 0, N, true);
-  const unsigned koffB = dma_src_off<D, BN, SWZ_ROWS>(0, ws1, lane, 0, N, true);
-  const unsigned voffB = dma_src_off<D, BN, SWZ_TR>(0, ws1, lane, 0, N, true);
+  const unsigned koffA = dma_src_off<D, BN, SWZ_ROWS>(0, ws0, lane, 0, Nk, true);
+  const unsigned voffA = dma_src_off<D, BN, SWZ_TR>(0, ws0, lane, 0, Nk, true);
+  const unsigned koffB = dma_src_off<D, BN, SWZ_ROWS>(0, ws1, lane, 0, Nk, true);
+  const unsigned voffB = dma_src_off<D, BN, SWZ_TR>(0, ws1, lane, 0, Nk, true);
   auto issue_slot = [&](int t, int ws, unsigned lds_tensor, const char* gsrc, unsigned off0,
                         auto kind) __attribute__((always_inline)) {
     constexpr int KIND = decltype(kind)::value;
-    const int k0 = t * BN;
+    const int k0 = kb + t * BN;
     const char* g = gsrc + (size_t)k0 * D * 2;
     const unsigned st = ldsb + ws * 1024 + lds_tensor + (t & 1) * C::TILE_BYTES;
-    if (k0 + BN <= N) {
+    if (k0 + BN <= Nk) {
 #pragma unroll
       for (int i = 0; i < C::DMA; ++i)
         dma16(g + i * C::DMA_STRIDE, off0, st + i * C::DMA_STRIDE);
     } else {
 #pragma unroll
       for (int i = 0; i < C::DMA; ++i)
-        dma16(g, dma_src_off<D, BN, KIND>(i, ws, lane, k0, N, false), st + i * C::DMA_STRIDE);
+        dma16(g, dma_src_off<D, BN, KIND>(i, ws, lane, k0, Nk, false), st + i * C::DMA_STRIDE);
     }
   };
   auto issue = [&](int t, unsigned lds_tensor, const char* gsrc, unsigned offA, unsigned offB,
@@ -174,11 +205,11 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(
   // Q^T as the B operand: lane holds Q[qrow][16c + 8h .. 16c + 8h + 7].
   bf16x8 qf[C::NQC];
   {
-    const uint32_t flip = negq ? 0x80008000u : 0u;
+    const uint32_t flip = a.negq ? 0x80008000u : 0u;
 #pragma unroll
     for (int cc = 0; cc < C::NQC; ++cc) {
       u32x4 raw = {0u, 0u, 0u, 0u};
-      if (qrow < N) raw = *reinterpret_cast<const u32x4*>(Qh + (size_t)qrow * D + 16 * cc + 8 * h);
+      if (qrow < Nq) raw = *reinterpret_cast<const u32x4*>(Qh + (size_t)qrow * D + 16 * cc + 8 * h);
       raw ^= flip;
       qf[cc] = __builtin_bit_cast(bf16x8, raw);
     }
@@ -313,15 +344,15 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(
   // sections 2 and 4) and form the probabilities again.
   auto softmax_phase = [&](int j) __attribute__((always_inline)) {
     if (j < 0 || j >= nkt) return;
-    const int k0 = j * BN;
-    if ((k0 + BN > N) || (CAUSAL && k0 + BN - 1 > wq0)) {
+    const int k0 = kb + j * BN;
+    if ((k0 + BN > ke) || (CAUSAL && k0 + BN - 1 > wq0 + koff)) {
       // register r of sub-block sb holds key k0 + 4h + off(sb, r) with
-      // off = 32sb + 8(r/4) + r%4; it is dead past the lane's limit (its own
-      // query under causal masking, and N - 1).  A tile wholly after the
-      // wave's queries gives p = 0 everywhere (m is finite from tile 0 on,
-      // which holds key 0).
-      int lim = N - 1 - k0 - 4 * h;
-      if (CAUSAL) lim = min(lim, qrow - k0 - 4 * h);
+      // off = 32sb + 8(r/4) + r%4; it is dead past the lane's limit (the
+      // last key its query sees under causal masking, and ke - 1).  Scores
+      // of a tile with no visible key give p = 0: m is finite (kMInit or a
+      // real maximum), so exp2(-inf - m) = 0 and no rebase is triggered.
+      int lim = ke - 1 - k0 - 4 * h;
+      if (CAUSAL) lim = min(lim, qrow + koff - k0 - 4 * h);
 #pragma unroll
       for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
@@ -406,22 +437,81 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(
       run(std::integral_constant<int, 1>{});
   }
 
-  // epilogue: one deferred division, then O and the log-sum-exp
+  // epilogue: one deferred division, then O and the log-sum-exp.  A row
+  // that saw no key (only possible with Nq > Nk, or in a key range wholly
+  // after it) has l = 0: O = 0 and lse = -inf, the merge law's empty block.
   const float lt = lsum + wave_xor32(lsum);
-  const float inv = 1.f / lt;
-  if (qrow < N) {
-    uint16_t* orow = O + base + (size_t)qrow * D;
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  const float lse = lt > 0.f ? (m + __log2f(lt)) * kLn2 : kNegInf;
+  if (qrow < Nq) {
+    if (a.nsplit == 1) {
+      uint16_t* orow = a.O + base + (size_t)qrow * D;
 #pragma unroll
-    for (int db = 0; db < C::NDB; ++db)
+      for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = 32 * db + 8 * g + 4 * h;
-        u32x2 out = {pack_bf16x2(acc[db][4 * g + 0] * inv, acc[db][4 * g + 1] * inv),
-                     pack_bf16x2(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv)};
-        *reinterpret_cast<u32x2*>(orow + d0) = out;
-      }
-    if (h == 0) LSE[(size_t)bh * N + qrow] = (m + __log2f(lt)) * kLn2;
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = 32 * db + 8 * g + 4 * h;
+          u32x2 out = {pack_bf16x2(acc[db][4 * g + 0] * inv, acc[db][4 * g + 1] * inv),
+                       pack_bf16x2(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv)};
+          *reinterpret_cast<u32x2*>(orow + d0) = out;
+        }
+      if (h == 0) a.LSE[(size_t)bh * Nq + qrow] = lse;
+    } else {
+      const size_t prow = ((size_t)sp * BH + bh) * Nq + qrow;
+      float* orow = a.Opart + prow * D;
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = 32 * db + 8 * g + 4 * h;
+          f32x4 out = {acc[db][4 * g + 0] * inv, acc[db][4 * g + 1] * inv,
+                       acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv};
+          *reinterpret_cast<f32x4*>(orow + d0) = out;
+        }
+      if (h == 0) a.Lpart[prow] = lse;
+    }
   }
+}
+
+// Merge of the key ranges ("Flash Attention, From First Principles", "The
+// scaffold": blocks over disjoint keys combine through their log-sum-exps):
+// lse = log sum_s e^{lse_s}, O = sum_s e^{lse_s - lse} O_s.  Ranges with
+// lse_s = -inf weigh 0; a row with no visible key at all keeps O = 0 and
+// lse = -inf.  One thread per (row, 8 features).
+template <int D>
+__global__ __launch_bounds__(256) void fwd_merge_kernel(const float* __restrict__ Opart,
+                                                        const float* __restrict__ Lpart,
+                                                        uint16_t* __restrict__ O,
+                                                        float* __restrict__ LSE, int rows,
+                                                        int nsplit) {
+  constexpr int TPR = D / 8;
+  const size_t gid = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t row = gid / TPR;
+  const int part = (int)(gid % TPR);
+  if (row >= (size_t)rows) return;
+  float mx = kNegInf;
+  for (int s = 0; s < nsplit; ++s) mx = fmaxf(mx, Lpart[(size_t)s * rows + row]);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float den = 0.f;
+  if (mx != kNegInf) {
+    for (int s = 0; s < nsplit; ++s) {
+      const float wgt = __expf(Lpart[(size_t)s * rows + row] - mx);
+      den += wgt;
+      const f32x4* src = reinterpret_cast<const f32x4*>(Opart + ((size_t)s * rows + row) * D +
+                                                        part * 8);
+      const f32x4 x0 = src[0], x1 = src[1];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[i] += wgt * x0[i];
+        acc[4 + i] += wgt * x1[i];
+      }
+    }
+  }
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+  u32x4 out = {pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
+               pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv)};
+  *reinterpret_cast<u32x4*>(O + row * D + part * 8) = out;
+  if (part == 0) LSE[row] = den > 0.f ? mx + __logf(den) : kNegInf;
 }
 
 // ---------------------------------------------------------------------------
@@ -613,20 +703,20 @@ inline void split_scale(float scale, float* c, int* negq) {
 }
 
 template <int D, int BN, bool CAUSAL>
-hipError_t launch_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
-                       int N, int group, float scale, hipStream_t stream) {
+hipError_t launch_bf16(const FwdArgs& a, hipStream_t stream) {
   using C = FwdCfg<D, BN>;
-  const int nqt = (N + kBM - 1) / kBM;
-  float c;
-  int negq;
-  split_scale(scale, &c, &negq);
   auto kern = fwd_bf16_kernel<D, BN, CAUSAL>;
   hipError_t e = hipFuncSetAttribute((const void*)kern,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, C::SMEM_BYTES);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(BH * nqt), dim3(64 * kWaves), C::SMEM_BYTES, stream,
-                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse,
-                     BH, N, nqt, c, negq, group);
+  hipLaunchKernelGGL(kern, dim3(a.BH * a.nqt * a.nsplit), dim3(64 * kWaves), C::SMEM_BYTES, stream,
+                     a);
+  e = hipGetLastError();
+  if (e != hipSuccess || a.nsplit == 1) return e;
+  const size_t rows = (size_t)a.BH * a.Nq;
+  const size_t threads = rows * (D / 8);
+  hipLaunchKernelGGL(fwd_merge_kernel<D>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                     stream, a.Opart, a.Lpart, a.O, a.LSE, (int)rows, a.nsplit);
   return hipGetLastError();
 }
 
@@ -649,14 +739,69 @@ hipError_t launch_f32(const float* q, const float* k, const float* v, float* o, 
 
 }  // namespace
 
+// Key splitting: only when the query tiles alone leave the chip idle (fewer
+// than 256 workgroups) and a workspace is given.  Each range keeps at least
+// four key tiles so its DMA pipeline fills; the workgroup count aims at two
+// per CU.
+FwdSplit fwd_split(int BH, int Nq, int Nk, int d) {
+  FwdSplit sp{1, Nk};
+  const int bn = 64;
+  const long long tiles = (long long)BH * ((Nq + kBM - 1) / kBM);
+  if (tiles <= 0 || tiles >= 256 || Nk <= 0) return sp;
+  const int nkt = (Nk + bn - 1) / bn;
+  int ns = (int)((512 + tiles - 1) / tiles);
+  ns = std::min(ns, nkt / 4);
+  if (ns <= 1) return sp;
+  const int tiles_per = (nkt + ns - 1) / ns;
+  sp.klen = tiles_per * bn;
+  sp.nsplit = (Nk + sp.klen - 1) / sp.klen;
+  (void)d;
+  return sp;
+}
+
+size_t fwd_workspace_bytes(int BH, int Nq, int Nk, int d) {
+  const FwdSplit sp = fwd_split(BH, Nq, Nk, d);
+  if (sp.nsplit <= 1) return 0;
+  const size_t rows = (size_t)sp.nsplit * BH * Nq;
+  return (rows * d * 4 + 255) / 256 * 256 + rows * 4;
+}
+
+hipError_t launch_fwd_bf16_kv(const void* q, const void* k, const void* v, void* o, float* lse,
+                              void* ws, int BH, int Nq, int Nk, int d, int group, bool causal,
+                              float scale, hipStream_t stream) {
+  FwdArgs a;
+  a.Q = (const uint16_t*)q;
+  a.K = (const uint16_t*)k;
+  a.V = (const uint16_t*)v;
+  a.O = (uint16_t*)o;
+  a.LSE = lse;
+  a.BH = BH;
+  a.Nq = Nq;
+  a.Nk = Nk;
+  a.koff = Nk - Nq;
+  a.nqt = (Nq + kBM - 1) / kBM;
+  a.group = group;
+  split_scale(scale, &a.c, &a.negq);
+  FwdSplit sp{1, Nk};
+  if (ws) sp = fwd_split(BH, Nq, Nk, d);
+  a.nsplit = sp.nsplit;
+  a.klen = sp.nsplit > 1 ? sp.klen : (Nk > 0 ? Nk : 1);
+  a.Opart = nullptr;
+  a.Lpart = nullptr;
+  if (a.nsplit > 1) {
+    const size_t rows = (size_t)a.nsplit * BH * Nq;
+    a.Opart = (float*)ws;
+    a.Lpart = (float*)((char*)ws + (rows * d * 4 + 255) / 256 * 256);
+  }
+  if (d == 128)
+    return causal ? launch_bf16<128, 64, true>(a, stream) : launch_bf16<128, 64, false>(a, stream);
+  return causal ? launch_bf16<64, 64, true>(a, stream) : launch_bf16<64, 64, false>(a, stream);
+}
+
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                            int BH, int N, int d, int group, bool causal, float scale,
                            hipStream_t stream) {
-  if (d == 128)
-    return causal ? launch_bf16<128, 64, true>(q, k, v, o, lse, BH, N, group, scale, stream)
-                  : launch_bf16<128, 64, false>(q, k, v, o, lse, BH, N, group, scale, stream);
-  return causal ? launch_bf16<64, 64, true>(q, k, v, o, lse, BH, N, group, scale, stream)
-                : launch_bf16<64, 64, false>(q, k, v, o, lse, BH, N, group, scale, stream);
+  return launch_fwd_bf16_kv(q, k, v, o, lse, nullptr, BH, N, N, d, group, causal, scale, stream);
 }
 
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,

@@ -14,6 +14,19 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
                            int BH, int N, int d, int group, bool causal, float scale,
                            hipStream_t stream);
 
+// Nq query rows against Nk keys (bottom-right causal alignment).  With a
+// workspace of fwd_workspace_bytes(), the keys may be split across
+// workgroups and merged by a second kernel; with ws == nullptr never.
+struct FwdSplit {
+  int nsplit;
+  int klen;
+};
+FwdSplit fwd_split(int BH, int Nq, int Nk, int d);
+size_t fwd_workspace_bytes(int BH, int Nq, int Nk, int d);
+hipError_t launch_fwd_bf16_kv(const void* q, const void* k, const void* v, void* o, float* lse,
+                              void* ws, int BH, int Nq, int Nk, int d, int group, bool causal,
+                              float scale, hipStream_t stream);
+
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                           int BH, int N, int d, bool causal, float scale, hipStream_t stream);
 

@@ -106,6 +106,40 @@ int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
                hipStream_t stream);
 
 /*
+ * fa_fwd_kv -- forward pass of Nq queries against Nk keys (cross-attention,
+ * a prompt or generated tokens against a key/value cache), bfloat16 tensors.
+ *
+ *   q, o        [B, H, Nq, d];  k, v  [B, Hkv, Nk, d];  lse [B, H, Nq].
+ *   Hkv         key / value heads as in fa_fwd_gqa (Hkv = H: one per head).
+ *   Nq, Nk      0 <= Nq, Nk <= FA_MAX_N, independent.
+ *   causal      the queries are the LAST Nq positions of the sequence: query i
+ *               sees key j iff j <= i + (Nk - Nq) (bottom-right alignment;
+ *               for Nq = Nk exactly the rule of fa_fwd).  A query that sees
+ *               no key (with causal masking the first Nq - Nk queries when
+ *               Nq > Nk; every query when Nk = 0) gets O = 0 and lse = -inf.
+ *   workspace   device memory of at least fa_fwd_kv_workspace_size(B, H, Nq,
+ *               Nk, d) bytes, 16-byte aligned; may be NULL when that size is 0.
+ *
+ * The pages define attention for one length n ("LLM Architecture Refresh
+ * [3]", the notes before the references, which also point out that
+ * generation splits a sequence into a prompt and new tokens); the alignment
+ * above is the reading that places the queries at the end.  When the query
+ * tiles alone would leave most of the GPU idle (few heads, small Nq: decode),
+ * the keys are split into ranges handled by separate workgroups, each writing
+ * a normalised partial output and its log-sum-exp to the workspace, and a
+ * second kernel merges the ranges by the block law of "Flash Attention, From
+ * First Principles", "The scaffold": lse = log sum_r e^{lse_r},
+ * O = sum_r e^{lse_r - lse} O_r.  The result is the same exact attention.
+ * Errors as fa_fwd, plus FA_ERR_WORKSPACE for a workspace that is too small;
+ * k and v may be NULL when Nk == 0.
+ */
+size_t fa_fwd_kv_workspace_size(int B, int H, int Nq, int Nk, int d);
+int fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse,
+              void* workspace, size_t workspace_bytes, int B, int H, int Hkv,
+              int Nq, int Nk, int d, int causal, float scale,
+              hipStream_t stream);
+
+/*
  * fa_fwd_f32 -- forward pass, float32 tensors end to end.
  *
  * Same operation, layout and rules as fa_fwd with every tensor float32 and

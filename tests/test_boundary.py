@@ -39,9 +39,10 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared_functions()
-    assert set(names) == {"fa_fwd", "fa_fwd_gqa", "fa_fwd_f32", "fa_bwd", "fa_bwd_gqa",
-                          "fa_bwd_workspace_size", "fa_status_string", "fa_bwd_preprocess",
-                          "fa_bwd_main", "fa_bwd_finalize"}
+    assert set(names) == {"fa_fwd", "fa_fwd_gqa", "fa_fwd_kv", "fa_fwd_kv_workspace_size",
+                          "fa_fwd_f32", "fa_bwd", "fa_bwd_gqa", "fa_bwd_workspace_size",
+                          "fa_status_string", "fa_bwd_preprocess", "fa_bwd_main",
+                          "fa_bwd_finalize"}
     for nm in names:
         assert hasattr(lib, nm), nm
 
@@ -190,3 +191,42 @@ def test_gqa_entry_points_reject_bad_head_counts(lib):
     assert b(4, 2, wsb=16) == fa.FA_ERR_WORKSPACE
     assert b(4, 2, dk=A + 8 * MB - 16) == fa.FA_ERR_ALIAS   # dk runs into dv
     assert b(0, 2) == fa.FA_OK
+
+
+def test_kv_workspace_size(lib):
+    # plenty of query tiles: no key split, no workspace
+    assert lib.fa_fwd_kv_workspace_size(1, 32, 4096, 4096, 128) == 0
+    assert lib.fa_fwd_kv_workspace_size(1, 2, 100, -1, 64) == 0
+    assert lib.fa_fwd_kv_workspace_size(1, 2, 100, 100, 96) == 0
+    # decode (one query row per head): the keys are split, partials need room
+    ws = lib.fa_fwd_kv_workspace_size(1, 2, 1, 4096, 128)
+    assert ws > 0 and ws % 4 == 0
+    assert ws >= 2 * 2 * 1 * (128 + 1) * 4       # at least two ranges of O and lse
+
+
+def test_kv_forward_rejects_bad_arguments(lib):
+    ws_need = lib.fa_fwd_kv_workspace_size(1, 2, 1, 4096, 128)
+    W = A + 9 * MB
+
+    def f(**kw):
+        g = dict(q=A, k=A + MB, v=A + 2 * MB, o=A + 3 * MB, lse=A + 4 * MB, ws=W,
+                 wsb=ws_need, B=1, H=2, Hkv=2, Nq=1, Nk=4096, d=128, causal=1, scale=0.1)
+        g.update(kw)
+        return lib.fa_fwd_kv(g["q"], g["k"], g["v"], g["o"], g["lse"], g["ws"], g["wsb"],
+                             g["B"], g["H"], g["Hkv"], g["Nq"], g["Nk"], g["d"], g["causal"],
+                             g["scale"], None)
+    assert f(Nk=-1) == fa.FA_ERR_SHAPE
+    assert f(Nk=fa.FA_MAX_N + 1) == fa.FA_ERR_SHAPE
+    assert f(Nq=-1) == fa.FA_ERR_SHAPE
+    assert f(Hkv=3) == fa.FA_ERR_SHAPE
+    assert f(d=80) == fa.FA_ERR_HEADDIM
+    assert f(scale=math.nan) == fa.FA_ERR_SCALE
+    assert f(k=None) == fa.FA_ERR_NULL
+    assert f(ws=None) == fa.FA_ERR_NULL
+    assert f(wsb=ws_need - 4) == fa.FA_ERR_WORKSPACE
+    assert f(ws=W + 8) == fa.FA_ERR_ALIGN
+    assert f(ws=A + MB + 64) == fa.FA_ERR_ALIAS      # workspace over k
+    assert f(lse=A + 3 * MB + 16) == fa.FA_ERR_ALIAS  # lse inside o
+    assert f(Nq=0, q=None, o=None) == fa.FA_OK        # nothing to compute
+    # with no keys, k and v may be NULL: the call gets past the pointer checks
+    assert f(Nk=0, k=None, v=None, ws=None, wsb=0, d=96) == fa.FA_ERR_HEADDIM
