@@ -8,7 +8,7 @@ fallback: if the library is missing, every call raises.
 
 Low-level entry points carry the C names (``fa_fwd``, ``fa_fwd_gqa``,
 ``fa_fwd_kv``, ``fa_fwd_kv_workspace_size``, ``fa_fwd_f32``, ``fa_bwd``,
-``fa_bwd_gqa``, ``fa_bwd_workspace_size``, ``fa_status_string``) and take
+``fa_bwd_gqa``, ``fa_bwd_kv``, ``fa_bwd_workspace_size``, ``fa_status_string``) and take
 preallocated tensors;
 ``forward``/``backward``/``attention`` allocate, and take key / value tensors
 with fewer heads than the queries (grouped-query attention) when the dtype is
@@ -27,7 +27,7 @@ import torch
 __all__ = [
     "FAError", "library_path", "load_library",
     "fa_fwd", "fa_fwd_gqa", "fa_fwd_kv", "fa_fwd_kv_workspace_size", "fa_fwd_f32",
-    "fa_bwd", "fa_bwd_gqa", "fa_bwd_workspace_size", "fa_status_string",
+    "fa_bwd", "fa_bwd_gqa", "fa_bwd_kv", "fa_bwd_workspace_size", "fa_status_string",
     "fa_bwd_preprocess", "fa_bwd_main", "fa_bwd_finalize",
     "forward", "backward", "attention",
     "FA_OK", "FA_ERR_NULL", "FA_ERR_SHAPE", "FA_ERR_HEADDIM", "FA_ERR_ALIGN",
@@ -92,6 +92,9 @@ def load_library():
     lib.fa_bwd_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
                                i, i, i, i, i, i, f, vp]
     lib.fa_bwd_gqa.restype = i
+    lib.fa_bwd_kv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                              i, i, i, i, i, i, i, f, vp]
+    lib.fa_bwd_kv.restype = i
     lib.fa_bwd_preprocess.argtypes = [vp, vp, vp, vp, ctypes.c_size_t, i, i, i, i, vp]
     lib.fa_bwd_preprocess.restype = i
     lib.fa_bwd_main.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
@@ -276,6 +279,30 @@ def fa_bwd_gqa(q, k, v, o, dout, lse, dq, dk, dv, workspace, causal: bool, scale
     _raise(st, "fa_bwd_gqa")
 
 
+def fa_bwd_kv(q, k, v, o, dout, lse, dq, dk, dv, workspace, causal: bool, scale: float,
+              stream=None) -> None:
+    """bf16 backward of ``fa_fwd_kv``: q, o, dout, dq [B,H,Nq,d]; k, v, dk, dv
+    [B,Hkv,Nk,d]; ``workspace`` of at least ``fa_bwd_workspace_size(B, H, Nq, d)``."""
+    B, H, Nq, d = _dims(q)
+    kd = _dims(k)
+    Hkv, Nk = kd[1], kd[2]
+    if kd[0] != B or kd[3] != d:
+        raise ValueError(f"k: shape {kd} does not match q {(B, H, Nq, d)} in B or d")
+    if H and (Hkv < 1 or Hkv > H or H % Hkv):
+        raise ValueError(f"query heads {H} are not a multiple of key/value heads {Hkv}")
+    for t, nm in ((q, "q"), (o, "o"), (dout, "dout"), (dq, "dq")):
+        _check(t, nm, (B, H, Nq, d), torch.bfloat16, q.device)
+    for t, nm in ((k, "k"), (v, "v"), (dk, "dk"), (dv, "dv")):
+        _check(t, nm, (B, Hkv, Nk, d), torch.bfloat16, q.device)
+    _check(lse, "lse", (B, H, Nq), torch.float32, q.device)
+    nbytes = _ws_bytes(workspace, q.device)
+    st = load_library().fa_bwd_kv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+                                  _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), nbytes,
+                                  B, H, Hkv, Nq, Nk, d, int(bool(causal)), float(scale),
+                                  _stream_handle(q.device, stream))
+    _raise(st, "fa_bwd_kv")
+
+
 def _ws_bytes(workspace, device):
     if workspace.device != device or not workspace.is_contiguous():
         raise ValueError("workspace: must be a contiguous tensor on q's device")
@@ -356,7 +383,9 @@ def backward(q, k, v, o, lse, do, causal: bool = False, scale: Optional[float] =
     dv = torch.empty_like(v)
     ws = torch.empty(max(1, fa_bwd_workspace_size(B, H, N, d)), dtype=torch.uint8,
                      device=q.device)
-    if k.dim() == 4 and k.shape[1] != H:
+    if k.dim() == 4 and k.shape[2] != N:
+        fa_bwd_kv(q, k, v, o, do, lse, dq, dk, dv, ws, causal, s, stream)
+    elif k.dim() == 4 and k.shape[1] != H:
         fa_bwd_gqa(q, k, v, o, do, lse, dq, dk, dv, ws, causal, s, stream)
     else:
         fa_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, causal, s, stream)

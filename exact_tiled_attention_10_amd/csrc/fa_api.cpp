@@ -88,35 +88,43 @@ int fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, i
 
 int bwd_bf16(const void* q, const void* k, const void* v, const void* o, const void* dout,
              const float* lse, void* dq, void* dk, void* dv, void* workspace,
-             size_t workspace_bytes, int B, int H, int Hkv, int N, int d, int causal, float scale,
-             hipStream_t stream) {
+             size_t workspace_bytes, int B, int H, int Hkv, int Nq, int Nk, int d, int causal,
+             float scale, hipStream_t stream) {
   size_t te = 0, re = 0;
-  int st = check_common(B, H, N, d, scale, &te, &re);
+  int st = check_common(B, H, Nq, d, scale, &te, &re);
   if (st != FA_OK) return st;
+  if (Nk < 0 || Nk > FA_MAX_N) return FA_ERR_SHAPE;
   st = check_heads(H, Hkv);
   if (st != FA_OK) return st;
-  if (re == 0) return FA_OK;
-  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace)
+  const size_t kve = H > 0 ? (size_t)B * (size_t)Hkv * (size_t)Nk * (size_t)d : 0;
+  if (re == 0 && kve == 0) return FA_OK;
+  const bool has_q = re > 0, has_k = kve > 0;
+  if ((has_q && (!q || !o || !dout || !lse || !dq || !workspace)) ||
+      (has_k && (!k || !v || !dk || !dv)))
     return FA_ERR_NULL;
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(dout) ||
       misaligned(lse) || misaligned(dq) || misaligned(dk) || misaligned(dv) ||
       misaligned(workspace))
     return FA_ERR_ALIGN;
-  const size_t need = fa::bwd_workspace_bytes(B * H, N, d);
+  const size_t need = fa::bwd_workspace_bytes(B * H, Nq, d);
   if (workspace_bytes < need) return FA_ERR_WORKSPACE;
-  const size_t tb = te * 2;
-  const size_t kvb = tb / (size_t)(H / Hkv);
+  const size_t tb = te * 2, kvb = kve * 2;
   const Range in[6] = {range_of(q, tb),    range_of(k, kvb),   range_of(v, kvb),
                        range_of(o, tb),    range_of(dout, tb), range_of(lse, re * 4)};
   const Range out[4] = {range_of(dq, tb), range_of(dk, kvb), range_of(dv, kvb),
                         range_of(workspace, need)};
   if (any_alias(in, 6, out, 4)) return FA_ERR_ALIAS;
   const int BH = B * H;
-  hipError_t e = fa::launch_bwd_pre(o, dout, lse, workspace, BH, N, d, stream);
-  if (e == hipSuccess)
-    e = fa::launch_bwd_main(q, k, v, dout, dk, dv, workspace, BH, N, d, H / Hkv, causal != 0,
-                            scale, stream);
-  if (e == hipSuccess) e = fa::launch_bwd_finalize(dq, workspace, BH, N, d, stream);
+  hipError_t e = hipSuccess;
+  if (has_q) e = fa::launch_bwd_pre(o, dout, lse, workspace, BH, Nq, d, stream);
+  if (e == hipSuccess && has_k) {
+    if (has_q)
+      e = fa::launch_bwd_main(q, k, v, dout, dk, dv, workspace, BH, Nq, Nk, d, H / Hkv,
+                              causal != 0, scale, stream);
+    else   // no queries: every key's gradient is 0
+      e = fa::launch_zero_bf16(dk, dv, kve, stream);
+  }
+  if (e == hipSuccess && has_q) e = fa::launch_bwd_finalize(dq, workspace, BH, Nq, d, stream);
   return from_hip(e);
 }
 
@@ -205,16 +213,24 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
            const float* lse, void* dq, void* dk, void* dv, void* workspace,
            size_t workspace_bytes, int B, int H, int N, int d, int causal, float scale,
            hipStream_t stream) {
-  return bwd_bf16(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, H, N, d,
-                  causal, scale, stream);
+  return bwd_bf16(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, H, N, N,
+                  d, causal, scale, stream);
 }
 
 int fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const void* dout,
                const float* lse, void* dq, void* dk, void* dv, void* workspace,
                size_t workspace_bytes, int B, int H, int Hkv, int N, int d, int causal,
                float scale, hipStream_t stream) {
-  return bwd_bf16(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, Hkv, N, d,
-                  causal, scale, stream);
+  return bwd_bf16(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, Hkv, N,
+                  N, d, causal, scale, stream);
+}
+
+int fa_bwd_kv(const void* q, const void* k, const void* v, const void* o, const void* dout,
+              const float* lse, void* dq, void* dk, void* dv, void* workspace,
+              size_t workspace_bytes, int B, int H, int Hkv, int Nq, int Nk, int d, int causal,
+              float scale, hipStream_t stream) {
+  return bwd_bf16(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, Hkv, Nq,
+                  Nk, d, causal, scale, stream);
 }
 
 int fa_bwd_preprocess(const void* o, const void* dout, const float* lse, void* workspace,
@@ -252,7 +268,7 @@ int fa_bwd_main(const void* q, const void* k, const void* v, const void* dout, v
   const Range in[4] = {range_of(q, tb), range_of(k, tb), range_of(v, tb), range_of(dout, tb)};
   const Range out[3] = {range_of(dk, tb), range_of(dv, tb), range_of(workspace, need)};
   if (any_alias(in, 4, out, 3)) return FA_ERR_ALIAS;
-  return from_hip(fa::launch_bwd_main(q, k, v, dout, dk, dv, workspace, B * H, N, d, 1,
+  return from_hip(fa::launch_bwd_main(q, k, v, dout, dk, dv, workspace, B * H, N, N, d, 1,
                                       causal != 0, scale, stream));
 }
 

@@ -151,7 +151,8 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_main_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ L2, const float* __restrict__ Dv, float* __restrict__ dQacc,
-    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int BHkv, int N, int Npad, int nkt,
+    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int BHkv, int Nq, int Nk, int koff,
+    int Npad, int nkt,
     int group, float scale, float c2) {
   using C = BwdCfg<D>;
   extern __shared__ __attribute__((aligned(1024))) char smem[];
@@ -168,20 +169,20 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_main_kernel(
   // multi-head attention).
   int kvh, kt;
   map_tile(blockIdx.x, BHkv, nkt, false, &kvh, &kt);
-  const size_t kvbase = (size_t)kvh * (size_t)N * D;
+  const size_t kvbase = (size_t)kvh * (size_t)Nk * D;
   const char* Kb = reinterpret_cast<const char*>(K + kvbase);
   const char* Vb = reinterpret_cast<const char*>(V + kvbase);
   // per query head g of the group: its Q, dO, L2, D and dQ accumulator slice
   auto qhead = [&](int g) { return (size_t)kvh * group + g; };
   auto Qb_of = [&](int g) {
-    return reinterpret_cast<const char*>(Q + qhead(g) * (size_t)N * D);
+    return reinterpret_cast<const char*>(Q + qhead(g) * (size_t)Nq * D);
   };
   auto dOb_of = [&](int g) {
-    return reinterpret_cast<const char*>(dO + qhead(g) * (size_t)N * D);
+    return reinterpret_cast<const char*>(dO + qhead(g) * (size_t)Nq * D);
   };
   auto dq_rsrc_of = [&](int g) {
-    return __builtin_amdgcn_make_buffer_rsrc(dQacc + qhead(g) * (size_t)N * D, (short)0,
-                                             (int)((unsigned)N * (unsigned)D * 4u), 0x00020000);
+    return __builtin_amdgcn_make_buffer_rsrc(dQacc + qhead(g) * (size_t)Nq * D, (short)0,
+                                             (int)((unsigned)Nq * (unsigned)D * 4u), 0x00020000);
   };
 
   const int k0 = kt * C::KEYS;
@@ -196,13 +197,16 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_main_kernel(
     const int slot = (j * C::WAVES + w) * 64 + lane;
     const int row = slot / C::CPRD;
     const int chunk = (slot % C::CPRD) ^ swz<C::CPRD, SWZ_BOTH>(row);
-    const int src = min(k0 + row, N - 1);
+    const int src = min(k0 + row, Nk - 1);
     dma16(Kb, (unsigned)((src * D + chunk * 8) * 2), lds0 + C::OFF_K + (j * C::WAVES + w) * 1024);
   }
 
-  const int nqb = (N + kBQ - 1) / kBQ;
-  const int qb0 = CAUSAL ? k0 / kBQ : 0;
-  const int nit = nqb - qb0;       // query blocks per query head
+  // Query i sees key j iff j <= i + koff (koff = Nk - Nq: the queries are the
+  // last Nq positions).  Under causal masking the first query block that
+  // sees any key of the tile is the one holding query k0 - koff.
+  const int nqb = (Nq + kBQ - 1) / kBQ;
+  const int qb0 = CAUSAL ? max(0, k0 - koff) / kBQ : 0;
+  const int nit = max(0, nqb - qb0);   // query blocks per query head
   const int ntot = group * nit;    // iterations: (query head, query block)
 
   // DMA of iteration t: query block qb0 + t % nit of query head t / nit (Q, dO
@@ -220,7 +224,7 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_main_kernel(
       const int slot = (j * C::WAVES + w) * 64 + lane;
       const int row = slot / C::CPRD;
       const int chunk = (slot % C::CPRD) ^ swz<C::CPRD, SWZ_BOTH>(row);
-      const int src = min(q0 + row, N - 1);
+      const int src = min(q0 + row, Nq - 1);
       const unsigned off = (unsigned)((src * D + chunk * 8) * 2);
       dma16(Qb, off, st + (j * C::WAVES + w) * 1024);
       dma16(dOb, off, st + C::QTILE + (j * C::WAVES + w) * 1024);
@@ -239,7 +243,7 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_main_kernel(
 #pragma unroll
   for (int cc = 0; cc < C::NDC; ++cc) {
     u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-    if (key < N) {
+    if (key < Nk) {
       a = *reinterpret_cast<const u32x4*>(Kb + ((size_t)key * D + 16 * cc + 8 * h) * 2);
       b = *reinterpret_cast<const u32x4*>(Vb + ((size_t)key * D + 16 * cc + 8 * h) * 2);
     }
@@ -300,7 +304,7 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_main_kernel(
       const int qsq = blk / C::NDB;
       const int dbq = blk % C::NDB;
       const int qs0 = q0 + 32 * qsq;
-      if (CAUSAL && k0 > qs0 + 31) continue;
+      if (CAUSAL && k0 > qs0 + 31 + koff) continue;
       // SWZ_BOTH depends on row bits 1..3: the two 8-row halves differ
       const int aoff0 = tile_off<C::CPRQ, SWZ_BOTH>(trow, 32 * qsq + tcol);
       const int aoff1 = tile_off<C::CPRQ, SWZ_BOTH>(trow + 8, 32 * qsq + tcol);
@@ -319,7 +323,7 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_main_kernel(
       }
       // acc: lane = feature 32*dbq + n, registers = queries qs0 + 4h + 8(r/4) + r%4
       const int voff = ((qs0 + 4 * h) * D + 32 * dbq + n) * 4;
-      if (qs0 + 31 < N) {
+      if (qs0 + 31 < Nq) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(
@@ -328,7 +332,7 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_main_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int qrow = qs0 + 4 * h + 8 * (r >> 2) + (r & 3);
-          if (qrow < N)
+          if (qrow < Nq)
             __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(
                 scale * acc[r], dq_rsrc, voff, (8 * (r >> 2) + (r & 3)) * D * 4, 0);
         }
@@ -356,7 +360,7 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_main_kernel(
       const int qs0 = q0 + 32 * qs;
       uint32_t sk[8];
       // the wave's keys all come after every query of the sub-block: dS = 0
-      const bool dead = CAUSAL && (wk0 > qs0 + 31);
+      const bool dead = CAUSAL && (wk0 > qs0 + 31 + koff);
       if (!dead) {
         const f32x16 zero = {};
         f32x16 s = zero, dp = zero;
@@ -374,11 +378,12 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_main_kernel(
           l2v[g] = *reinterpret_cast<const f32x4*>(sL2 + 32 * qs + 8 * g + 4 * h);
           ddv[g] = *reinterpret_cast<const f32x4*>(sD + 32 * qs + 8 * g + 4 * h);
         }
-        const bool need_mask = (qs0 + 31 >= N) || (wk0 + 31 >= N) || (CAUSAL && wk0 + 31 > qs0);
+        const bool need_mask =
+            (qs0 + 31 >= Nq) || (wk0 + 31 >= Nk) || (CAUSAL && wk0 + 31 > qs0 + koff);
         int lo = -1, hi = 1 << 30;   // live offsets: lo < off+1 ... i.e. off >= lo, off < hi
         if (need_mask) {
-          if (CAUSAL) lo = key - qs0 - 4 * h;
-          hi = key < N ? N - qs0 - 4 * h : -(1 << 30);
+          if (CAUSAL) lo = key - koff - qs0 - 4 * h;
+          hi = key < Nk ? Nq - qs0 - 4 * h : -(1 << 30);
         }
         uint32_t pk[8];
         // P and dS; the mask compares exist only in the masked instance (a
@@ -440,7 +445,7 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_main_kernel(
   if (ntot > 0) dq_step(ntot - 1);
 
   // epilogue: dK = scale * dK^T acc, dV = dV^T acc (lane = key, registers = features)
-  if (key < N) {
+  if (key < Nk) {
     uint16_t* dkrow = dK + kvbase + (size_t)key * D;
     uint16_t* dvrow = dV + kvbase + (size_t)key * D;
 #pragma unroll
@@ -473,10 +478,10 @@ inline WsLayout ws_layout(void* ws, int BH, int N) {
 
 template <int D, bool CAUSAL>
 hipError_t launch_main(const void* q, const void* k, const void* v, const void* dout,
-                       const WsLayout& w, void* dk, void* dv, int BH, int N, int group,
+                       const WsLayout& w, void* dk, void* dv, int BH, int Nq, int Nk, int group,
                        float scale, hipStream_t stream) {
   using C = BwdCfg<D>;
-  const int nkt = (N + C::KEYS - 1) / C::KEYS;
+  const int nkt = (Nk + C::KEYS - 1) / C::KEYS;
   const int BHkv = BH / group;
   auto kern = bwd_main_kernel<D, CAUSAL>;
   hipError_t e =
@@ -484,9 +489,20 @@ hipError_t launch_main(const void* q, const void* k, const void* v, const void* 
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(BHkv * nkt), dim3(C::THREADS), C::SMEM, stream,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
-                     (const uint16_t*)dout, w.l2, w.dv, w.dq, (uint16_t*)dk, (uint16_t*)dv, BHkv, N,
-                     pad_rows(N), nkt, group, scale, scale * kLog2e);
+                     (const uint16_t*)dout, w.l2, w.dv, w.dq, (uint16_t*)dk, (uint16_t*)dv, BHkv, Nq,
+                     Nk, Nk - Nq, pad_rows(Nq), nkt, group, scale, scale * kLog2e);
   return hipGetLastError();
+}
+
+// dK = dV = 0 when there are no queries (nothing to differentiate through).
+__global__ __launch_bounds__(256) void zero_pair_kernel(uint32_t* __restrict__ a,
+                                                        uint32_t* __restrict__ b, size_t n8) {
+  // one thread per 8 bf16 (16 bytes) of each tensor
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  reinterpret_cast<u32x4*>(a)[i] = z;
+  reinterpret_cast<u32x4*>(b)[i] = z;
 }
 
 }  // namespace
@@ -514,14 +530,26 @@ hipError_t launch_bwd_pre(const void* o, const void* dout, const float* lse, voi
 }
 
 hipError_t launch_bwd_main(const void* q, const void* k, const void* v, const void* dout,
-                           void* dk, void* dv, void* ws, int BH, int N, int d, int group,
+                           void* dk, void* dv, void* ws, int BH, int Nq, int Nk, int d, int group,
                            bool causal, float scale, hipStream_t stream) {
-  const WsLayout w = ws_layout(ws, BH, N);
+  if (Nk <= 0) return hipSuccess;   // no keys: no dK / dV rows, dQ stays 0
+  const WsLayout w = ws_layout(ws, BH, Nq);
   if (d == 128)
-    return causal ? launch_main<128, true>(q, k, v, dout, w, dk, dv, BH, N, group, scale, stream)
-                  : launch_main<128, false>(q, k, v, dout, w, dk, dv, BH, N, group, scale, stream);
-  return causal ? launch_main<64, true>(q, k, v, dout, w, dk, dv, BH, N, group, scale, stream)
-                : launch_main<64, false>(q, k, v, dout, w, dk, dv, BH, N, group, scale, stream);
+    return causal
+               ? launch_main<128, true>(q, k, v, dout, w, dk, dv, BH, Nq, Nk, group, scale, stream)
+               : launch_main<128, false>(q, k, v, dout, w, dk, dv, BH, Nq, Nk, group, scale, stream);
+  return causal
+             ? launch_main<64, true>(q, k, v, dout, w, dk, dv, BH, Nq, Nk, group, scale, stream)
+             : launch_main<64, false>(q, k, v, dout, w, dk, dv, BH, Nq, Nk, group, scale, stream);
+}
+
+hipError_t launch_zero_bf16(void* a, void* b, size_t elems, hipStream_t stream) {
+  // bf16 tensors of d = 64 or 128 per row: a multiple of 8 elements
+  const size_t n8 = elems / 8;
+  if (n8 == 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_pair_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream,
+                     (uint32_t*)a, (uint32_t*)b, n8);
+  return hipGetLastError();
 }
 
 hipError_t launch_bwd_finalize(void* dq, const void* ws, int BH, int N, int d,

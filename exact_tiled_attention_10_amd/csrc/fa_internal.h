@@ -38,9 +38,13 @@ size_t bwd_workspace_bytes(int BH, int N, int d);
 hipError_t launch_bwd_pre(const void* o, const void* dout, const float* lse, void* ws, int BH,
                           int N, int d, hipStream_t stream);
 // BH = batch * query heads; `group` query heads share each key / value head.
+// Nq query rows (the workspace is sized by them) against Nk keys, causal
+// alignment as in launch_fwd_bf16_kv.
 hipError_t launch_bwd_main(const void* q, const void* k, const void* v, const void* dout,
-                           void* dk, void* dv, void* ws, int BH, int N, int d, int group,
+                           void* dk, void* dv, void* ws, int BH, int Nq, int Nk, int d, int group,
                            bool causal, float scale, hipStream_t stream);
+// Two bf16 tensors of `elems` elements each (a multiple of 8) set to 0.
+hipError_t launch_zero_bf16(void* a, void* b, size_t elems, hipStream_t stream);
 hipError_t launch_bwd_finalize(void* dq, const void* ws, int BH, int N, int d,
                                hipStream_t stream);
 

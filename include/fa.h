@@ -201,6 +201,23 @@ int fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o,
                int N, int d, int causal, float scale, hipStream_t stream);
 
 /*
+ * fa_bwd_kv -- backward pass of fa_fwd_kv (Nq queries against Nk keys,
+ * bottom-right causal alignment, grouped-query heads), bfloat16 tensors.
+ *
+ *   q, o, dout, dq  [B, H, Nq, d];  k, v, dk, dv  [B, Hkv, Nk, d];
+ *   lse [B, H, Nq] as fa_fwd_kv returned it.
+ *   workspace       at least fa_bwd_workspace_size(B, H, Nq, d) bytes.
+ *
+ * Gradients of sum(O * dO) as for fa_bwd: query rows with no visible key get
+ * dQ = 0; keys no query sees get dK = dV = 0 (with Nq = 0 every key, and
+ * then only k, v, dk and dv need to be given).  Errors as fa_bwd.
+ */
+int fa_bwd_kv(const void* q, const void* k, const void* v, const void* o,
+              const void* dout, const float* lse, void* dq, void* dk, void* dv,
+              void* workspace, size_t workspace_bytes, int B, int H, int Hkv,
+              int Nq, int Nk, int d, int causal, float scale, hipStream_t stream);
+
+/*
  * The three stages fa_bwd runs, in order, on the same stream.  Calling them in
  * sequence with the same arguments is exactly fa_bwd; they exist for callers
  * that schedule or time the stages separately.  Each validates like fa_bwd

@@ -40,7 +40,8 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = _declared_functions()
     assert set(names) == {"fa_fwd", "fa_fwd_gqa", "fa_fwd_kv", "fa_fwd_kv_workspace_size",
-                          "fa_fwd_f32", "fa_bwd", "fa_bwd_gqa", "fa_bwd_workspace_size",
+                          "fa_fwd_f32", "fa_bwd", "fa_bwd_gqa", "fa_bwd_kv",
+                          "fa_bwd_workspace_size",
                           "fa_status_string", "fa_bwd_preprocess", "fa_bwd_main",
                           "fa_bwd_finalize"}
     for nm in names:
@@ -230,3 +231,30 @@ def test_kv_forward_rejects_bad_arguments(lib):
     assert f(Nq=0, q=None, o=None) == fa.FA_OK        # nothing to compute
     # with no keys, k and v may be NULL: the call gets past the pointer checks
     assert f(Nk=0, k=None, v=None, ws=None, wsb=0, d=96) == fa.FA_ERR_HEADDIM
+
+
+def test_kv_backward_rejects_bad_arguments(lib):
+    ws = lib.fa_bwd_workspace_size(1, 2, 10, 64)
+
+    def b(**kw):
+        g = dict(q=A, k=A + MB, v=A + 2 * MB, o=A + 3 * MB, dout=A + 4 * MB, lse=A + 5 * MB,
+                 dq=A + 6 * MB, dk=A + 7 * MB, dv=A + 8 * MB, ws=A + 9 * MB, wsb=ws, B=1, H=2,
+                 Hkv=1, Nq=10, Nk=300, d=64, causal=1, scale=0.125)
+        g.update(kw)
+        return lib.fa_bwd_kv(g["q"], g["k"], g["v"], g["o"], g["dout"], g["lse"], g["dq"],
+                             g["dk"], g["dv"], g["ws"], g["wsb"], g["B"], g["H"], g["Hkv"],
+                             g["Nq"], g["Nk"], g["d"], g["causal"], g["scale"], None)
+    assert b(Nk=-3) == fa.FA_ERR_SHAPE
+    assert b(Hkv=3) == fa.FA_ERR_SHAPE
+    assert b(wsb=ws - 16) == fa.FA_ERR_WORKSPACE
+    assert b(dk=None) == fa.FA_ERR_NULL
+    assert b(q=None) == fa.FA_ERR_NULL
+    # k holds 1 head of 300 x 64 bf16 (38400 bytes): a dk starting inside it aliases
+    assert b(dk=A + MB + 38400 - 16) == fa.FA_ERR_ALIAS
+    # no queries and no keys: a no-op with no pointers at all
+    assert b(Nq=0, Nk=0, q=None, k=None, v=None, o=None, dout=None, lse=None, dq=None,
+             dk=None, dv=None, ws=None, wsb=0) == fa.FA_OK
+    # no queries: the query-side pointers are not needed (the call would then
+    # zero dk and dv on the device, so only a rejected form is tried here)
+    assert b(Nq=0, q=None, o=None, dout=None, lse=None, dq=None, ws=None, dk=None) == \
+        fa.FA_ERR_NULL

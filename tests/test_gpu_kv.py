@@ -136,3 +136,68 @@ def test_llama8b_decode_against_long_cache():
     _say(f"[llama8b decode] workspace {nb} bytes")
     assert nb > 0
     _check(q, k, v, True, 1 / math.sqrt(d), o, lse)
+
+
+# --- backward (fa_bwd_kv) ------------------------------------------------------
+
+def _bwd(q, k, v, do, causal, scale):
+    o, lse, _ = _run(q, k, v, causal, scale)
+    qd, kd, vd, dod = (t.cuda() for t in (q, k, v, do))
+    dq = torch.full_like(qd, float("nan"))
+    dk = torch.full_like(kd, float("nan"))
+    dv = torch.full_like(vd, float("nan"))
+    B, H, Nq, d = q.shape
+    ws = torch.full((max(1, fa.fa_bwd_workspace_size(B, H, Nq, d)),), 0xFF, dtype=torch.uint8,
+                    device="cuda")
+    fa.fa_bwd_kv(qd, kd, vd, o, dod, lse, dq, dk, dv, ws, causal, scale)
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+def _check_grads(q, k, v, do, causal, scale, got):
+    from oracle import naive_bwd_kv
+    ref = naive_bwd_kv(_f64(q), _f64(k), _f64(v), _f64(do), scale, causal)
+    # one bf16 ulp of the largest reference magnitude, never below 2e-2 (the
+    # summed gradients of shared key/value heads can pass O(1))
+    tol = max(TOL, 2.0 ** -7 * max(float(np.max(np.abs(r))) if r.size else 0.0 for r in ref))
+    errs = [float(np.max(np.abs(_f64(g) - r))) if r.size else 0.0 for g, r in zip(got, ref)]
+    _say(f"   max|d dQ|={errs[0]:.3e} |d dK|={errs[1]:.3e} |d dV|={errs[2]:.3e} (tol {tol:.3e})")
+    for g in got:
+        assert torch.isfinite(g).all()
+    assert max(errs) <= tol
+
+
+BWD_SHAPES = [(1, 300), (5, 700), (64, 97), (300, 1000), (1000, 300), (129, 1), (257, 600)]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("nq,nk", BWD_SHAPES)
+def test_kv_backward(nq, nk, causal, d):
+    _say(f"[kv bwd] Nq={nq} Nk={nk} d={d} causal={causal}")
+    q, k, v = _inputs(2, 2, 2, nq, nk, d, seed=700 + nq + nk)
+    do = make_gqa_inputs(2, 2, 2, nq, d, seed=900 + nq, with_do=True)[3]
+    got = _bwd(q, k, v, do, causal, 1 / math.sqrt(d))
+    _check_grads(q, k, v, do, causal, 1 / math.sqrt(d), got)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_kv_backward_gqa(causal):
+    _say(f"[kv bwd gqa] causal={causal}")
+    q, k, v = _inputs(1, 8, 2, 200, 520, 64, seed=11)
+    do = make_gqa_inputs(1, 8, 2, 200, 64, seed=12, with_do=True)[3]
+    got = _bwd(q, k, v, do, causal, 0.125)
+    _check_grads(q, k, v, do, causal, 0.125, got)
+
+
+def test_kv_backward_no_queries_zeroes_key_gradients():
+    k, v = _inputs(1, 2, 2, 3, 70, 64, seed=13)[1:]
+    kd, vd = k.cuda(), v.cuda()
+    dk = torch.full_like(kd, float("nan"))
+    dv = torch.full_like(vd, float("nan"))
+    st = fa.load_library().fa_bwd_kv(None, kd.data_ptr(), vd.data_ptr(), None, None, None, None,
+                                     dk.data_ptr(), dv.data_ptr(), None, 0, 1, 2, 2, 0, 70, 64,
+                                     1, 0.125, None)
+    torch.cuda.synchronize()
+    assert st == fa.FA_OK
+    assert torch.all(dk == 0) and torch.all(dv == 0)
