@@ -156,6 +156,74 @@ def run_fwd_sweep(reps: int = 20, warm_s: float = 0.05):
     return out
 
 
+def _time_launches(fn, reps: int = 20, warm_s: float = 0.05):
+    """Mean ms per call of ``fn`` (HIP events on the current stream) after
+    ``warm_s`` seconds of warm-up."""
+    import torch
+    t_end = time.perf_counter() + warm_s
+    n = 0
+    while n < 3 or time.perf_counter() < t_end:
+        fn()
+        n += 1
+        if n % 16 == 0:
+            torch.cuda.synchronize()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(reps):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / reps
+
+
+def run_extra_sweep():
+    """Grouped-query and different-length shapes: Llama-3.1-8B's real head
+    sharing (32 query heads over 8 key/value heads) for the causal N = 4096
+    forward and backward, and decode -- one new token per sequence against a
+    32k-token cache, split across workgroups by key range -- whose bound is
+    HBM (every key and value byte is read once per key/value head)."""
+    import torch
+    import exact_tiled_attention_10_amd as fa
+    from workloads import make_gqa_inputs
+
+    out = {}
+    B, H, Hkv, N, d = 1, 32, 8, 4096, 128
+    q, k, v, do = (t.cuda() for t in make_gqa_inputs(B, H, Hkv, N, d, seed=6, with_do=True))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    sc = 1 / math.sqrt(d)
+    ms = _time_launches(lambda: fa.fa_fwd_gqa(q, k, v, o, lse, True, sc))
+    tf = fwd_flops(B, H, N, d, True) / (ms * 1e-3) / 1e12
+    out["llama8b_gqa32x8_n4096_causal_fwd"] = dict(
+        ms=round(ms, 4), tflops=round(tf, 1), pct_of_bf16_peak=round(100 * tf / PEAK_BF16_TFLOPS, 1))
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(fa.fa_bwd_workspace_size(B, H, N, d), dtype=torch.uint8, device="cuda")
+    ms = _time_launches(lambda: fa.fa_bwd_gqa(q, k, v, o, do, lse, dq, dk, dv, ws, True, sc))
+    tf = 2.5 * fwd_flops(B, H, N, d, True) / (ms * 1e-3) / 1e12
+    out["llama8b_gqa32x8_n4096_causal_bwd"] = dict(
+        ms=round(ms, 4), tflops=round(tf, 1), pct_of_bf16_peak=round(100 * tf / PEAK_BF16_TFLOPS, 1))
+    del q, k, v, do, o, lse, dq, dk, dv, ws
+
+    B, Nk = 8, 32768
+    q = make_gqa_inputs(B, H, Hkv, 1, d, seed=7)[0].cuda()
+    k, v = (t.cuda() for t in make_gqa_inputs(B, H, Hkv, Nk, d, seed=8)[1:])
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, 1), dtype=torch.float32, device="cuda")
+    nb = fa.fa_fwd_kv_workspace_size(B, H, 1, Nk, d)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
+    ms = _time_launches(lambda: fa.fa_fwd_kv(q, k, v, o, lse, ws, True, sc), reps=50)
+    nbytes = 2 * B * Hkv * Nk * d * 2 + 2 * B * H * d * 2 + B * H * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    out["llama8b_decode_b8_gqa32x8_nk32768"] = dict(
+        ms=round(ms, 4), algorithmic_bytes=nbytes, gbs=round(gbs, 1),
+        frac_of_hbm_peak=round(gbs / PEAK_HBM_GBS, 4), workspace_bytes=nb)
+    del q, k, v, o, lse, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 # ---------------------------------------------------------------------------
 # oracle on the host cores
 # ---------------------------------------------------------------------------
@@ -338,6 +406,7 @@ def main(argv=None):
     )
     if not args.no_sweep:
         line["fwd_sweep"] = run_fwd_sweep()
+        line["extra_sweep"] = run_extra_sweep()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = run_cpu_baseline(args.cpu_seconds)
     print(json.dumps(line), flush=True)

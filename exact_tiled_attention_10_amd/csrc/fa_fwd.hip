@@ -167,12 +167,14 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(const FwdArgs a) {
   // DMA: tile t of K (V) goes to K (V) stage t & 1.  Round j issues K tile
   // j + 1 and V tile j; they land by the end of round j and are read in round
   // j + 1 (K by the scores of tile j + 1, V by the value product of tile j).
-  // Only the group that starts a round with its softmax phase issues them
-  // (each of its waves two 1 KiB slots per DMA step): a DMA instruction costs
-  // about 16 cycles at the CU's address unit, and a burst of them would
-  // otherwise hold back the start of the other group's matrix phase.
+  // Each tile is issued at the start of a softmax phase, never during a
+  // matrix phase (a DMA instruction costs about 16 cycles at the CU's address
+  // unit; a burst of them held back the other group's matrix work): group 1
+  // issues K tile j + 1 as round j begins, group 0 issues V tile j when its
+  // softmax half of round j begins (V stage j & 1 was last read in round
+  // j - 1).  Each wave fills two 1 KiB slots per DMA step of its tile.
   const unsigned ldsb = __builtin_amdgcn_readfirstlane(lds_addr(smem_raw));
-  const int ws0 = w & 3, ws1 = ws0 + 4;   // the two DMA slots a group-1 wave fills
+  const int ws0 = w & 3, ws1 = ws0 + 4;   // the two DMA slots a wave fills
   const unsigned koffA = dma_src_off<D, BN, SWZ_ROWS>(0, ws0, lane, 0, Nk, true);
   const unsigned voffA = dma_src_off<D, BN, SWZ_TR>(0, ws0, lane, 0, Nk, true);
   const unsigned koffB = dma_src_off<D, BN, SWZ_ROWS>(0, ws1, lane, 0, Nk, true);
@@ -392,11 +394,11 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(const FwdArgs a) {
   auto round = [&](int j, auto parity, auto group, auto kind) __attribute__((always_inline)) {
     if constexpr (decltype(group)::value == 1) {
       if (j + 1 < nkt) issue(j + 1, 0u, Kb, koffA, koffB, rows_t{});
-      if (j < nkt) issue(j, (unsigned)C::OFF_V, Vb, voffA, voffB, tr_t{});
     }
     if constexpr (decltype(group)::value == 0) {
       matrix_phase(parity, kind);
       phase_barrier();
+      if (j < nkt) issue(j, (unsigned)C::OFF_V, Vb, voffA, voffB, tr_t{});
       softmax_phase(j);
     } else {
       softmax_phase(j - 1);
