@@ -179,9 +179,10 @@ def _time_launches(fn, reps: int = 20, warm_s: float = 0.05):
 
 
 def run_extra_sweep():
-    """Grouped-query and different-length shapes: Llama-3.1-8B's real head
-    sharing (32 query heads over 8 key/value heads) for the causal N = 4096
-    forward and backward, and decode -- one new token per sequence against a
+    """Grouped-query, head-dimension-256 and different-length shapes:
+    Llama-3.1-8B's real head sharing (32 query heads over 8 key/value heads)
+    for the causal N = 4096 forward and backward, the d = 256 causal forward at
+    [1, 16, 4096, 256], and decode -- one new token per sequence against a
     32k-token cache, split across workgroups by key range -- whose bound is
     HBM (every key and value byte is read once per key/value head)."""
     import torch
@@ -205,6 +206,16 @@ def run_extra_sweep():
     out["llama8b_gqa32x8_n4096_causal_bwd"] = dict(
         ms=round(ms, 4), tflops=round(tf, 1), pct_of_bf16_peak=round(100 * tf / PEAK_BF16_TFLOPS, 1))
     del q, k, v, do, o, lse, dq, dk, dv, ws
+
+    B, H2, N2, d2 = 1, 16, 4096, 256
+    q, k, v = (t.cuda() for t in make_gqa_inputs(B, H2, H2, N2, d2, seed=9))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H2, N2), dtype=torch.float32, device="cuda")
+    ms = _time_launches(lambda: fa.fa_fwd(q, k, v, o, lse, True, 1 / 16.0))
+    tf = fwd_flops(B, H2, N2, d2, True) / (ms * 1e-3) / 1e12
+    out["d256_n4096_causal_fwd"] = dict(
+        ms=round(ms, 4), tflops=round(tf, 1), pct_of_bf16_peak=round(100 * tf / PEAK_BF16_TFLOPS, 1))
+    del q, k, v, o, lse
 
     B, Nk = 8, 32768
     q = make_gqa_inputs(B, H, Hkv, 1, d, seed=7)[0].cuda()

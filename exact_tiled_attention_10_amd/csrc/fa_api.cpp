@@ -28,11 +28,12 @@ bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) !
 
 // Shape, head-dim and scale checks shared by every entry point.  On success
 // writes the element count of one [B, H, N, d] tensor and of one [B, H, N]
-// statistic.
+// statistic.  d is 64 or 128 everywhere; the bf16 forwards (wide = true) also
+// take 256.
 int check_common(int B, int H, int N, int d, float scale, size_t* tensor_elems,
-                 size_t* row_elems) {
+                 size_t* row_elems, bool wide = false) {
   if (B < 0 || H < 0 || N < 0 || N > FA_MAX_N) return FA_ERR_SHAPE;
-  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (d != 64 && d != 128 && !(wide && d == 256)) return FA_ERR_HEADDIM;
   const long long bh = (long long)B * (long long)H;
   if (bh > INT_MAX) return FA_ERR_SHAPE;
   // grid size: one workgroup per (batch*head, 64-row tile) at most
@@ -69,7 +70,7 @@ int check_heads(int H, int Hkv) {
 int fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
              int Hkv, int N, int d, int causal, float scale, hipStream_t stream) {
   size_t te = 0, re = 0;
-  int st = check_common(B, H, N, d, scale, &te, &re);
+  int st = check_common(B, H, N, d, scale, &te, &re, true);
   if (st != FA_OK) return st;
   st = check_heads(H, Hkv);
   if (st != FA_OK) return st;
@@ -133,7 +134,7 @@ int bwd_bf16(const void* q, const void* k, const void* v, const void* o, const v
 int check_kv(int B, int H, int Hkv, int Nq, int Nk, int d, float scale, size_t* q_elems,
              size_t* kv_elems, size_t* rows) {
   size_t te = 0, re = 0;
-  int st = check_common(B, H, Nq, d, scale, &te, &re);
+  int st = check_common(B, H, Nq, d, scale, &te, &re, true);
   if (st != FA_OK) return st;
   if (Nk < 0 || Nk > FA_MAX_N) return FA_ERR_SHAPE;
   st = check_heads(H, Hkv);
@@ -150,7 +151,7 @@ extern "C" {
 
 size_t fa_fwd_kv_workspace_size(int B, int H, int Nq, int Nk, int d) {
   size_t te = 0, re = 0;
-  if (check_common(B, H, Nq, d, 1.f, &te, &re) != FA_OK) return 0;
+  if (check_common(B, H, Nq, d, 1.f, &te, &re, true) != FA_OK) return 0;
   if (Nk < 0 || Nk > FA_MAX_N || re == 0) return 0;
   return fa::fwd_workspace_bytes(B * H, Nq, Nk, d);
 }
@@ -295,7 +296,8 @@ const char* fa_status_string(int status) {
     case FA_ERR_SHAPE:
       return "invalid shape (B, H or N negative, N too large, size overflow, or H not a "
              "multiple of Hkv)";
-    case FA_ERR_HEADDIM: return "unsupported head dimension (must be 64 or 128)";
+    case FA_ERR_HEADDIM:
+      return "unsupported head dimension (64 or 128; the bf16 forwards also take 256)";
     case FA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
     case FA_ERR_ALIAS: return "an output overlaps an input or another output";
     case FA_ERR_SCALE: return "scale is not finite";

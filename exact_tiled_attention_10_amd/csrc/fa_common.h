@@ -94,22 +94,24 @@ __device__ __forceinline__ int tr_group_pos(int lg) { return ((lg & 1) << 1) | (
 // therefore touches 16 distinct 16-byte slots modulo 256 bytes.  Two swizzles
 // cover the two read patterns the kernels use:
 //   SWZ_ROWS  16 consecutive rows read at the same chunk (a row-operand
-//             read: lane n reads row n).  CPR 16: swz = r % 16;
+//             read: lane n reads row n).  CPR 16 and 32: swz = r % 16;
 //             CPR 8 (two rows per 256 B): swz = (r / 2) % 8.
 //   SWZ_TR    transposing reads: rows r0..r0+3 (r0 % 4 == 0) at four
-//             consecutive chunks 4b..4b+3.  CPR 16: swz = 4 (r % 4);
+//             consecutive chunks 4b..4b+3.  CPR 16 and 32: swz = 4 (r % 4);
 //             CPR 8: swz = 4 ((r / 2) % 2).
-//   SWZ_BOTH  both patterns on one tile: CPR 16: swz = 4 (r % 4) + (r / 4) % 4;
-//             CPR 8: swz = 4 ((r / 2) % 2) + (r / 4) % 4.
+//   SWZ_BOTH  both patterns on one tile: CPR 16 and 32: swz = 4 (r % 4) +
+//             (r / 4) % 4; CPR 8: swz = 4 ((r / 2) % 2) + (r / 4) % 4.
+// (A row of CPR 32 spans 512 bytes, so rows are 256-byte aligned like CPR 16
+// and the same swizzles apply.)
 // ---------------------------------------------------------------------------
 enum { SWZ_ROWS = 0, SWZ_TR = 1, SWZ_BOTH = 2 };
 
 template <int CPR, int KIND>
 __device__ __forceinline__ int swz(int r) {
-  static_assert(CPR == 8 || CPR == 16, "rows of 64 or 128 bf16");
-  if (KIND == SWZ_ROWS) return CPR == 16 ? (r & 15) : ((r >> 1) & 7);
-  if (KIND == SWZ_TR) return CPR == 16 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2);
-  return CPR == 16 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+  static_assert(CPR == 8 || CPR == 16 || CPR == 32, "rows of 64, 128 or 256 bf16");
+  if (KIND == SWZ_ROWS) return CPR >= 16 ? (r & 15) : ((r >> 1) & 7);
+  if (KIND == SWZ_TR) return CPR >= 16 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2);
+  return CPR >= 16 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
 }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));

@@ -475,6 +475,214 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(const FwdArgs a) {
   }
 }
 
+// Head dimension 256 ("Flash Attention, From First Principles", "The rent
+// arithmetic": the accumulator and the query tile grow with d, the tiles
+// shrink).  The ping-pong kernel above needs ~270 registers per wave at this
+// size, past the 256 that two waves per SIMD allow, so this kernel runs ONE
+// wave per SIMD (512 registers: the 32 x 256 accumulator, the query tile and
+// the scores fit with room) and no second group to overlap with: per 32-key
+// tile a wave forms S^T = K Q^T (16 MFMAs), the probabilities against its
+// running max (same lazy rebase as above), and O^T += V^T P^T (16 MFMAs).  At
+// d = 256 a score costs 32 MFMA cycles against a few VALU cycles, so the
+// serial order costs little.  K and V tiles arrive by DMA, two stages deep,
+// one barrier per tile.  Workgroup: 4 waves x 32 queries = 128 queries.
+constexpr int kWaves256 = 4;
+constexpr int kBM256 = 32 * kWaves256;
+constexpr int kBN256 = 32;
+
+template <bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void fwd_d256_kernel(const FwdArgs a) {
+  constexpr int D = 256;
+  constexpr int BN = kBN256;
+  constexpr int CPR = D / 8;                  // 16-byte chunks per row
+  constexpr int ROW = CPR * 16;               // bytes per row
+  constexpr int TILE = BN * ROW;              // one K or V tile (16 KiB)
+  constexpr int NQC = D / 16;                 // k-steps of the score product
+  constexpr int NDB = D / 32;                 // 32-feature output blocks
+  constexpr int DMA = TILE / (16 * 64 * kWaves256);   // DMAs per lane per tile
+  constexpr int OFF_V = 2 * TILE;
+  extern __shared__ __attribute__((aligned(1024))) char smem_raw[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 31;
+  const int h = lane >> 5;
+  const int BH = a.BH, Nq = a.Nq, Nk = a.Nk, koff = a.koff;
+  const float c = a.c;
+
+  int bh, qt, sp = 0;
+  {
+    int bid = blockIdx.x;
+    if (a.nsplit > 1) {
+      sp = bid % a.nsplit;
+      bid /= a.nsplit;
+    }
+    map_tile(bid, BH, a.nqt, CAUSAL, &bh, &qt);
+  }
+  const size_t base = (size_t)bh * (size_t)Nq * D;
+  const size_t kvbase = (size_t)(bh / a.group) * (size_t)Nk * D;
+  const char* Kb = reinterpret_cast<const char*>(a.K + kvbase);
+  const char* Vb = reinterpret_cast<const char*>(a.V + kvbase);
+  const int q0 = qt * kBM256;
+  const int wq0 = q0 + 32 * w;
+  const int qrow = wq0 + n;
+
+  const int kb = sp * a.klen;
+  int ke = min(Nk, kb + a.klen);
+  if (CAUSAL) ke = min(ke, q0 + kBM256 + koff);
+  const int nkt = ke > kb ? (ke - kb + BN - 1) / BN : 0;
+
+  // DMA of tile t into stage t & 1: slot (i * 4 + w) * 64 + lane of the tile
+  const unsigned ldsb = __builtin_amdgcn_readfirstlane(lds_addr(smem_raw));
+  auto issue = [&](int t) __attribute__((always_inline)) {
+    const int k0 = kb + t * BN;
+    const char* gk = Kb + (size_t)k0 * ROW;
+    const char* gv = Vb + (size_t)k0 * ROW;
+    const unsigned stk = ldsb + (t & 1) * TILE;
+    const unsigned stv = ldsb + OFF_V + (t & 1) * TILE;
+#pragma unroll
+    for (int i = 0; i < DMA; ++i) {
+      const int slot = (i * kWaves256 + w) * 64 + lane;
+      const int row = slot / CPR;
+      const int src_row = min(k0 + row, Nk - 1) - k0;
+      const int ck = (slot % CPR) ^ swz<CPR, SWZ_ROWS>(row);
+      const int cv = (slot % CPR) ^ swz<CPR, SWZ_TR>(row);
+      const unsigned dst = (unsigned)((i * kWaves256 + w) * 1024);
+      dma16(gk, (unsigned)(src_row * ROW + ck * 16), stk + dst);
+      dma16(gv, (unsigned)(src_row * ROW + cv * 16), stv + dst);
+    }
+  };
+  if (nkt > 0) issue(0);
+
+  bf16x8 qf[NQC];
+  {
+    const uint32_t flip = a.negq ? 0x80008000u : 0u;
+    const uint16_t* Qh = a.Q + base;
+#pragma unroll
+    for (int cc = 0; cc < NQC; ++cc) {
+      u32x4 raw = {0u, 0u, 0u, 0u};
+      if (qrow < Nq)
+        raw = *reinterpret_cast<const u32x4*>(Qh + (size_t)qrow * D + 16 * cc + 8 * h);
+      raw ^= flip;
+      qf[cc] = __builtin_bit_cast(bf16x8, raw);
+    }
+  }
+  const int ka = tile_off<CPR, SWZ_ROWS>(n, 8 * h);
+  const int vrow0 = 4 * (lane >> 5) + ((lane & 15) >> 2);
+  const int vcol0 = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int va = tile_off<CPR, SWZ_TR>(vrow0, vcol0);
+
+  f32x16 acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+  float m = kMInit;
+  float lsum = 0.f;
+
+  for (int j = 0; j < nkt; ++j) {
+    // tile j landed for every wave; every wave is done with tile j - 1
+    wait_vmem();
+    __syncthreads();
+    if (j + 1 < nkt) issue(j + 1);
+    const char* ks = smem_raw + (j & 1) * TILE;
+    const char* vs = smem_raw + OFF_V + (j & 1) * TILE;
+    const int k0 = kb + j * BN;
+
+    f32x16 s = {};
+#pragma unroll
+    for (int cc = 0; cc < NQC; ++cc) {
+      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + (ka ^ (32 * cc)));
+      s = mfma_32x32x16_bf16(kf, qf[cc], s);
+    }
+    if ((k0 + BN > ke) || (CAUSAL && k0 + BN - 1 > wq0 + koff)) {
+      int lim = ke - 1 - k0 - 4 * h;
+      if (CAUSAL) lim = min(lim, qrow + koff - k0 - 4 * h);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int off = 8 * (r >> 2) + (r & 3);
+        s[r] = off > lim ? kNegInf : s[r];
+      }
+    }
+    uint32_t pk[8];
+    auto probs = [&]() __attribute__((always_inline)) {
+      float part[2] = {0.f, 0.f};
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -m));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r + 1], c, -m));
+        pk[r >> 1] = pack_bf16x2(p0, p1);
+        part[(r >> 1) & 1] += p0 + p1;
+      }
+      return part[0] + part[1];
+    };
+    float ps = probs();
+    if (__any(ps > kSumBound)) {
+      float mx = kNegInf;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+      mx = fmaxf(mx, wave_xor32(mx));
+      const float m_new = fmaxf(m, mx * c);
+      const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+      lsum *= alpha;
+      m = m_new;
+      ps = probs();
+    }
+    lsum += ps;
+
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const bf16x8 b = __builtin_bit_cast(
+          bf16x8, u32x4{pk[4 * half], pk[4 * half + 1], pk[4 * half + 2], pk[4 * half + 3]});
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const char* vp = vs + (va ^ (64 * db)) + 16 * half * ROW;
+        const u32x2 lo = lds_read_tr16(vp);
+        const u32x2 hi = lds_read_tr16(vp + 8 * ROW);
+        acc[db] = mfma_32x32x16_bf16(__builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y}),
+                                     b, acc[db]);
+      }
+    }
+  }
+
+  const float lt = lsum + wave_xor32(lsum);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  const float lse = lt > 0.f ? (m + __log2f(lt)) * kLn2 : kNegInf;
+  if (qrow < Nq) {
+    if (a.nsplit == 1) {
+      uint16_t* orow = a.O + base + (size_t)qrow * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = 32 * db + 8 * g + 4 * h;
+          u32x2 out = {pack_bf16x2(acc[db][4 * g + 0] * inv, acc[db][4 * g + 1] * inv),
+                       pack_bf16x2(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv)};
+          *reinterpret_cast<u32x2*>(orow + d0) = out;
+        }
+      if (h == 0) a.LSE[(size_t)bh * Nq + qrow] = lse;
+    } else {
+      const size_t prow = ((size_t)sp * BH + bh) * Nq + qrow;
+      float* orow = a.Opart + prow * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = 32 * db + 8 * g + 4 * h;
+          f32x4 out = {acc[db][4 * g + 0] * inv, acc[db][4 * g + 1] * inv,
+                       acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv};
+          *reinterpret_cast<f32x4*>(orow + d0) = out;
+        }
+      if (h == 0) a.Lpart[prow] = lse;
+    }
+  }
+}
+
 // Merge of the key ranges ("Flash Attention, From First Principles", "The
 // scaffold": blocks over disjoint keys combine through their log-sum-exps):
 // lse = log sum_s e^{lse_s}, O = sum_s e^{lse_s - lse} O_s.  Ranges with
@@ -704,6 +912,8 @@ inline void split_scale(float scale, float* c, int* negq) {
   *c = a > 0.f ? a * kLog2e : 1e-30f;
 }
 
+hipError_t launch_merge(const FwdArgs& a, int d, hipStream_t stream);
+
 template <int D, int BN, bool CAUSAL>
 hipError_t launch_bf16(const FwdArgs& a, hipStream_t stream) {
   using C = FwdCfg<D, BN>;
@@ -715,11 +925,36 @@ hipError_t launch_bf16(const FwdArgs& a, hipStream_t stream) {
                      a);
   e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
+  return launch_merge(a, D, stream);
+}
+
+hipError_t launch_merge(const FwdArgs& a, int d, hipStream_t stream) {
   const size_t rows = (size_t)a.BH * a.Nq;
-  const size_t threads = rows * (D / 8);
-  hipLaunchKernelGGL(fwd_merge_kernel<D>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
-                     stream, a.Opart, a.Lpart, a.O, a.LSE, (int)rows, a.nsplit);
+  const size_t threads = rows * (d / 8);
+  const dim3 grid((unsigned)((threads + 255) / 256));
+  if (d == 256)
+    hipLaunchKernelGGL(fwd_merge_kernel<256>, grid, dim3(256), 0, stream, a.Opart, a.Lpart, a.O,
+                       a.LSE, (int)rows, a.nsplit);
+  else if (d == 128)
+    hipLaunchKernelGGL(fwd_merge_kernel<128>, grid, dim3(256), 0, stream, a.Opart, a.Lpart, a.O,
+                       a.LSE, (int)rows, a.nsplit);
+  else
+    hipLaunchKernelGGL(fwd_merge_kernel<64>, grid, dim3(256), 0, stream, a.Opart, a.Lpart, a.O,
+                       a.LSE, (int)rows, a.nsplit);
   return hipGetLastError();
+}
+
+template <bool CAUSAL>
+hipError_t launch_d256(const FwdArgs& a, hipStream_t stream) {
+  constexpr int smem = 4 * kBN256 * 256 * 2;
+  auto kern = fwd_d256_kernel<CAUSAL>;
+  hipError_t e =
+      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(a.BH * a.nqt * a.nsplit), dim3(64 * kWaves256), smem, stream, a);
+  e = hipGetLastError();
+  if (e != hipSuccess || a.nsplit == 1) return e;
+  return launch_merge(a, 256, stream);
 }
 
 template <int D, bool CAUSAL>
@@ -747,8 +982,9 @@ hipError_t launch_f32(const float* q, const float* k, const float* v, float* o, 
 // per CU.
 FwdSplit fwd_split(int BH, int Nq, int Nk, int d) {
   FwdSplit sp{1, Nk};
-  const int bn = 64;
-  const long long tiles = (long long)BH * ((Nq + kBM - 1) / kBM);
+  const int bn = 64;   // a multiple of every kernel's key tile
+  const int bm = d == 256 ? kBM256 : kBM;
+  const long long tiles = (long long)BH * ((Nq + bm - 1) / bm);
   if (tiles <= 0 || tiles >= 256 || Nk <= 0) return sp;
   const int nkt = (Nk + bn - 1) / bn;
   int ns = (int)((512 + tiles - 1) / tiles);
@@ -757,7 +993,6 @@ FwdSplit fwd_split(int BH, int Nq, int Nk, int d) {
   const int tiles_per = (nkt + ns - 1) / ns;
   sp.klen = tiles_per * bn;
   sp.nsplit = (Nk + sp.klen - 1) / sp.klen;
-  (void)d;
   return sp;
 }
 
@@ -781,7 +1016,7 @@ hipError_t launch_fwd_bf16_kv(const void* q, const void* k, const void* v, void*
   a.Nq = Nq;
   a.Nk = Nk;
   a.koff = Nk - Nq;
-  a.nqt = (Nq + kBM - 1) / kBM;
+  a.nqt = (Nq + (d == 256 ? kBM256 : kBM) - 1) / (d == 256 ? kBM256 : kBM);
   a.group = group;
   split_scale(scale, &a.c, &a.negq);
   FwdSplit sp{1, Nk};
@@ -795,6 +1030,7 @@ hipError_t launch_fwd_bf16_kv(const void* q, const void* k, const void* v, void*
     a.Opart = (float*)ws;
     a.Lpart = (float*)((char*)ws + (rows * d * 4 + 255) / 256 * 256);
   }
+  if (d == 256) return causal ? launch_d256<true>(a, stream) : launch_d256<false>(a, stream);
   if (d == 128)
     return causal ? launch_bf16<128, 64, true>(a, stream) : launch_bf16<128, 64, false>(a, stream);
   return causal ? launch_bf16<64, 64, true>(a, stream) : launch_bf16<64, 64, false>(a, stream);

@@ -37,7 +37,8 @@
  *          validated before any HIP call is made, so a rejected call touches
  *          neither the device nor the stream.  B*H*N == 0 is a valid no-op.
  *          Nothing is thrown across the ABI.
- * Sizes    d must be 64 or 128.  B, H >= 0; 0 <= N <= FA_MAX_N.
+ * Sizes    d must be 64 or 128; the bfloat16 forwards (fa_fwd, fa_fwd_gqa,
+ *          fa_fwd_kv) also take d = 256.  B, H >= 0; 0 <= N <= FA_MAX_N.
  * Scale    Any finite float (the usual value is 1/sqrt(d)).
  */
 #ifndef FA_H_
@@ -56,7 +57,7 @@ enum {
   FA_ERR_NULL = 1,      /* a required pointer is NULL                        */
   FA_ERR_SHAPE = 2,     /* B, H or N negative, N > FA_MAX_N, overflow, or a
                            head count H that Hkv does not divide             */
-  FA_ERR_HEADDIM = 3,   /* d is not 64 or 128                                 */
+  FA_ERR_HEADDIM = 3,   /* d not supported by the entry point (see Sizes)     */
   FA_ERR_ALIGN = 4,     /* a tensor pointer is not 16-byte aligned            */
   FA_ERR_ALIAS = 5,     /* an output overlaps an input or another output      */
   FA_ERR_SCALE = 6,     /* scale is NaN or infinite                           */
@@ -80,7 +81,10 @@ enum {
  * Scores, the running max / running sum and the output accumulator are fp32;
  * the probability tile is rounded to bfloat16 for the P V product.  Tiles
  * whose keys all lie in the future of every query of the tile are skipped
- * ("LLM Architecture Refresh [3]", section 7).
+ * ("LLM Architecture Refresh [3]", section 7).  d = 64, 128 or 256 (d = 256
+ * runs a kernel with one wave per SIMD: its accumulator and query tile do not
+ * fit the two-wave schedule; "Flash Attention, From First Principles", "The
+ * rent arithmetic", on tiles shrinking as d grows).
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int H, int N, int d, int causal, float scale,

@@ -258,3 +258,17 @@ def test_kv_backward_rejects_bad_arguments(lib):
     # zero dk and dv on the device, so only a rejected form is tried here)
     assert b(Nq=0, q=None, o=None, dout=None, lse=None, dq=None, ws=None, dk=None) == \
         fa.FA_ERR_NULL
+
+
+def test_head_dim_256_only_on_the_bf16_forwards(lib):
+    # the bf16 forwards get past the head-dim check (then stop at the NULL q);
+    # the fp32 forward and the backward reject d = 256
+    assert _fwd(lib, d=256, q=None) == fa.FA_ERR_NULL
+    assert _fwd(lib, d=256, q=None, f32=True) == fa.FA_ERR_HEADDIM
+    assert lib.fa_fwd_gqa(None, A + MB, A + 2 * MB, A + 3 * MB, A + 4 * MB, 1, 2, 1, 100, 256,
+                          1, 0.1, None) == fa.FA_ERR_NULL
+    assert lib.fa_fwd_kv(None, A + MB, A + 2 * MB, A + 3 * MB, A + 4 * MB, None, 0, 1, 2, 2, 10,
+                         100, 256, 1, 0.1, None) == fa.FA_ERR_NULL
+    assert _bwd(lib, d=256) == fa.FA_ERR_HEADDIM
+    assert lib.fa_bwd_workspace_size(1, 2, 100, 256) == 0
+    assert _fwd(lib, d=512) == fa.FA_ERR_HEADDIM
