@@ -30,6 +30,8 @@ from .attention import (
     visible_mask_kv,
     naive_fwd_kv,
     naive_bwd_kv,
+    e4m3_decode,
+    naive_fwd_fp8,
 )
 from .tiled import (
     online_normaliser,
@@ -51,6 +53,8 @@ __all__ = [
     "visible_mask_kv",
     "naive_fwd_kv",
     "naive_bwd_kv",
+    "e4m3_decode",
+    "naive_fwd_fp8",
     "online_normaliser",
     "tiled_fwd",
     "tiled_bwd",

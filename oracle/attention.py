@@ -348,3 +348,39 @@ def naive_bwd_kv(q, k, v, do, scale: float, causal: bool = False):
             dq[b, h] = float(scale) * (ds @ k[b, g])             # dQ = s dS K
             dk[b, g] += float(scale) * (ds.T @ q[b, h])          # dK = s dS^T Q
     return dq, dk, dv
+
+
+# ---------------------------------------------------------------------------
+# 8-bit floating-point inputs
+#
+# "LLM Architecture Refresh [3]", section 8 points at FP8 matrix inputs (the
+# FA-3 direction) without fixing a format.  The reading taken: the OCP e4m3
+# format ("float8 e4m3fn": 1 sign bit, 4 exponent bits with bias 7, 3
+# mantissa bits; exponent 0 holds the subnormals m/8 * 2^-6; the all-ones
+# exponent with mantissa 7 is NaN; no infinities), one dequantisation factor
+# per tensor.  The oracle decodes the bytes to the exact values they stand for
+# and evaluates the plain definition on them in float64.
+# ---------------------------------------------------------------------------
+
+def e4m3_decode(codes) -> np.ndarray:
+    """float64 values of OCP e4m3 byte codes (any integer array)."""
+    c = np.asarray(codes).astype(np.int64) & 0xFF
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    mant = (c & 0x7).astype(np.float64)
+    val = np.where(e == 0, mant / 8.0 * 2.0 ** -6, (1.0 + mant / 8.0) * 2.0 ** (e - 7))
+    val = np.where((c & 0x7F) == 0x7F, np.nan, val)
+    return sign * val
+
+
+def naive_fwd_fp8(q8, k8, v8, q_scale: float, k_scale: float, v_scale: float, scale: float,
+                  causal: bool = False):
+    """Exact attention of the dequantised e4m3 tensors, float64: (O, lse).
+
+    q8, k8, v8: e4m3 byte codes [..., N, d]; the tensors are q_scale * q8,
+    k_scale * k8 and v_scale * v8.
+    """
+    q = float(q_scale) * e4m3_decode(q8)
+    k = float(k_scale) * e4m3_decode(k8)
+    v = float(v_scale) * e4m3_decode(v8)
+    return naive_fwd(q, k, v, scale, causal)

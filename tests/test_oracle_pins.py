@@ -494,3 +494,32 @@ def test_kv_decode_row_sees_every_key():
     k, v = (rng.standard_normal((1, 2, 40, 8)) for _ in range(2))
     for a, b in zip(naive_fwd_kv(q, k, v, 0.5, True), naive_fwd_kv(q, k, v, 0.5, False)):
         assert np.array_equal(a, b)
+
+
+# --- e4m3 inputs -------------------------------------------------------------------
+
+def test_e4m3_decode_matches_the_format_and_the_library():
+    """Spot values of the OCP e4m3 format, and every one of the 256 codes
+    against torch's float8_e4m3fn conversion (a library routine)."""
+    from oracle import e4m3_decode
+    spots = {0x38: 1.0, 0x40: 2.0, 0x30: 0.5, 0x7E: 448.0, 0x01: 2.0 ** -9, 0x08: 2.0 ** -6,
+             0x07: 7 * 2.0 ** -9, 0xB8: -1.0, 0x00: 0.0, 0x3C: 1.5}
+    for code, val in spots.items():
+        assert e4m3_decode(code) == val, hex(code)
+    assert np.isnan(e4m3_decode(0x7F)) and np.isnan(e4m3_decode(0xFF))
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    mine = e4m3_decode(codes)
+    both_nan = np.isnan(ref) & np.isnan(mine)
+    assert np.all(both_nan | (ref == mine))
+
+
+def test_fp8_oracle_is_attention_of_the_dequantised_inputs():
+    from oracle import naive_fwd_fp8
+    from workloads import make_fp8_inputs
+    q8, k8, v8, sq, sk, sv = make_fp8_inputs(1, 2, 40, 16, seed=3)
+    o, lse = naive_fwd_fp8(q8.numpy(), k8.numpy(), v8.numpy(), sq, sk, sv, 0.25, True)
+    deq = [x.view(torch.float8_e4m3fn).to(torch.float64) * s
+           for x, s in ((q8, sq), (k8, sk), (v8, sv))]
+    ref = torch.nn.functional.scaled_dot_product_attention(*deq, is_causal=True, scale=0.25)
+    assert np.max(np.abs(o - ref.numpy())) < 1e-13

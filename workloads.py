@@ -111,3 +111,24 @@ def make_gqa_inputs(B: int, H: int, Hkv: int, N: int, d: int, dtype=torch.bfloat
     if with_do:
         out.append(torch.randn((B, H, N, d), generator=g, dtype=torch.float32).to(dtype))
     return tuple(out)
+
+
+def make_fp8_inputs(B: int, H: int, N: int, d: int, seed: int = 0):
+    """e4m3 inputs: (q8, k8, v8) as uint8 byte codes [B, H, N, d] and their
+    dequantisation factors (q_scale, k_scale, v_scale).
+
+    torch.randn float32 tensors (q, k, v in that order) are scaled by
+    448 / max|x| (the largest e4m3 value) and cast to torch.float8_e4m3fn
+    (round to nearest even); the factor that maps the codes back is
+    max|x| / 448.
+    """
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    out, scales = [], []
+    for _ in range(3):
+        x = torch.randn((B, H, N, d), generator=g, dtype=torch.float32)
+        amax = float(x.abs().max()) if x.numel() else 1.0
+        s = (amax / 448.0) if amax > 0 else 1.0
+        out.append((x / s).to(torch.float8_e4m3fn).view(torch.uint8))
+        scales.append(s)
+    return out[0], out[1], out[2], scales[0], scales[1], scales[2]
