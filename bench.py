@@ -37,6 +37,7 @@ if ROOT not in sys.path:
 METRIC = "attention fwd/bwd TFLOP/s and % of bf16 MFMA peak at N=1k-32k, d=64/128"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # sources each kernel is built from: counter-derived traffic is used only while
 # they are unchanged
@@ -182,7 +183,8 @@ def run_extra_sweep():
     """Grouped-query, head-dimension-256 and different-length shapes:
     Llama-3.1-8B's real head sharing (32 query heads over 8 key/value heads)
     for the causal N = 4096 forward and backward, the d = 256 causal forward at
-    [1, 16, 4096, 256], and decode -- one new token per sequence against a
+    [1, 16, 4096, 256], the e4m3 forward at [1, 32, 4096, 128] causal (against
+    the fp8 peak), and decode -- one new token per sequence against a
     32k-token cache, split across workgroups by key range -- whose bound is
     HBM (every key and value byte is read once per key/value head)."""
     import torch
@@ -216,6 +218,18 @@ def run_extra_sweep():
     out["d256_n4096_causal_fwd"] = dict(
         ms=round(ms, 4), tflops=round(tf, 1), pct_of_bf16_peak=round(100 * tf / PEAK_BF16_TFLOPS, 1))
     del q, k, v, o, lse
+
+    from workloads import make_fp8_inputs
+    q8, k8, v8, sq, sk, sv = make_fp8_inputs(1, 32, 4096, 128, seed=10)
+    q8, k8, v8 = q8.cuda(), k8.cuda(), v8.cuda()
+    o = torch.empty((1, 32, 4096, 128), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((1, 32, 4096), dtype=torch.float32, device="cuda")
+    ms = _time_launches(lambda: fa.fa_fwd_fp8(q8, k8, v8, o, lse, sq, sk, sv, True, sc))
+    tf = fwd_flops(1, 32, 4096, 128, True) / (ms * 1e-3) / 1e12
+    out["fp8_llama8b_n4096_causal_fwd"] = dict(
+        ms=round(ms, 4), tflops=round(tf, 1), pct_of_fp8_peak=round(100 * tf / PEAK_FP8_TFLOPS, 1),
+        pct_of_bf16_peak=round(100 * tf / PEAK_BF16_TFLOPS, 1))
+    del q8, k8, v8, o, lse
 
     B, Nk = 8, 32768
     q = make_gqa_inputs(B, H, Hkv, 1, d, seed=7)[0].cuda()

@@ -26,7 +26,8 @@ import torch
 
 __all__ = [
     "FAError", "library_path", "load_library",
-    "fa_fwd", "fa_fwd_gqa", "fa_fwd_kv", "fa_fwd_kv_workspace_size", "fa_fwd_f32",
+    "fa_fwd", "fa_fwd_gqa", "fa_fwd_kv", "fa_fwd_kv_workspace_size", "fa_fwd_fp8",
+    "fa_fwd_f32",
     "fa_bwd", "fa_bwd_gqa", "fa_bwd_kv", "fa_bwd_workspace_size", "fa_status_string",
     "fa_bwd_preprocess", "fa_bwd_main", "fa_bwd_finalize",
     "forward", "backward", "attention",
@@ -82,6 +83,8 @@ def load_library():
     lib.fa_fwd_kv.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i, i, i, i, i, i, i, f,
                               vp]
     lib.fa_fwd_kv.restype = i
+    lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, f, f, f, i, i, i, i, i, f, vp]
+    lib.fa_fwd_fp8.restype = i
     lib.fa_fwd_f32.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
     lib.fa_fwd_f32.restype = i
     lib.fa_bwd_workspace_size.argtypes = [i, i, i, i]
@@ -225,6 +228,25 @@ def fa_fwd_kv(q, k, v, o, lse, workspace, causal: bool, scale: float, stream=Non
                                   int(bool(causal)), float(scale),
                                   _stream_handle(q.device, stream))
     _raise(st, "fa_fwd_kv")
+
+
+def fa_fwd_fp8(q8, k8, v8, o, lse, q_scale: float, k_scale: float, v_scale: float,
+               causal: bool, scale: float, stream=None) -> None:
+    """Forward on e4m3 inputs: ``q8``, ``k8``, ``v8`` [B,H,N,128] uint8 byte
+    codes (or torch.float8_e4m3fn) standing for q_scale * q8 etc.; ``o``
+    [B,H,N,128] bf16 and ``lse`` [B,H,N] f32 outputs."""
+    B, H, N, d = _dims(q8)
+    for t, nm in ((q8, "q8"), (k8, "k8"), (v8, "v8")):
+        if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
+            raise ValueError(f"{nm}: dtype {t.dtype} is not an e4m3 byte tensor")
+        _check(t, nm, (B, H, N, d), t.dtype, q8.device)
+    _check(o, "o", (B, H, N, d), torch.bfloat16, q8.device)
+    _check(lse, "lse", (B, H, N), torch.float32, q8.device)
+    st = load_library().fa_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(o), _ptr(lse),
+                                   float(q_scale), float(k_scale), float(v_scale), B, H, N, d,
+                                   int(bool(causal)), float(scale),
+                                   _stream_handle(q8.device, stream))
+    _raise(st, "fa_fwd_fp8")
 
 
 def fa_fwd_f32(q, k, v, o, lse, causal: bool, scale: float, stream=None) -> None:

@@ -188,6 +188,27 @@ int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
   return fwd_bf16(q, k, v, o, lse, B, H, Hkv, N, d, causal, scale, stream);
 }
 
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, float q_scale,
+               float k_scale, float v_scale, int B, int H, int N, int d, int causal, float scale,
+               hipStream_t stream) {
+  size_t te = 0, re = 0;
+  int st = check_common(B, H, N, d, scale, &te, &re);
+  if (st != FA_OK) return st;
+  if (d != 128) return FA_ERR_HEADDIM;
+  const float score = scale * q_scale * k_scale;
+  if (!isfinite(q_scale) || !isfinite(k_scale) || !isfinite(v_scale) || !isfinite(score))
+    return FA_ERR_SCALE;
+  if (re == 0) return FA_OK;
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(lse))
+    return FA_ERR_ALIGN;
+  const Range in[3] = {range_of(q, te), range_of(k, te), range_of(v, te)};
+  const Range out[2] = {range_of(o, te * 2), range_of(lse, re * 4)};
+  if (any_alias(in, 3, out, 2)) return FA_ERR_ALIAS;
+  return from_hip(
+      fa::launch_fwd_fp8(q, k, v, o, lse, B * H, N, d, causal != 0, score, v_scale, stream));
+}
+
 int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H,
                int N, int d, int causal, float scale, hipStream_t stream) {
   size_t te = 0, re = 0;

@@ -683,6 +683,265 @@ __global__ __launch_bounds__(256, 1) void fwd_d256_kernel(const FwdArgs a) {
   }
 }
 
+// FP8 forward ("LLM Architecture Refresh [3]", section 8: the FA-3 direction
+// of lower-precision matrix inputs).  Q, K and V arrive as OCP e4m3 bytes
+// with one dequantisation factor per tensor; both products run on
+// v_mfma_f32_32x32x64_f8f6f4 (fp8 inputs, fp32 accumulation), so the
+// probabilities are rounded to e4m3 for the P V product -- the error budget
+// of this path (3 mantissa bits on each p) is stated with its tests.  The
+// running max / sum, the rescale and the lse stay fp32 exactly as in the bf16
+// kernels.  Head dimension 128; 4 waves x 32 queries per workgroup, 64-key
+// tiles, one wave per SIMD (the fp8 products are half as long as the bf16
+// ones, so a wave interleaves little and the structure is the d = 256 one).
+//
+// Operand layouts of the 32x32x64 fp8 MFMA (same lane / byte -> k mapping in
+// A and B): lane l holds row (A) or column (B) l % 32 and 32 bytes, the k
+// values of half l / 32.
+//   S^T = K Q^T: A = K rows (32 consecutive features of the key per lane),
+//       B = Q^T (the same 32 features of the query).
+//   O^T += V^T P^T: B = P^T: lane (query n, half h) byte 16 sb + r holds p
+//       of key 32 sb + 8 (r / 4) + 4 h + r % 4 (the S^T accumulator's own
+//       registers, converted in place); A = V^T: four ds_read_b64_tr_b8 per
+//       32-feature block, read t giving bytes 8 t .. 8 t + 7 = keys
+//       16 t + 4 h + {0, 1, 2, 3, 8, 9, 10, 11} of that feature.
+// ds_read_b64_tr_b8: in each 16-lane group, lane 2j + c reads 8 bytes of row
+// j (bytes 8c .. 8c + 7 of a 16-byte column chunk); output lane i receives
+// byte i of rows 0..7.  K and V tiles use the row swizzle (r / 2) % 8 on
+// their 16-byte chunks, conflict-free for both read patterns.
+constexpr int kWavesF8 = 4;
+constexpr int kBMF8 = 32 * kWavesF8;
+constexpr int kBNF8 = 64;
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+
+__device__ __forceinline__ f32x16 mfma_32x32x64_f8(const i32x8& a, const i32x8& b,
+                                                   const f32x16& c) {
+  // formats 0 / 0: both operands e4m3; no block scales
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+__device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
+
+template <bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void fwd_fp8_kernel(const FwdArgs a, float vscale) {
+  constexpr int D = 128;
+  constexpr int BN = kBNF8;
+  constexpr int ROW = D;                      // bytes per fp8 row
+  constexpr int TILE = BN * ROW;              // 8 KiB
+  constexpr int DMA = TILE / (16 * 64 * kWavesF8);   // DMAs per lane per tile
+  constexpr int OFF_V = 2 * TILE;
+  extern __shared__ __attribute__((aligned(1024))) char smem_raw[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 31;
+  const int h = lane >> 5;
+  const int BH = a.BH, Nq = a.Nq, Nk = a.Nk, koff = a.koff;
+  const float c = a.c;
+  const unsigned char* Q8 = reinterpret_cast<const unsigned char*>(a.Q);
+  const unsigned char* K8 = reinterpret_cast<const unsigned char*>(a.K);
+  const unsigned char* V8 = reinterpret_cast<const unsigned char*>(a.V);
+
+  int bh, qt, sp = 0;
+  {
+    int bid = blockIdx.x;
+    if (a.nsplit > 1) {
+      sp = bid % a.nsplit;
+      bid /= a.nsplit;
+    }
+    map_tile(bid, BH, a.nqt, CAUSAL, &bh, &qt);
+  }
+  const size_t base = (size_t)bh * (size_t)Nq * D;
+  const size_t kvbase = (size_t)(bh / a.group) * (size_t)Nk * D;
+  const char* Kb = reinterpret_cast<const char*>(K8 + kvbase);
+  const char* Vb = reinterpret_cast<const char*>(V8 + kvbase);
+  const int q0 = qt * kBMF8;
+  const int wq0 = q0 + 32 * w;
+  const int qrow = wq0 + n;
+
+  const int kb = sp * a.klen;
+  int ke = min(Nk, kb + a.klen);
+  if (CAUSAL) ke = min(ke, q0 + kBMF8 + koff);
+  const int nkt = ke > kb ? (ke - kb + BN - 1) / BN : 0;
+
+  const unsigned ldsb = __builtin_amdgcn_readfirstlane(lds_addr(smem_raw));
+  auto issue = [&](int t) __attribute__((always_inline)) {
+    const int k0 = kb + t * BN;
+    const char* gk = Kb + (size_t)k0 * ROW;
+    const char* gv = Vb + (size_t)k0 * ROW;
+    const unsigned stk = ldsb + (t & 1) * TILE;
+    const unsigned stv = ldsb + OFF_V + (t & 1) * TILE;
+#pragma unroll
+    for (int i = 0; i < DMA; ++i) {
+      const int slot = (i * kWavesF8 + w) * 64 + lane;
+      const int row = slot / 8;
+      const int src_row = min(k0 + row, Nk - 1) - k0;
+      const int chunk = (slot % 8) ^ swz8(row);
+      const unsigned src = (unsigned)(src_row * ROW + chunk * 16);
+      const unsigned dst = (unsigned)((i * kWavesF8 + w) * 1024);
+      dma16(gk, src, stk + dst);
+      dma16(gv, src, stv + dst);
+    }
+  };
+  if (nkt > 0) issue(0);
+
+  // Q^T operand, k-steps cc = 0, 1: features 64 cc + 32 h .. + 31 (a
+  // negative score factor flips the e4m3 sign bits: exact)
+  i32x8 qf[2];
+  const uint32_t flip = a.negq ? 0x80808080u : 0u;
+#pragma unroll
+  for (int cc = 0; cc < 2; ++cc) {
+    u32x4 lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
+    if (qrow < Nq) {
+      const u32x4* src =
+          reinterpret_cast<const u32x4*>(Q8 + base + (size_t)qrow * D + 64 * cc + 32 * h);
+      lo = src[0] ^ flip;
+      hi = src[1] ^ flip;
+    }
+    qf[cc] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                   (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  }
+  // K operand address of (sub-block sb, k-step cc, 16-byte part u): row
+  // 32 sb + n, chunk 4 cc + 2 h + u
+  auto koff_of = [&](int sb, int cc, int u) __attribute__((always_inline)) {
+    const int row = 32 * sb + n;
+    return row * ROW + (((4 * cc + 2 * h + u) ^ swz8(row)) << 4);
+  };
+  // V^T operand address of (feature block db, read t): row 16 t + 4 h +
+  // 8 (j / 4) + j % 4, bytes 8 c of chunk 2 db + (lane % 32) / 16
+  const int jv = (lane & 15) >> 1;
+  const int cv = lane & 1;
+  const int gv = (lane >> 4) & 1;
+  auto voff_of = [&](int db, int t) __attribute__((always_inline)) {
+    const int row = 16 * t + 4 * h + 8 * (jv >> 2) + (jv & 3);
+    return row * ROW + (((2 * db + gv) ^ swz8(row)) << 4) + 8 * cv;
+  };
+
+  f32x16 acc[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+  float m = kMInit;
+  float lsum = 0.f;
+
+  for (int j = 0; j < nkt; ++j) {
+    wait_vmem();
+    __syncthreads();
+    if (j + 1 < nkt) issue(j + 1);
+    const char* ks = smem_raw + (j & 1) * TILE;
+    const char* vs = smem_raw + OFF_V + (j & 1) * TILE;
+    const int k0 = kb + j * BN;
+
+    f32x16 s[2];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      s[sb] = f32x16{};
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(ks + koff_of(sb, cc, 0));
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(ks + koff_of(sb, cc, 1));
+        const i32x8 kf = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                          (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        s[sb] = mfma_32x32x64_f8(kf, qf[cc], s[sb]);
+      }
+    }
+    if ((k0 + BN > ke) || (CAUSAL && k0 + BN - 1 > wq0 + koff)) {
+      int lim = ke - 1 - k0 - 4 * h;
+      if (CAUSAL) lim = min(lim, qrow + koff - k0 - 4 * h);
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int off = 32 * sb + 8 * (r >> 2) + (r & 3);
+          s[sb][r] = off > lim ? kNegInf : s[sb][r];
+        }
+    }
+    int pw[8];
+    auto probs = [&]() __attribute__((always_inline)) {
+      float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int r = 0; r < 16; r += 4) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][r], c, -m));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][r + 1], c, -m));
+          const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][r + 2], c, -m));
+          const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][r + 3], c, -m));
+          int word = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+          word = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, word, true);
+          pw[4 * sb + (r >> 2)] = word;
+          part[r >> 2] += (p0 + p1) + (p2 + p3);
+        }
+      return (part[0] + part[1]) + (part[2] + part[3]);
+    };
+    float ps = probs();
+    if (__any(ps > kSumBound)) {
+      float mx = kNegInf;
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sb][r]);
+      mx = fmaxf(mx, wave_xor32(mx));
+      const float m_new = fmaxf(m, mx * c);
+      const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+      lsum *= alpha;
+      m = m_new;
+      ps = probs();
+    }
+    lsum += ps;
+    const i32x8 pb = {pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      i32x2 r4[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        r4[t] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vs + voff_of(db, t)));
+      const i32x8 vf = {r4[0].x, r4[0].y, r4[1].x, r4[1].y, r4[2].x, r4[2].y, r4[3].x, r4[3].y};
+      acc[db] = mfma_32x32x64_f8(vf, pb, acc[db]);
+    }
+  }
+
+  const float lt = lsum + wave_xor32(lsum);
+  const float inv = lt > 0.f ? vscale / lt : 0.f;
+  const float lse = lt > 0.f ? (m + __log2f(lt)) * kLn2 : kNegInf;
+  if (qrow < Nq) {
+    if (a.nsplit == 1) {
+      uint16_t* orow = a.O + base + (size_t)qrow * D;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = 32 * db + 8 * g + 4 * h;
+          u32x2 out = {pack_bf16x2(acc[db][4 * g + 0] * inv, acc[db][4 * g + 1] * inv),
+                       pack_bf16x2(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv)};
+          *reinterpret_cast<u32x2*>(orow + d0) = out;
+        }
+      if (h == 0) a.LSE[(size_t)bh * Nq + qrow] = lse;
+    } else {
+      const size_t prow = ((size_t)sp * BH + bh) * Nq + qrow;
+      float* orow = a.Opart + prow * D;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = 32 * db + 8 * g + 4 * h;
+          f32x4 out = {acc[db][4 * g + 0] * inv, acc[db][4 * g + 1] * inv,
+                       acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv};
+          *reinterpret_cast<f32x4*>(orow + d0) = out;
+        }
+      if (h == 0) a.Lpart[prow] = lse;
+    }
+  }
+}
+
 // Merge of the key ranges ("Flash Attention, From First Principles", "The
 // scaffold": blocks over disjoint keys combine through their log-sum-exps):
 // lse = log sum_s e^{lse_s}, O = sum_s e^{lse_s - lse} O_s.  Ranges with
@@ -957,6 +1216,20 @@ hipError_t launch_d256(const FwdArgs& a, hipStream_t stream) {
   return launch_merge(a, 256, stream);
 }
 
+template <bool CAUSAL>
+hipError_t launch_fp8(const FwdArgs& a, float vscale, hipStream_t stream) {
+  constexpr int smem = 4 * kBNF8 * 128;
+  auto kern = fwd_fp8_kernel<CAUSAL>;
+  hipError_t e =
+      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(a.BH * a.nqt * a.nsplit), dim3(64 * kWavesF8), smem, stream, a,
+                     vscale);
+  e = hipGetLastError();
+  if (e != hipSuccess || a.nsplit == 1) return e;
+  return launch_merge(a, 128, stream);
+}
+
 template <int D, bool CAUSAL>
 hipError_t launch_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                       int BH, int N, float scale, hipStream_t stream) {
@@ -1034,6 +1307,30 @@ hipError_t launch_fwd_bf16_kv(const void* q, const void* k, const void* v, void*
   if (d == 128)
     return causal ? launch_bf16<128, 64, true>(a, stream) : launch_bf16<128, 64, false>(a, stream);
   return causal ? launch_bf16<64, 64, true>(a, stream) : launch_bf16<64, 64, false>(a, stream);
+}
+
+hipError_t launch_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int BH, int N, int d, bool causal, float score_scale, float v_scale,
+                          hipStream_t stream) {
+  if (d != 128) return hipErrorInvalidValue;
+  FwdArgs a;
+  a.Q = (const uint16_t*)q;   // byte tensors; the kernel reads them as e4m3
+  a.K = (const uint16_t*)k;
+  a.V = (const uint16_t*)v;
+  a.O = (uint16_t*)o;
+  a.LSE = lse;
+  a.Opart = nullptr;
+  a.Lpart = nullptr;
+  a.BH = BH;
+  a.Nq = N;
+  a.Nk = N;
+  a.koff = 0;
+  a.nqt = (N + kBMF8 - 1) / kBMF8;
+  a.nsplit = 1;
+  a.klen = N > 0 ? N : 1;
+  a.group = 1;
+  split_scale(score_scale, &a.c, &a.negq);
+  return causal ? launch_fp8<true>(a, v_scale, stream) : launch_fp8<false>(a, v_scale, stream);
 }
 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,

@@ -27,6 +27,12 @@ hipError_t launch_fwd_bf16_kv(const void* q, const void* k, const void* v, void*
                               void* ws, int BH, int Nq, int Nk, int d, int group, bool causal,
                               float scale, hipStream_t stream);
 
+// e4m3 Q, K, V (one byte per element), d = 128; score_scale already holds
+// scale * q_scale * k_scale; O = v_scale * softmax(...) (fp8 V).
+hipError_t launch_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int BH, int N, int d, bool causal, float score_scale, float v_scale,
+                          hipStream_t stream);
+
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                           int BH, int N, int d, bool causal, float scale, hipStream_t stream);
 

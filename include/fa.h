@@ -144,6 +144,31 @@ int fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse,
               hipStream_t stream);
 
 /*
+ * fa_fwd_fp8 -- forward pass with 8-bit floating-point inputs (the FA-3
+ * direction of "LLM Architecture Refresh [3]", section 8).
+ *
+ *   q, k, v   [B, H, N, d] OCP e4m3 ("float8 e4m3fn") bytes, one byte per
+ *             element; the values they stand for are q_scale * q, k_scale * k
+ *             and v_scale * v (one dequantisation factor per tensor).
+ *   o         [B, H, N, d] bfloat16 output;  lse [B, H, N] float32 output.
+ *   d         128 only (FA_ERR_HEADDIM otherwise).
+ *
+ * Computes the attention of the dequantised tensors: S = scale * q_scale *
+ * k_scale * (q k^T), lse and O = v_scale * softmax(S) v.  Both products run
+ * on the fp8 matrix cores with fp32 accumulation; the probabilities are
+ * rounded to e4m3 (3 mantissa bits) for the P V product, while the running
+ * max, the running sum and lse are fp32 from the unrounded probabilities.  So
+ * lse is as accurate as the bf16 path's, and each output element carries an
+ * error of at most about 2^-4 of the probability-weighted |v| it averages
+ * (plus the bf16 rounding of O); the tests state the bound per element.
+ * Errors as fa_fwd, plus FA_ERR_SCALE for a non-finite scale factor or
+ * product of factors.
+ */
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+               float q_scale, float k_scale, float v_scale, int B, int H, int N,
+               int d, int causal, float scale, hipStream_t stream);
+
+/*
  * fa_fwd_f32 -- forward pass, float32 tensors end to end.
  *
  * Same operation, layout and rules as fa_fwd with every tensor float32 and

@@ -40,7 +40,7 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = _declared_functions()
     assert set(names) == {"fa_fwd", "fa_fwd_gqa", "fa_fwd_kv", "fa_fwd_kv_workspace_size",
-                          "fa_fwd_f32", "fa_bwd", "fa_bwd_gqa", "fa_bwd_kv",
+                          "fa_fwd_fp8", "fa_fwd_f32", "fa_bwd", "fa_bwd_gqa", "fa_bwd_kv",
                           "fa_bwd_workspace_size",
                           "fa_status_string", "fa_bwd_preprocess", "fa_bwd_main",
                           "fa_bwd_finalize"}
@@ -272,3 +272,23 @@ def test_head_dim_256_only_on_the_bf16_forwards(lib):
     assert _bwd(lib, d=256) == fa.FA_ERR_HEADDIM
     assert lib.fa_bwd_workspace_size(1, 2, 100, 256) == 0
     assert _fwd(lib, d=512) == fa.FA_ERR_HEADDIM
+
+
+def test_fp8_forward_rejects_bad_arguments(lib):
+    def f(**kw):
+        g = dict(q=A, k=A + MB, v=A + 2 * MB, o=A + 3 * MB, lse=A + 5 * MB, qs=0.01, ks=0.01,
+                 vs=0.01, B=1, H=2, N=100, d=128, causal=1, scale=0.09)
+        g.update(kw)
+        return lib.fa_fwd_fp8(g["q"], g["k"], g["v"], g["o"], g["lse"], g["qs"], g["ks"],
+                              g["vs"], g["B"], g["H"], g["N"], g["d"], g["causal"], g["scale"],
+                              None)
+    assert f(d=64) == fa.FA_ERR_HEADDIM
+    assert f(d=256) == fa.FA_ERR_HEADDIM
+    assert f(qs=math.inf) == fa.FA_ERR_SCALE
+    assert f(vs=math.nan) == fa.FA_ERR_SCALE
+    assert f(qs=1e30, ks=1e30) == fa.FA_ERR_SCALE      # the product overflows
+    assert f(q=None) == fa.FA_ERR_NULL
+    assert f(k=A + MB + 4) == fa.FA_ERR_ALIGN
+    # q holds 2 x 100 x 128 bytes = 25600: an o starting inside it aliases
+    assert f(o=A + 25600 - 16) == fa.FA_ERR_ALIAS
+    assert f(N=0, q=None) == fa.FA_OK
