@@ -97,7 +97,7 @@ def run_step_bench(steps: int, warmup: int):
         fa.fa_bwd_main(q, k, v, do, dk, dv, ws, causal, w.scale)
         if ev is not None:
             ev[3].record(stream)
-        fa.fa_bwd_finalize(dq, ws)
+        fa.fa_bwd_finalize(dq, ws, q, k, v, do, causal, w.scale)
 
     for _ in range(warmup):
         step()

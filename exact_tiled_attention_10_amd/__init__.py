@@ -103,7 +103,8 @@ def load_library():
     lib.fa_bwd_main.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
                                 i, i, i, i, i, f, vp]
     lib.fa_bwd_main.restype = i
-    lib.fa_bwd_finalize.argtypes = [vp, vp, ctypes.c_size_t, i, i, i, i, vp]
+    lib.fa_bwd_finalize.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i, i, i, i, i, f,
+                                    vp]
     lib.fa_bwd_finalize.restype = i
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
@@ -332,7 +333,8 @@ def _ws_bytes(workspace, device):
 
 
 def fa_bwd_preprocess(o, dout, lse, workspace, stream=None) -> None:
-    """Backward stage 1: lse*log2(e), D = rowsum(dO * O), zeroed dQ accumulator."""
+    """Backward stage 1: lse*log2(e), D = rowsum(dO * O) (and at d = 64 a
+    zeroed dQ accumulator)."""
     B, H, N, d = _dims(o)
     for t, nm in ((o, "o"), (dout, "dout")):
         _check(t, nm, (B, H, N, d), torch.bfloat16, o.device)
@@ -345,7 +347,8 @@ def fa_bwd_preprocess(o, dout, lse, workspace, stream=None) -> None:
 
 def fa_bwd_main(q, k, v, dout, dk, dv, workspace, causal: bool, scale: float,
                 stream=None) -> None:
-    """Backward stage 2: the key-tile kernel (dK, dV, dQ accumulation)."""
+    """Backward stage 2: the key-tile kernel (dK, dV; at d = 64 also the dQ
+    accumulation)."""
     B, H, N, d = _dims(q)
     for t, nm in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout"), (dk, "dk"), (dv, "dv")):
         _check(t, nm, (B, H, N, d), torch.bfloat16, q.device)
@@ -357,12 +360,21 @@ def fa_bwd_main(q, k, v, dout, dk, dv, workspace, causal: bool, scale: float,
     _raise(st, "fa_bwd_main")
 
 
-def fa_bwd_finalize(dq, workspace, stream=None) -> None:
-    """Backward stage 3: dQ = bf16(accumulator)."""
+def fa_bwd_finalize(dq, workspace, q=None, k=None, v=None, dout=None, causal: bool = False,
+                    scale: float = 1.0, stream=None) -> None:
+    """Backward stage 3: dQ.  d = 64: dQ = bf16(accumulator) (q, k, v, dout
+    unused); d = 128, 256: the query-tile dQ kernel, which needs q, k, v,
+    dout, causal and scale as given to the other stages."""
     B, H, N, d = _dims(dq)
     _check(dq, "dq", (B, H, N, d), torch.bfloat16, dq.device)
-    st = load_library().fa_bwd_finalize(_ptr(dq), _ptr(workspace),
-                                        _ws_bytes(workspace, dq.device), B, H, N, d,
+    if d != 64:
+        for t, nm in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
+            if t is None:
+                raise ValueError(f"{nm} is needed by the d = {d} dQ stage")
+            _check(t, nm, (B, H, N, d), torch.bfloat16, dq.device)
+    st = load_library().fa_bwd_finalize(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq),
+                                        _ptr(workspace), _ws_bytes(workspace, dq.device),
+                                        B, H, N, d, int(bool(causal)), float(scale),
                                         _stream_handle(dq.device, stream))
     _raise(st, "fa_bwd_finalize")
 

@@ -28,8 +28,8 @@ bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) !
 
 // Shape, head-dim and scale checks shared by every entry point.  On success
 // writes the element count of one [B, H, N, d] tensor and of one [B, H, N]
-// statistic.  d is 64 or 128 everywhere; the bf16 forwards (wide = true) also
-// take 256.
+// statistic.  d is 64 or 128 everywhere; the bf16 entry points (wide = true)
+// also take 256.
 int check_common(int B, int H, int N, int d, float scale, size_t* tensor_elems,
                  size_t* row_elems, bool wide = false) {
   if (B < 0 || H < 0 || N < 0 || N > FA_MAX_N) return FA_ERR_SHAPE;
@@ -92,7 +92,7 @@ int bwd_bf16(const void* q, const void* k, const void* v, const void* o, const v
              size_t workspace_bytes, int B, int H, int Hkv, int Nq, int Nk, int d, int causal,
              float scale, hipStream_t stream) {
   size_t te = 0, re = 0;
-  int st = check_common(B, H, Nq, d, scale, &te, &re);
+  int st = check_common(B, H, Nq, d, scale, &te, &re, true);
   if (st != FA_OK) return st;
   if (Nk < 0 || Nk > FA_MAX_N) return FA_ERR_SHAPE;
   st = check_heads(H, Hkv);
@@ -125,7 +125,9 @@ int bwd_bf16(const void* q, const void* k, const void* v, const void* o, const v
     else   // no queries: every key's gradient is 0
       e = fa::launch_zero_bf16(dk, dv, kve, stream);
   }
-  if (e == hipSuccess && has_q) e = fa::launch_bwd_finalize(dq, workspace, BH, Nq, d, stream);
+  if (e == hipSuccess && has_q)
+    e = fa::launch_bwd_finalize(q, k, v, dout, dq, workspace, BH, Nq, Nk, d, H / Hkv,
+                                causal != 0, scale, stream);
   return from_hip(e);
 }
 
@@ -227,7 +229,7 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
 
 size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
   size_t te = 0, re = 0;
-  if (check_common(B, H, N, d, 1.0f, &te, &re) != FA_OK) return 0;
+  if (check_common(B, H, N, d, 1.0f, &te, &re, true) != FA_OK) return 0;
   return fa::bwd_workspace_bytes(B * H, N, d);
 }
 
@@ -258,7 +260,7 @@ int fa_bwd_kv(const void* q, const void* k, const void* v, const void* o, const 
 int fa_bwd_preprocess(const void* o, const void* dout, const float* lse, void* workspace,
                       size_t workspace_bytes, int B, int H, int N, int d, hipStream_t stream) {
   size_t te = 0, re = 0;
-  int st = check_common(B, H, N, d, 1.0f, &te, &re);
+  int st = check_common(B, H, N, d, 1.0f, &te, &re, true);
   if (st != FA_OK) return st;
   if (re == 0) return FA_OK;
   if (!o || !dout || !lse || !workspace) return FA_ERR_NULL;
@@ -277,7 +279,7 @@ int fa_bwd_main(const void* q, const void* k, const void* v, const void* dout, v
                 void* dv, void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
                 int causal, float scale, hipStream_t stream) {
   size_t te = 0, re = 0;
-  int st = check_common(B, H, N, d, scale, &te, &re);
+  int st = check_common(B, H, N, d, scale, &te, &re, true);
   if (st != FA_OK) return st;
   if (re == 0) return FA_OK;
   if (!q || !k || !v || !dout || !dk || !dv || !workspace) return FA_ERR_NULL;
@@ -294,20 +296,27 @@ int fa_bwd_main(const void* q, const void* k, const void* v, const void* dout, v
                                       causal != 0, scale, stream));
 }
 
-int fa_bwd_finalize(void* dq, const void* workspace, size_t workspace_bytes, int B, int H, int N,
-                    int d, hipStream_t stream) {
+int fa_bwd_finalize(const void* q, const void* k, const void* v, const void* dout, void* dq,
+                    const void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                    int causal, float scale, hipStream_t stream) {
   size_t te = 0, re = 0;
-  int st = check_common(B, H, N, d, 1.0f, &te, &re);
+  int st = check_common(B, H, N, d, scale, &te, &re, true);
   if (st != FA_OK) return st;
   if (re == 0) return FA_OK;
   if (!dq || !workspace) return FA_ERR_NULL;
-  if (misaligned(dq) || misaligned(workspace)) return FA_ERR_ALIGN;
+  if (d != 64 && (!q || !k || !v || !dout)) return FA_ERR_NULL;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(dout) || misaligned(dq) ||
+      misaligned(workspace))
+    return FA_ERR_ALIGN;
   const size_t need = fa::bwd_workspace_bytes(B * H, N, d);
   if (workspace_bytes < need) return FA_ERR_WORKSPACE;
-  const Range in[1] = {range_of(workspace, need)};
-  const Range out[1] = {range_of(dq, te * 2)};
-  if (any_alias(in, 1, out, 1)) return FA_ERR_ALIAS;
-  return from_hip(fa::launch_bwd_finalize(dq, workspace, B * H, N, d, stream));
+  const size_t tb = te * 2;
+  const Range in[5] = {range_of(workspace, need), range_of(q, tb), range_of(k, tb),
+                       range_of(v, tb), range_of(dout, tb)};
+  const Range out[1] = {range_of(dq, tb)};
+  if (any_alias(in, d == 64 ? 1 : 5, out, 1)) return FA_ERR_ALIAS;
+  return from_hip(fa::launch_bwd_finalize(q, k, v, dout, dq, workspace, B * H, N, N, d, 1,
+                                          causal != 0, scale, stream));
 }
 
 const char* fa_status_string(int status) {
@@ -318,7 +327,7 @@ const char* fa_status_string(int status) {
       return "invalid shape (B, H or N negative, N too large, size overflow, or H not a "
              "multiple of Hkv)";
     case FA_ERR_HEADDIM:
-      return "unsupported head dimension (64 or 128; the bf16 forwards also take 256)";
+      return "unsupported head dimension (64 or 128; the bf16 entry points also take 256)";
     case FA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
     case FA_ERR_ALIAS: return "an output overlaps an input or another output";
     case FA_ERR_SCALE: return "scale is not finite";

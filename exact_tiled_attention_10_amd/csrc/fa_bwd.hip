@@ -82,9 +82,11 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
       acc += bf16_bits_to_float(a[k] & 0xffffu) * bf16_bits_to_float(b[k] & 0xffffu);
       acc += bf16_bits_to_float(a[k] >> 16) * bf16_bits_to_float(b[k] >> 16);
     }
-    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    *reinterpret_cast<f32x4*>(dQacc + off) = z;
-    *reinterpret_cast<f32x4*>(dQacc + off + 4) = z;
+    if (dQacc) {   // only the atomic (d = 64) path has an accumulator
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      *reinterpret_cast<f32x4*>(dQacc + off) = z;
+      *reinterpret_cast<f32x4*>(dQacc + off + 4) = z;
+    }
   }
 #pragma unroll
   for (int s = TPR / 2; s >= 1; s >>= 1) acc += __shfl_xor(acc, s, 64);
@@ -113,7 +115,11 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(const float* __restrict__ d
 // ---------------------------------------------------------------------------
 template <int D>
 struct BwdCfg {
-  static constexpr int WAVES = D == 64 ? 8 : 4;   // d=64: 2 waves/SIMD; d=128: 1
+  static constexpr int WAVES = D == 64 ? 8 : 4;   // d=64: 2 waves/SIMD; else 1
+  // d = 64: dQ = dS K accumulated here with float atomics; d >= 128: dQ is
+  // the query-stationary kernel's, this one makes dK and dV only (no K tile
+  // or dS tile in LDS, no atomics)
+  static constexpr bool DQA = (D == 64);
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int KEYS = 32 * WAVES;         // keys per workgroup
   static constexpr int CPRD = D / 8;              // 16-byte chunks per Q / dO / K row
@@ -128,9 +134,9 @@ struct BwdCfg {
   static constexpr int KTILE = KEYS * D * 2;
   static constexpr int DSTILE = KEYS * kBQ * 2;
   static constexpr int OFF_K = 0;
-  static constexpr int OFF_ST = KTILE;                    // two stages
+  static constexpr int OFF_ST = DQA ? KTILE : 0;          // two stages
   static constexpr int OFF_DS = OFF_ST + 2 * STAGE;       // two dS buffers
-  static constexpr int SMEM = OFF_DS + 2 * DSTILE;
+  static constexpr int SMEM = OFF_DS + (DQA ? 2 * DSTILE : 0);
   static constexpr int QDMA = QTILE / 16 / THREADS;       // DMAs per thread per tile
   static constexpr int KDMA = KTILE / 16 / THREADS;
   // dQ = dS K in 32x32 blocks of the [kBQ, D] tile, each over all the tile's
@@ -193,7 +199,7 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_main_kernel(
   // key tile (row-major) for the K^T operand of dQ, read transposing by 16-
   // and 32-lane groups whose rows lie 8 apart: SWZ_BOTH keeps them apart
 #pragma unroll
-  for (int j = 0; j < C::KDMA; ++j) {
+  for (int j = 0; j < (C::DQA ? C::KDMA : 0); ++j) {
     const int slot = (j * C::WAVES + w) * 64 + lane;
     const int row = slot / C::CPRD;
     const int chunk = (slot % C::CPRD) ^ swz<C::CPRD, SWZ_BOTH>(row);
@@ -253,19 +259,21 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_main_kernel(
 
   // per-lane LDS offsets
   // row-operand reads of Q / dO (A of S and dP): row 32qs + n, features 16cc + 8h
-  int qro[C::NDC];
-#pragma unroll
-  for (int cc = 0; cc < C::NDC; ++cc) qro[cc] = tile_off<C::CPRD, SWZ_BOTH>(n, 16 * cc + 8 * h);
+  // (chunk index and swizzle occupy disjoint bits, so feature chunk cc / block
+  // db is the cc = 0 / db = 0 offset XOR 32 cc / 64 db: two base registers
+  // instead of an offset per chunk)
+  const int qro0 = tile_off<C::CPRD, SWZ_BOTH>(n, 8 * h);
+  auto qro = [&](int cc) __attribute__((always_inline)) { return qro0 ^ (32 * cc); };
   // transposing reads: 16-lane group g reads rows 4*(g/2) + j (+8 for the
   // second read) and columns 16*(g%2) + 4*(lane%4) of a 32-column block
   const int trow = 4 * (lane >> 5) + ((lane & 15) >> 2);
   const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  int qtr[C::NDB][2];   // dO^T / Q^T A operands (rows = queries)
-#pragma unroll
-  for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-    for (int rd = 0; rd < 2; ++rd)
-      qtr[db][rd] = tile_off<C::CPRD, SWZ_BOTH>(trow + 8 * rd, 32 * db + tcol);
+  // dO^T / Q^T A operands (rows = queries): rows trow and trow + 8
+  const int qtr0 = tile_off<C::CPRD, SWZ_BOTH>(trow, tcol);
+  const int qtr1 = tile_off<C::CPRD, SWZ_BOTH>(trow + 8, tcol);
+  auto qtr = [&](int db, int rd) __attribute__((always_inline)) {
+    return (rd ? qtr1 : qtr0) ^ (64 * db);
+  };
   // dS writes: row 32w + n (this lane's key), queries 32qs + 8g + 4h .. +3.
   // The dS tile is row-written and transposing-read, so it uses SWZ_BOTH; its
   // chunk positions are not affine in g, hence one offset per (qs, g).
@@ -292,7 +300,7 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_main_kernel(
   // P, or zeros written by waves with no visible key), so the k loop is
   // straight-line and only a block with no visible key at all is skipped.
   auto dq_step = [&](int t) {
-    if (w >= C::DQW) return;
+    if (!C::DQA || w >= C::DQW) return;
     const int gq = t / nit;
     const int q0 = (qb0 + (t - gq * nit)) * kBQ;
     const __amdgpu_buffer_rsrc_t dq_rsrc = dq_rsrc_of(gq);
@@ -346,7 +354,7 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_main_kernel(
     wait_vmem();
     __syncthreads();
     if (t + 1 < ntot) issue(t + 1);
-    if (t > 0) dq_step(t - 1);
+    if (C::DQA && t > 0) dq_step(t - 1);
 
     const char* st = smem + C::OFF_ST + (t & 1) * C::STAGE;
     const char* sQ = st;
@@ -366,8 +374,8 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_main_kernel(
         f32x16 s = zero, dp = zero;
 #pragma unroll
         for (int cc = 0; cc < C::NDC; ++cc) {
-          const bf16x8 aq = *reinterpret_cast<const bf16x8*>(sQ + qro[cc] + 32 * qs * C::RBD);
-          const bf16x8 ag = *reinterpret_cast<const bf16x8*>(sdO + qro[cc] + 32 * qs * C::RBD);
+          const bf16x8 aq = *reinterpret_cast<const bf16x8*>(sQ + qro(cc) + 32 * qs * C::RBD);
+          const bf16x8 ag = *reinterpret_cast<const bf16x8*>(sdO + qro(cc) + 32 * qs * C::RBD);
           s = mfma_32x32x16_bf16(aq, kf[cc], s);
           dp = mfma_32x32x16_bf16(ag, vf[cc], dp);
         }
@@ -419,10 +427,10 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_main_kernel(
           const int rowoff = (32 * qs + 16 * half) * C::RBD;
 #pragma unroll
           for (int db = 0; db < C::NDB; ++db) {
-            const u32x2 g0 = lds_read_tr16(sdO + qtr[db][0] + rowoff);
-            const u32x2 g1 = lds_read_tr16(sdO + qtr[db][1] + rowoff);
-            const u32x2 q0v = lds_read_tr16(sQ + qtr[db][0] + rowoff);
-            const u32x2 q1v = lds_read_tr16(sQ + qtr[db][1] + rowoff);
+            const u32x2 g0 = lds_read_tr16(sdO + qtr(db, 0) + rowoff);
+            const u32x2 g1 = lds_read_tr16(sdO + qtr(db, 1) + rowoff);
+            const u32x2 q0v = lds_read_tr16(sQ + qtr(db, 0) + rowoff);
+            const u32x2 q1v = lds_read_tr16(sQ + qtr(db, 1) + rowoff);
             dv[db] = mfma_32x32x16_bf16(__builtin_bit_cast(bf16x8, u32x4{g0.x, g0.y, g1.x, g1.y}),
                                         bp, dv[db]);
             dk[db] = mfma_32x32x16_bf16(
@@ -435,14 +443,18 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_main_kernel(
       }
       // dS (bf16) into LDS as [key][query]: registers 4g..4g+3 are queries
       // 32qs + 8g + 4h .. +3
+      if constexpr (C::DQA) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-        *reinterpret_cast<u32x2*>(dsb + dsw[qs][g]) = u32x2{sk[2 * g], sk[2 * g + 1]};
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<u32x2*>(dsb + dsw[qs][g]) = u32x2{sk[2 * g], sk[2 * g + 1]};
+      }
     }
   }
-  wait_vmem();
-  __syncthreads();
-  if (ntot > 0) dq_step(ntot - 1);
+  if constexpr (C::DQA) {
+    wait_vmem();
+    __syncthreads();
+    if (ntot > 0) dq_step(ntot - 1);
+  }
 
   // epilogue: dK = scale * dK^T acc, dV = dV^T acc (lane = key, registers = features)
   if (key < Nk) {
@@ -505,10 +517,203 @@ __global__ __launch_bounds__(256) void zero_pair_kernel(uint32_t* __restrict__ a
   reinterpret_cast<u32x4*>(b)[i] = z;
 }
 
+// ---------------------------------------------------------------------------
+// 4. dQ without atomics (d = 128 and 256): query-stationary
+// ---------------------------------------------------------------------------
+// At d >= 128 the key-tile kernel's dQ float atomics cost more than all its
+// matrix work (measured at d = 128: 860 us with them, 398 us without), so
+// there dQ gets its own pass over the key tiles, the loop order of the
+// forward: a workgroup owns 128 queries (4 waves x 32, one wave per SIMD) and
+// streams the key / value tiles past them, recomputing per tile
+//   S^T  = K Q^T,   dP^T = V dO^T       (MFMA; lane = query, as the forward)
+//   P    = exp2(c2 S - L2),  dS = P (dP - D)
+//   dQ^T += K^T dS^T                    (MFMA; dS^T already the B operand)
+// and writes dQ = scale * dQ^T once, in bf16: 1.5x the matrix work of the
+// key-tile kernel's dQ product ("FlashAttention from scratch", Follow-up
+// questions: dQ accumulated separately from dK and dV).  The K tile is read
+// both by rows (S) and transposed (dQ), so it uses the two-pattern swizzle;
+// V is only read by rows.
+template <int D>
+struct DqCfg {
+  static constexpr int WAVES = 4;
+  static constexpr int QB = 32 * WAVES;
+  static constexpr int BN = D == 256 ? 32 : 64;
+  static constexpr int CPR = D / 8;
+  static constexpr int ROW = CPR * 16;
+  static constexpr int TILE = BN * ROW;
+  static constexpr int NSB = BN / 32;
+  static constexpr int NQC = D / 16;
+  static constexpr int NDB = D / 32;
+  static constexpr int DMA = TILE / (16 * 64 * WAVES);
+  static constexpr int OFF_V = 2 * TILE;
+  static constexpr int SMEM = 4 * TILE;
+  static_assert(DMA * 16 * 64 * WAVES == TILE, "DMA split");
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void bwd_dq_direct_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+    const float* __restrict__ L2, const float* __restrict__ Dv, uint16_t* __restrict__ dQ,
+    int BH, int Nq, int Nk, int koff, int Npad, int nqt, int group, float scale, float c2) {
+  using C = DqCfg<D>;
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 31;
+  const int h = lane >> 5;
+
+  int bh, qt;
+  map_tile(blockIdx.x, BH, nqt, CAUSAL, &bh, &qt);
+  const size_t qbase = (size_t)bh * (size_t)Nq * D;
+  const size_t kvbase = (size_t)(bh / group) * (size_t)Nk * D;
+  const char* Kb = reinterpret_cast<const char*>(K + kvbase);
+  const char* Vb = reinterpret_cast<const char*>(V + kvbase);
+  const int q0 = qt * C::QB;
+  const int wq0 = q0 + 32 * w;
+  const int qrow = wq0 + n;
+  const int ke = CAUSAL ? min(Nk, q0 + C::QB + koff) : Nk;
+  const int nkt = ke > 0 ? (ke + C::BN - 1) / C::BN : 0;
+
+  const unsigned lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem));
+  auto issue = [&](int t) __attribute__((always_inline)) {
+    const int k0 = t * C::BN;
+    const char* gk = Kb + (size_t)k0 * C::ROW;
+    const char* gv = Vb + (size_t)k0 * C::ROW;
+#pragma unroll
+    for (int i = 0; i < C::DMA; ++i) {
+      const int slot = (i * C::WAVES + w) * 64 + lane;
+      const int row = slot / C::CPR;
+      const int src_row = min(k0 + row, Nk - 1) - k0;
+      const int ck = (slot % C::CPR) ^ swz<C::CPR, SWZ_BOTH>(row);
+      const int cv = (slot % C::CPR) ^ swz<C::CPR, SWZ_ROWS>(row);
+      const unsigned dst = (unsigned)((i * C::WAVES + w) * 1024);
+      dma16(gk, (unsigned)(src_row * C::ROW + ck * 16), lds0 + (t & 1) * C::TILE + dst);
+      dma16(gv, (unsigned)(src_row * C::ROW + cv * 16), lds0 + C::OFF_V + (t & 1) * C::TILE + dst);
+    }
+  };
+  if (nkt > 0) issue(0);
+
+  // Q^T and dO^T as B operands: lane = query, features 16 cc + 8 h .. + 7
+  bf16x8 qf[C::NQC], gf[C::NQC];
+#pragma unroll
+  for (int cc = 0; cc < C::NQC; ++cc) {
+    u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+    if (qrow < Nq) {
+      a = *reinterpret_cast<const u32x4*>(Q + qbase + (size_t)qrow * D + 16 * cc + 8 * h);
+      b = *reinterpret_cast<const u32x4*>(dO + qbase + (size_t)qrow * D + 16 * cc + 8 * h);
+    }
+    qf[cc] = __builtin_bit_cast(bf16x8, a);
+    gf[cc] = __builtin_bit_cast(bf16x8, b);
+  }
+  const float l2 = qrow < Nq ? L2[(size_t)bh * Npad + qrow] : 0.f;
+  const float dd = qrow < Nq ? Dv[(size_t)bh * Npad + qrow] : 0.f;
+
+  // row reads (A of S^T and dP^T): row 32 sb + n, chunk 2 cc + h
+  const int ka = tile_off<C::CPR, SWZ_BOTH>(n, 8 * h);
+  const int va = tile_off<C::CPR, SWZ_ROWS>(n, 8 * h);
+  // transposing reads of the K tile (A of dQ^T = K^T dS^T), the forward's
+  // V^T pattern: rows vrow0 (+ 8) of each 16-key chunk, columns 32 db + vcol0
+  const int vrow0 = 4 * (lane >> 5) + ((lane & 15) >> 2);
+  const int vcol0 = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int kt_lo = tile_off<C::CPR, SWZ_BOTH>(vrow0, vcol0);
+  const int kt_hi = tile_off<C::CPR, SWZ_BOTH>(vrow0 + 8, vcol0);
+
+  f32x16 acc[C::NDB];
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+
+  for (int j = 0; j < nkt; ++j) {
+    wait_vmem();
+    __syncthreads();
+    if (j + 1 < nkt) issue(j + 1);
+    const char* ks = smem + (j & 1) * C::TILE;
+    const char* vs = smem + C::OFF_V + (j & 1) * C::TILE;
+    const int k0 = j * C::BN;
+
+    f32x16 s[C::NSB], dp[C::NSB];
+#pragma unroll
+    for (int sb = 0; sb < C::NSB; ++sb) {
+      s[sb] = f32x16{};
+      dp[sb] = f32x16{};
+#pragma unroll
+      for (int cc = 0; cc < C::NQC; ++cc) {
+        const bf16x8 kf =
+            *reinterpret_cast<const bf16x8*>(ks + (ka ^ (32 * cc)) + 32 * sb * C::ROW);
+        const bf16x8 vf =
+            *reinterpret_cast<const bf16x8*>(vs + (va ^ (32 * cc)) + 32 * sb * C::ROW);
+        s[sb] = mfma_32x32x16_bf16(kf, qf[cc], s[sb]);
+        dp[sb] = mfma_32x32x16_bf16(vf, gf[cc], dp[sb]);
+      }
+    }
+    // register r of sub-block sb holds key k0 + 32 sb + 8 (r / 4) + 4 h + r % 4
+    const bool masked = (k0 + C::BN > Nk) || (CAUSAL && k0 + C::BN - 1 > wq0 + koff);
+    int lim = Nk - 1 - k0 - 4 * h;
+    if (CAUSAL) lim = min(lim, qrow + koff - k0 - 4 * h);
+    uint32_t dsk[C::NSB][8];
+    auto form = [&](auto mk) __attribute__((always_inline)) {
+#pragma unroll
+      for (int sb = 0; sb < C::NSB; ++sb)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          float d2[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int rr = r + u;
+            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][rr], c2, -l2));
+            if constexpr (decltype(mk)::value) {
+              const int off = 32 * sb + 8 * (rr >> 2) + (rr & 3);
+              p = off > lim ? 0.f : p;   // select after the exp: l2 may be -inf
+            }
+            d2[u] = p * (dp[sb][rr] - dd);
+          }
+          dsk[sb][r >> 1] = pack_bf16x2(d2[0], d2[1]);
+        }
+    };
+    if (masked)
+      form(std::true_type{});
+    else
+      form(std::false_type{});
+
+#pragma unroll
+    for (int kc = 0; kc < C::BN / 16; ++kc) {
+      const int sb = kc >> 1, half = kc & 1;
+      const bf16x8 b = __builtin_bit_cast(
+          bf16x8, u32x4{dsk[sb][4 * half], dsk[sb][4 * half + 1], dsk[sb][4 * half + 2],
+                        dsk[sb][4 * half + 3]});
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) {
+        const u32x2 lo = lds_read_tr16(ks + (kt_lo ^ (64 * db)) + 16 * kc * C::ROW);
+        const u32x2 hi = lds_read_tr16(ks + (kt_hi ^ (64 * db)) + 16 * kc * C::ROW);
+        acc[db] = mfma_32x32x16_bf16(__builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y}),
+                                     b, acc[db]);
+      }
+    }
+  }
+
+  if (qrow < Nq) {
+    uint16_t* drow = dQ + qbase + (size_t)qrow * D;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * db + 8 * g + 4 * h;
+        u32x2 out = {pack_bf16x2(scale * acc[db][4 * g + 0], scale * acc[db][4 * g + 1]),
+                     pack_bf16x2(scale * acc[db][4 * g + 2], scale * acc[db][4 * g + 3])};
+        *reinterpret_cast<u32x2*>(drow + d0) = out;
+      }
+  }
+}
+
 }  // namespace
 
 size_t bwd_workspace_bytes(int BH, int N, int d) {
-  return 2 * round256((size_t)BH * pad_rows(N) * 4) + (size_t)BH * N * d * 4;
+  // L2 and D rows; the fp32 dQ accumulator only where dQ is accumulated by
+  // atomics (d = 64)
+  return 2 * round256((size_t)BH * pad_rows(N) * 4) + (d == 64 ? (size_t)BH * N * d * 4 : 0);
 }
 
 hipError_t launch_bwd_pre(const void* o, const void* dout, const float* lse, void* ws, int BH,
@@ -518,14 +723,17 @@ hipError_t launch_bwd_pre(const void* o, const void* dout, const float* lse, voi
   const size_t prow = (size_t)BH * Npad;
   const size_t threads = prow * (d / 8);
   const unsigned blocks = (unsigned)((threads + 255) / 256);
-  if (d == 128)
-    hipLaunchKernelGGL(bwd_pre_kernel<128>, dim3(blocks), dim3(256), 0, stream,
-                       (const uint16_t*)o, (const uint16_t*)dout, lse, w.l2, w.dv, w.dq, N, Npad,
-                       prow);
+  const uint16_t* o16 = (const uint16_t*)o;
+  const uint16_t* g16 = (const uint16_t*)dout;
+  if (d == 256)
+    hipLaunchKernelGGL(bwd_pre_kernel<256>, dim3(blocks), dim3(256), 0, stream, o16, g16, lse,
+                       w.l2, w.dv, (float*)nullptr, N, Npad, prow);
+  else if (d == 128)
+    hipLaunchKernelGGL(bwd_pre_kernel<128>, dim3(blocks), dim3(256), 0, stream, o16, g16, lse,
+                       w.l2, w.dv, (float*)nullptr, N, Npad, prow);
   else
-    hipLaunchKernelGGL(bwd_pre_kernel<64>, dim3(blocks), dim3(256), 0, stream,
-                       (const uint16_t*)o, (const uint16_t*)dout, lse, w.l2, w.dv, w.dq, N, Npad,
-                       prow);
+    hipLaunchKernelGGL(bwd_pre_kernel<64>, dim3(blocks), dim3(256), 0, stream, o16, g16, lse,
+                       w.l2, w.dv, w.dq, N, Npad, prow);
   return hipGetLastError();
 }
 
@@ -534,6 +742,10 @@ hipError_t launch_bwd_main(const void* q, const void* k, const void* v, const vo
                            bool causal, float scale, hipStream_t stream) {
   if (Nk <= 0) return hipSuccess;   // no keys: no dK / dV rows, dQ stays 0
   const WsLayout w = ws_layout(ws, BH, Nq);
+  if (d == 256)
+    return causal
+               ? launch_main<256, true>(q, k, v, dout, w, dk, dv, BH, Nq, Nk, group, scale, stream)
+               : launch_main<256, false>(q, k, v, dout, w, dk, dv, BH, Nq, Nk, group, scale, stream);
   if (d == 128)
     return causal
                ? launch_main<128, true>(q, k, v, dout, w, dk, dv, BH, Nq, Nk, group, scale, stream)
@@ -552,13 +764,40 @@ hipError_t launch_zero_bf16(void* a, void* b, size_t elems, hipStream_t stream) 
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_finalize(void* dq, const void* ws, int BH, int N, int d,
-                               hipStream_t stream) {
-  const WsLayout w = ws_layout(const_cast<void*>(ws), BH, N);
-  const size_t n8 = (size_t)BH * N * d / 8;
-  hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream,
-                     w.dq, (uint16_t*)dq, n8);
+template <int D, bool CAUSAL>
+hipError_t launch_dq(const void* q, const void* k, const void* v, const void* dout, void* dq,
+                     const WsLayout& w, int BH, int Nq, int Nk, int group, float scale,
+                     hipStream_t stream) {
+  using C = DqCfg<D>;
+  auto kern = bwd_dq_direct_kernel<D, CAUSAL>;
+  hipError_t e =
+      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::SMEM);
+  if (e != hipSuccess) return e;
+  const int nqt = (Nq + C::QB - 1) / C::QB;
+  hipLaunchKernelGGL(kern, dim3(BH * nqt), dim3(64 * C::WAVES), C::SMEM, stream,
+                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
+                     (const uint16_t*)dout, w.l2, w.dv, (uint16_t*)dq, BH, Nq, Nk, Nk - Nq,
+                     pad_rows(Nq), nqt, group, scale, scale * kLog2e);
   return hipGetLastError();
+}
+
+hipError_t launch_bwd_finalize(const void* q, const void* k, const void* v, const void* dout,
+                               void* dq, const void* ws, int BH, int Nq, int Nk, int d, int group,
+                               bool causal, float scale, hipStream_t stream) {
+  const WsLayout w = ws_layout(const_cast<void*>(ws), BH, Nq);
+  if (d == 64) {
+    const size_t n8 = (size_t)BH * Nq * d / 8;
+    if (n8 == 0) return hipSuccess;
+    hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream,
+                       w.dq, (uint16_t*)dq, n8);
+    return hipGetLastError();
+  }
+  if (Nk <= 0) return launch_zero_bf16(dq, dq, (size_t)BH * Nq * d, stream);
+  if (d == 256)
+    return causal ? launch_dq<256, true>(q, k, v, dout, dq, w, BH, Nq, Nk, group, scale, stream)
+                  : launch_dq<256, false>(q, k, v, dout, dq, w, BH, Nq, Nk, group, scale, stream);
+  return causal ? launch_dq<128, true>(q, k, v, dout, dq, w, BH, Nq, Nk, group, scale, stream)
+                : launch_dq<128, false>(q, k, v, dout, dq, w, BH, Nq, Nk, group, scale, stream);
 }
 
 }  // namespace fa

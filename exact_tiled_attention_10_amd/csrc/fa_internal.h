@@ -51,7 +51,10 @@ hipError_t launch_bwd_main(const void* q, const void* k, const void* v, const vo
                            bool causal, float scale, hipStream_t stream);
 // Two bf16 tensors of `elems` elements each (a multiple of 8) set to 0.
 hipError_t launch_zero_bf16(void* a, void* b, size_t elems, hipStream_t stream);
-hipError_t launch_bwd_finalize(void* dq, const void* ws, int BH, int N, int d,
-                               hipStream_t stream);
+// d = 64: dQ = bf16(accumulator); d = 128, 256: the query-stationary dQ
+// kernel (recomputes S and dP; no accumulator).
+hipError_t launch_bwd_finalize(const void* q, const void* k, const void* v, const void* dout,
+                               void* dq, const void* ws, int BH, int Nq, int Nk, int d, int group,
+                               bool causal, float scale, hipStream_t stream);
 
 }  // namespace fa

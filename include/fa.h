@@ -37,8 +37,9 @@
  *          validated before any HIP call is made, so a rejected call touches
  *          neither the device nor the stream.  B*H*N == 0 is a valid no-op.
  *          Nothing is thrown across the ABI.
- * Sizes    d must be 64 or 128; the bfloat16 forwards (fa_fwd, fa_fwd_gqa,
- *          fa_fwd_kv) also take d = 256.  B, H >= 0; 0 <= N <= FA_MAX_N.
+ * Sizes    d must be 64 or 128; the bfloat16 entry points (the forwards
+ *          fa_fwd, fa_fwd_gqa, fa_fwd_kv and the backwards) also take
+ *          d = 256; fa_fwd_fp8 takes 128 only.  B, H >= 0; 0 <= N <= FA_MAX_N.
  * Scale    Any finite float (the usual value is 1/sqrt(d)).
  */
 #ifndef FA_H_
@@ -183,7 +184,7 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o,
  *
  * Returns 0 for invalid shapes.  The workspace holds, per row, lse * log2(e)
  * and D = rowsum(dO * O) (float32, each head padded to a multiple of 64 rows)
- * and the float32 dQ accumulator ([B, H, N, d]).
+ * and, at d = 64 only, the float32 dQ accumulator ([B, H, N, d]).
  */
 size_t fa_bwd_workspace_size(int B, int H, int N, int d);
 
@@ -202,9 +203,11 @@ size_t fa_bwd_workspace_size(int B, int H, int N, int d);
  * Recomputes every probability tile from Q, K and lse ("FlashAttention from
  * scratch", Follow-up questions): P = exp(S - L); dV += P^T dO; dP = dO V^T;
  * D = rowsum(dO * O); dS = P * (dP - D); dK += scale * dS^T Q; dQ += scale *
- * dS K.  dK and dV accumulate per key tile; dQ accumulates across key tiles
- * in the float32 workspace with atomic adds, so dQ may differ between runs in
- * its last bits.
+ * dS K.  dK and dV accumulate per key tile.  dQ is accumulated separately:
+ * at d = 64 across key tiles in the float32 workspace with atomic adds (dQ
+ * may then differ between runs in its last bits); at d = 128 and 256 by a
+ * second pass that owns query tiles and recomputes S and dP (no atomics,
+ * deterministic).  d = 64, 128 or 256.
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            const void* dout, const float* lse, void* dq, void* dk, void* dv,
@@ -253,12 +256,17 @@ int fa_bwd_kv(const void* q, const void* k, const void* v, const void* o,
  * (its own pointers only) and reads/writes the workspace as documented.
  *
  * fa_bwd_preprocess -- lse * log2(e) and D = rowsum(dO * O) into the
- *                      workspace; zeroes the workspace's fp32 dQ accumulator.
+ *                      workspace; at d = 64 zeroes the workspace's fp32 dQ
+ *                      accumulator.
  * fa_bwd_main       -- the key-tile kernel: recomputes P from q, k and the
- *                      workspace's log-sum-exp, writes dk and dv, and adds
- *                      scale * dS K into the dQ accumulator (float atomics).
- *                      Needs the preprocess stage's workspace contents.
- * fa_bwd_finalize   -- dq = bf16(dQ accumulator).
+ *                      workspace's log-sum-exp and writes dk and dv; at d = 64
+ *                      it also adds scale * dS K into the dQ accumulator
+ *                      (float atomics).  Needs the preprocess stage's
+ *                      workspace contents.
+ * fa_bwd_finalize   -- dq: at d = 64 bf16(dQ accumulator) (q, k, v, dout,
+ *                      causal and scale are not read and may be NULL / any);
+ *                      at d = 128 and 256 the query-tile dQ kernel, which
+ *                      needs them and the preprocess stage's workspace.
  */
 int fa_bwd_preprocess(const void* o, const void* dout, const float* lse,
                       void* workspace, size_t workspace_bytes, int B, int H,
@@ -267,8 +275,10 @@ int fa_bwd_main(const void* q, const void* k, const void* v, const void* dout,
                 void* dk, void* dv, void* workspace, size_t workspace_bytes,
                 int B, int H, int N, int d, int causal, float scale,
                 hipStream_t stream);
-int fa_bwd_finalize(void* dq, const void* workspace, size_t workspace_bytes,
-                    int B, int H, int N, int d, hipStream_t stream);
+int fa_bwd_finalize(const void* q, const void* k, const void* v,
+                    const void* dout, void* dq, const void* workspace,
+                    size_t workspace_bytes, int B, int H, int N, int d, int causal,
+                    float scale, hipStream_t stream);
 
 /* fa_status_string -- static, human-readable text for a status code. */
 const char* fa_status_string(int status);

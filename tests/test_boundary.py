@@ -99,10 +99,13 @@ def test_forward_empty_is_noop(lib, f32):
 def test_workspace_size(lib):
     assert lib.fa_bwd_workspace_size(1, 2, 100, 32) == 0
     assert lib.fa_bwd_workspace_size(1, 2, -1, 64) == 0
-    for (B, H, N, d) in ((1, 2, 100, 64), (4, 16, 2048, 64), (1, 8, 32768, 128)):
+    for (B, H, N, d) in ((1, 2, 100, 64), (4, 16, 2048, 64), (1, 8, 32768, 128),
+                         (1, 2, 300, 256)):
         ws = lib.fa_bwd_workspace_size(B, H, N, d)
-        # at least D (fp32 per row) plus the fp32 dQ accumulator
-        assert ws >= B * H * N * 4 + B * H * N * d * 4
+        # L2 and D (fp32 per row), plus the fp32 dQ accumulator where dQ is
+        # accumulated with atomics (d = 64)
+        need = 2 * B * H * N * 4 + (B * H * N * d * 4 if d == 64 else 0)
+        assert ws >= need
         assert ws % 16 == 0
 
 
@@ -161,10 +164,20 @@ def test_backward_stages_reject_bad_arguments(lib):
     assert mk(dk=A + 8 * MB + 16) == fa.FA_ERR_ALIAS        # dk overlaps dv
     assert mk(ws=A + MB) == fa.FA_ERR_ALIAS                 # workspace over k
     assert mk(scale=math.inf) == fa.FA_ERR_SCALE
-    assert lib.fa_bwd_finalize(A + 6 * MB, w, 4, 1, 2, 100, 64, None) == fa.FA_ERR_WORKSPACE
-    assert lib.fa_bwd_finalize(None, w, ws, 1, 2, 100, 64, None) == fa.FA_ERR_NULL
-    assert lib.fa_bwd_finalize(w + 16, w, ws, 1, 2, 100, 64, None) == fa.FA_ERR_ALIAS
-    assert lib.fa_bwd_finalize(A + 6 * MB + 2, w, ws, 1, 2, 100, 64, None) == fa.FA_ERR_ALIGN
+    fin = lambda dq, wsp, wsb, d=64, q=None, k=None, v=None, g=None: lib.fa_bwd_finalize(  # noqa
+        q, k, v, g, dq, wsp, wsb, 1, 2, 100, d, 1, 0.125, None)
+    assert fin(A + 6 * MB, w, 4) == fa.FA_ERR_WORKSPACE
+    assert fin(None, w, ws) == fa.FA_ERR_NULL
+    assert fin(w + 16, w, ws) == fa.FA_ERR_ALIAS
+    assert fin(A + 6 * MB + 2, w, ws) == fa.FA_ERR_ALIGN
+    # d = 128: the query-tile dQ kernel needs q, k, v and dout
+    ws128 = lib.fa_bwd_workspace_size(1, 2, 100, 128)
+    assert fin(A + 6 * MB, w, ws128, d=128) == fa.FA_ERR_NULL
+    assert fin(A + 6 * MB, w, ws128, d=128, q=A, k=A + MB, v=A + 2 * MB,
+               g=A + 6 * MB + 64) == fa.FA_ERR_ALIAS          # dq over dout
+    # only the d = 64 path keeps a dQ accumulator in the workspace
+    assert ws128 < lib.fa_bwd_workspace_size(1, 2, 100, 64) * 2
+    assert lib.fa_bwd_workspace_size(1, 2, 100, 256) == ws128
 
 
 def test_gqa_entry_points_reject_bad_head_counts(lib):
@@ -260,17 +273,17 @@ def test_kv_backward_rejects_bad_arguments(lib):
         fa.FA_ERR_NULL
 
 
-def test_head_dim_256_only_on_the_bf16_forwards(lib):
-    # the bf16 forwards get past the head-dim check (then stop at the NULL q);
-    # the fp32 forward and the backward reject d = 256
+def test_head_dim_256_only_on_the_bf16_entry_points(lib):
+    # the bf16 forwards and backwards get past the head-dim check (then stop at
+    # a NULL pointer); the fp32 and fp8 forwards reject d = 256
     assert _fwd(lib, d=256, q=None) == fa.FA_ERR_NULL
     assert _fwd(lib, d=256, q=None, f32=True) == fa.FA_ERR_HEADDIM
     assert lib.fa_fwd_gqa(None, A + MB, A + 2 * MB, A + 3 * MB, A + 4 * MB, 1, 2, 1, 100, 256,
                           1, 0.1, None) == fa.FA_ERR_NULL
     assert lib.fa_fwd_kv(None, A + MB, A + 2 * MB, A + 3 * MB, A + 4 * MB, None, 0, 1, 2, 2, 10,
                          100, 256, 1, 0.1, None) == fa.FA_ERR_NULL
-    assert _bwd(lib, d=256) == fa.FA_ERR_HEADDIM
-    assert lib.fa_bwd_workspace_size(1, 2, 100, 256) == 0
+    assert _bwd(lib, d=256, dout=None) == fa.FA_ERR_NULL    # the backward takes 256 too
+    assert lib.fa_bwd_workspace_size(1, 2, 100, 256) > 0
     assert _fwd(lib, d=512) == fa.FA_ERR_HEADDIM
 
 

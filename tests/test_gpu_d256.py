@@ -101,3 +101,35 @@ def test_d256_large_sampled():
         wl = max(wl, float(np.max(np.abs(gl[0, h, rows] - rl))))
     _say(f"[d256 4096 sampled] max|dO|={wo:.3e} max|dlse|={wl:.3e}")
     assert wo <= TOL and wl <= TOL_LSE
+
+
+# --- backward at d = 256 -----------------------------------------------------------
+
+def _bwd_check(q, k, v, do, causal, scale):
+    from oracle import naive_bwd_kv
+    qd, kd, vd, dod = (t.cuda() for t in (q, k, v, do))
+    o, lse = fa.forward(qd, kd, vd, causal, scale)
+    dq, dk, dv = fa.backward(qd, kd, vd, o, lse, dod, causal, scale)
+    torch.cuda.synchronize()
+    ref = naive_bwd_kv(_f64(q), _f64(k), _f64(v), _f64(do), scale, causal)
+    tol = max(TOL, 2.0 ** -7 * max(float(np.max(np.abs(r))) for r in ref))
+    errs = [float(np.max(np.abs(_f64(g) - r))) for g, r in zip((dq, dk, dv), ref)]
+    _say(f"   max|d dQ|={errs[0]:.3e} |d dK|={errs[1]:.3e} |d dV|={errs[2]:.3e} (tol {tol:.3e})")
+    for g in (dq, dk, dv):
+        assert torch.isfinite(g).all()
+    assert max(errs) <= tol
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 33, 129, 300])
+def test_d256_backward(N, causal):
+    _say(f"[d256 bwd] N={N} causal={causal}")
+    q, k, v, do = make_inputs(1, 2, N, D, torch.bfloat16, seed=1500 + N, with_do=True)
+    _bwd_check(q, k, v, do, causal, 1 / math.sqrt(D))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_d256_backward_gqa_and_lengths(causal):
+    q = make_gqa_inputs(1, 4, 2, 150, D, seed=1600, with_do=True)
+    k, v = make_gqa_inputs(1, 4, 2, 400, D, seed=1601)[1:]
+    _bwd_check(q[0], k, v, q[3], causal, 1 / math.sqrt(D))
