@@ -236,7 +236,7 @@ def run_extra_sweep():
     k, v = (t.cuda() for t in make_gqa_inputs(B, H, Hkv, Nk, d, seed=8)[1:])
     o = torch.empty_like(q)
     lse = torch.empty((B, H, 1), dtype=torch.float32, device="cuda")
-    nb = fa.fa_fwd_kv_workspace_size(B, H, 1, Nk, d)
+    nb = fa.fa_fwd_kv_workspace_size(B, H, Hkv, 1, Nk, d)
     ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
     ms = _time_launches(lambda: fa.fa_fwd_kv(q, k, v, o, lse, ws, True, sc), reps=50)
     nbytes = 2 * B * Hkv * Nk * d * 2 + 2 * B * H * d * 2 + B * H * 4

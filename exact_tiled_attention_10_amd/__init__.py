@@ -78,7 +78,7 @@ def load_library():
     lib.fa_fwd.restype = i
     lib.fa_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
     lib.fa_fwd_gqa.restype = i
-    lib.fa_fwd_kv_workspace_size.argtypes = [i, i, i, i, i]
+    lib.fa_fwd_kv_workspace_size.argtypes = [i, i, i, i, i, i]
     lib.fa_fwd_kv_workspace_size.restype = ctypes.c_size_t
     lib.fa_fwd_kv.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i, i, i, i, i, i, i, f,
                               vp]
@@ -202,8 +202,8 @@ def fa_fwd_gqa(q, k, v, o, lse, causal: bool, scale: float, stream=None) -> None
     _raise(st, "fa_fwd_gqa")
 
 
-def fa_fwd_kv_workspace_size(B: int, H: int, Nq: int, Nk: int, d: int) -> int:
-    return int(load_library().fa_fwd_kv_workspace_size(B, H, Nq, Nk, d))
+def fa_fwd_kv_workspace_size(B: int, H: int, Hkv: int, Nq: int, Nk: int, d: int) -> int:
+    return int(load_library().fa_fwd_kv_workspace_size(B, H, Hkv, Nq, Nk, d))
 
 
 def fa_fwd_kv(q, k, v, o, lse, workspace, causal: bool, scale: float, stream=None) -> None:
@@ -395,7 +395,7 @@ def forward(q, k, v, causal: bool = False, scale: Optional[float] = None,
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     if q.dtype != torch.float32 and k.dim() == 4 and k.shape[2] != N:
-        nb = fa_fwd_kv_workspace_size(B, H, N, k.shape[2], d)
+        nb = fa_fwd_kv_workspace_size(B, H, k.shape[1], N, k.shape[2], d)
         ws = torch.empty(nb, dtype=torch.uint8, device=q.device) if nb else None
         fa_fwd_kv(q, k, v, o, lse, ws, causal, s, stream)
     elif q.dtype == torch.float32:

@@ -151,11 +151,11 @@ int check_kv(int B, int H, int Hkv, int Nq, int Nk, int d, float scale, size_t* 
 
 extern "C" {
 
-size_t fa_fwd_kv_workspace_size(int B, int H, int Nq, int Nk, int d) {
+size_t fa_fwd_kv_workspace_size(int B, int H, int Hkv, int Nq, int Nk, int d) {
   size_t te = 0, re = 0;
   if (check_common(B, H, Nq, d, 1.f, &te, &re, true) != FA_OK) return 0;
-  if (Nk < 0 || Nk > FA_MAX_N || re == 0) return 0;
-  return fa::fwd_workspace_bytes(B * H, Nq, Nk, d);
+  if (Nk < 0 || Nk > FA_MAX_N || re == 0 || check_heads(H, Hkv) != FA_OK) return 0;
+  return fa::fwd_workspace_bytes(B * H, H / Hkv, Nq, Nk, d);
 }
 
 int fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
@@ -169,7 +169,7 @@ int fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse, 
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(lse) ||
       misaligned(workspace))
     return FA_ERR_ALIGN;
-  const size_t need = fa::fwd_workspace_bytes(B * H, Nq, Nk, d);
+  const size_t need = fa::fwd_workspace_bytes(B * H, H / Hkv, Nq, Nk, d);
   if (need > 0 && workspace_bytes < need) return FA_ERR_WORKSPACE;
   if (need > 0 && !workspace) return FA_ERR_NULL;
   const Range in[3] = {range_of(q, qe * 2), range_of(k, kve * 2), range_of(v, kve * 2)};

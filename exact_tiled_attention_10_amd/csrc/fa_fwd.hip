@@ -942,6 +942,194 @@ __global__ __launch_bounds__(256, 1) void fwd_fp8_kernel(const FwdArgs a, float 
   }
 }
 
+// Decode (few query rows per key / value head: generated tokens against a
+// cache, "LLM Architecture Refresh [3]", section 6 and the notes on prompt and
+// generated tokens).  The 256-query tile would compute 256 rows for each key
+// tile and use a handful.  Here one wave owns EVERY query row that reads a key
+// / value head -- the group's query heads times the Nq positions, R <= 32 rows
+// packed into the 32 MFMA columns -- so each key and value byte is read once
+// per key / value head, and each workgroup (one wave) streams one range of the
+// keys.  S^T = K Q^T (lane = packed row), the lazy-rebase softmax and
+// O^T += V^T P^T are the forward kernel's; ranges merge through
+// fwd_merge_kernel.  32-key tiles by DMA, two stages (a wave's own, no
+// barrier).
+constexpr int kBNDec = 32;
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(64) void fwd_decode_kernel(const FwdArgs a) {
+  constexpr int BN = kBNDec;
+  constexpr int CPR = D / 8;
+  constexpr int ROW = CPR * 16;
+  constexpr int TILE = BN * ROW;
+  constexpr int NQC = D / 16;
+  constexpr int NDB = D / 32;
+  constexpr int DMA = TILE / (16 * 64);
+  constexpr int OFF_V = 2 * TILE;
+  extern __shared__ __attribute__((aligned(1024))) char smem_raw[];
+
+  const int lane = threadIdx.x;
+  const int n = lane & 31;
+  const int h = lane >> 5;
+  const int Nq = a.Nq, Nk = a.Nk, koff = a.koff;
+  const float c = a.c;
+  const int R = a.group * Nq;                 // packed rows of this head's group
+  const int kvh = blockIdx.x / a.nsplit;      // b * Hkv + key/value head
+  const int sp = blockIdx.x - kvh * a.nsplit;
+  const bool live = n < R;
+  const int g = live ? n / Nq : 0;            // query head within the group
+  const int pos = live ? n - g * Nq : 0;      // query position
+  const int bh = kvh * a.group + g;           // b * H + query head
+  const size_t qoff = ((size_t)bh * Nq + pos) * D;
+  const size_t kvbase = (size_t)kvh * (size_t)Nk * D;
+  const char* Kb = reinterpret_cast<const char*>(a.K + kvbase);
+  const char* Vb = reinterpret_cast<const char*>(a.V + kvbase);
+
+  const int kb = sp * a.klen;
+  const int ke = min(Nk, kb + a.klen);
+  const int nkt = ke > kb ? (ke - kb + BN - 1) / BN : 0;
+
+  const unsigned ldsb = __builtin_amdgcn_readfirstlane(lds_addr(smem_raw));
+  auto issue = [&](int t) __attribute__((always_inline)) {
+    const int k0 = kb + t * BN;
+    const char* gk = Kb + (size_t)k0 * ROW;
+    const char* gv = Vb + (size_t)k0 * ROW;
+#pragma unroll
+    for (int i = 0; i < DMA; ++i) {
+      const int slot = i * 64 + lane;
+      const int row = slot / CPR;
+      const int src_row = min(k0 + row, Nk - 1) - k0;
+      const int ck = (slot % CPR) ^ swz<CPR, SWZ_ROWS>(row);
+      const int cv = (slot % CPR) ^ swz<CPR, SWZ_TR>(row);
+      dma16(gk, (unsigned)(src_row * ROW + ck * 16), ldsb + (t & 1) * TILE + i * 1024);
+      dma16(gv, (unsigned)(src_row * ROW + cv * 16), ldsb + OFF_V + (t & 1) * TILE + i * 1024);
+    }
+  };
+  if (nkt > 0) issue(0);
+
+  bf16x8 qf[NQC];
+  {
+    const uint32_t flip = a.negq ? 0x80008000u : 0u;
+#pragma unroll
+    for (int cc = 0; cc < NQC; ++cc) {
+      u32x4 raw = {0u, 0u, 0u, 0u};
+      if (live) raw = *reinterpret_cast<const u32x4*>(a.Q + qoff + 16 * cc + 8 * h);
+      raw ^= flip;
+      qf[cc] = __builtin_bit_cast(bf16x8, raw);
+    }
+  }
+  const int ka = tile_off<CPR, SWZ_ROWS>(n, 8 * h);
+  const int vrow0 = 4 * (lane >> 5) + ((lane & 15) >> 2);
+  const int vcol0 = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int va = tile_off<CPR, SWZ_TR>(vrow0, vcol0);
+
+  f32x16 acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+  float m = kMInit;
+  float lsum = 0.f;
+  // last key this lane's row sees (rows past R see nothing)
+  const int last = live ? (CAUSAL ? min(ke - 1, pos + koff) : ke - 1) : -1;
+
+  for (int j = 0; j < nkt; ++j) {
+    wait_vmem();   // this wave's DMA of tile j landed (tile j - 1's reads are done)
+    if (j + 1 < nkt) issue(j + 1);
+    const char* ks = smem_raw + (j & 1) * TILE;
+    const char* vs = smem_raw + OFF_V + (j & 1) * TILE;
+    const int k0 = kb + j * BN;
+
+    f32x16 s = {};
+#pragma unroll
+    for (int cc = 0; cc < NQC; ++cc) {
+      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + (ka ^ (32 * cc)));
+      s = mfma_32x32x16_bf16(kf, qf[cc], s);
+    }
+    {
+      const int lim = last - k0 - 4 * h;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int off = 8 * (r >> 2) + (r & 3);
+        s[r] = off > lim ? kNegInf : s[r];
+      }
+    }
+    uint32_t pk[8];
+    auto probs = [&]() __attribute__((always_inline)) {
+      float part[2] = {0.f, 0.f};
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -m));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r + 1], c, -m));
+        pk[r >> 1] = pack_bf16x2(p0, p1);
+        part[(r >> 1) & 1] += p0 + p1;
+      }
+      return part[0] + part[1];
+    };
+    float ps = probs();
+    if (__any(ps > kSumBound)) {
+      float mx = kNegInf;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+      mx = fmaxf(mx, wave_xor32(mx));
+      const float m_new = fmaxf(m, mx * c);
+      const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+      lsum *= alpha;
+      m = m_new;
+      ps = probs();
+    }
+    lsum += ps;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const bf16x8 b = __builtin_bit_cast(
+          bf16x8, u32x4{pk[4 * half], pk[4 * half + 1], pk[4 * half + 2], pk[4 * half + 3]});
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const char* vp = vs + (va ^ (64 * db)) + 16 * half * ROW;
+        const u32x2 lo = lds_read_tr16(vp);
+        const u32x2 hi = lds_read_tr16(vp + 8 * ROW);
+        acc[db] = mfma_32x32x16_bf16(__builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y}),
+                                     b, acc[db]);
+      }
+    }
+  }
+
+  const float lt = lsum + wave_xor32(lsum);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  const float lse = lt > 0.f ? (m + __log2f(lt)) * kLn2 : kNegInf;
+  if (live) {
+    if (a.nsplit == 1) {
+      uint16_t* orow = a.O + qoff;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+          const int d0 = 32 * db + 8 * gg + 4 * h;
+          u32x2 out = {pack_bf16x2(acc[db][4 * gg + 0] * inv, acc[db][4 * gg + 1] * inv),
+                       pack_bf16x2(acc[db][4 * gg + 2] * inv, acc[db][4 * gg + 3] * inv)};
+          *reinterpret_cast<u32x2*>(orow + d0) = out;
+        }
+      if (h == 0) a.LSE[(size_t)bh * Nq + pos] = lse;
+    } else {
+      const size_t prow = ((size_t)sp * a.BH + bh) * Nq + pos;
+      float* orow = a.Opart + prow * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+          const int d0 = 32 * db + 8 * gg + 4 * h;
+          f32x4 out = {acc[db][4 * gg + 0] * inv, acc[db][4 * gg + 1] * inv,
+                       acc[db][4 * gg + 2] * inv, acc[db][4 * gg + 3] * inv};
+          *reinterpret_cast<f32x4*>(orow + d0) = out;
+        }
+      if (h == 0) a.Lpart[prow] = lse;
+    }
+  }
+}
+
 // Merge of the key ranges ("Flash Attention, From First Principles", "The
 // scaffold": blocks over disjoint keys combine through their log-sum-exps):
 // lse = log sum_s e^{lse_s}, O = sum_s e^{lse_s - lse} O_s.  Ranges with
@@ -1203,6 +1391,19 @@ hipError_t launch_merge(const FwdArgs& a, int d, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int D, bool CAUSAL>
+hipError_t launch_decode(const FwdArgs& a, hipStream_t stream) {
+  constexpr int smem = 4 * kBNDec * D * 2;
+  auto kern = fwd_decode_kernel<D, CAUSAL>;
+  hipError_t e =
+      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3((a.BH / a.group) * a.nsplit), dim3(64), smem, stream, a);
+  e = hipGetLastError();
+  if (e != hipSuccess || a.nsplit == 1) return e;
+  return launch_merge(a, D, stream);
+}
+
 template <bool CAUSAL>
 hipError_t launch_d256(const FwdArgs& a, hipStream_t stream) {
   constexpr int smem = 4 * kBN256 * 256 * 2;
@@ -1249,30 +1450,47 @@ hipError_t launch_f32(const float* q, const float* k, const float* v, float* o, 
 
 }  // namespace
 
-// Key splitting: only when the query tiles alone leave the chip idle (fewer
-// than 256 workgroups) and a workspace is given.  Each range keeps at least
-// four key tiles so its DMA pipeline fills; the workgroup count aims at two
-// per CU.
-FwdSplit fwd_split(int BH, int Nq, int Nk, int d) {
-  FwdSplit sp{1, Nk};
+// Plan of a forward launch.  Decode: when all query rows that read a key /
+// value head fit one wave (group * Nq <= 32, d = 64 or 128) the packed-rows
+// kernel runs, its keys split into ranges of at least 128 keys aiming at four
+// one-wave workgroups per CU.  Otherwise the tile kernels, whose keys are
+// split only when the query tiles alone leave the chip idle (fewer than 256
+// workgroups): ranges of at least four 64-key tiles, two workgroups per CU.
+// Splitting needs the caller's workspace (has_ws).
+FwdPlan fwd_plan(int BH, int group, int Nq, int Nk, int d, bool has_ws) {
+  FwdPlan pl{0, 1, Nk};
+  if (Nk <= 0 || BH <= 0 || Nq <= 0) return pl;
   const int bn = 64;   // a multiple of every kernel's key tile
+  const int nkt = (Nk + bn - 1) / bn;
+  if ((d == 64 || d == 128) && (long long)group * Nq <= 32) {
+    pl.decode = 1;
+    if (!has_ws) return pl;
+    const long long heads = BH / group;
+    int ns = (int)((1024 + heads - 1) / heads);
+    ns = std::min(ns, std::max(1, Nk / 128));
+    if (ns <= 1) return pl;
+    const int tiles_per = (nkt + ns - 1) / ns;
+    pl.klen = tiles_per * bn;
+    pl.nsplit = (Nk + pl.klen - 1) / pl.klen;
+    return pl;
+  }
+  if (!has_ws) return pl;
   const int bm = d == 256 ? kBM256 : kBM;
   const long long tiles = (long long)BH * ((Nq + bm - 1) / bm);
-  if (tiles <= 0 || tiles >= 256 || Nk <= 0) return sp;
-  const int nkt = (Nk + bn - 1) / bn;
+  if (tiles >= 256) return pl;
   int ns = (int)((512 + tiles - 1) / tiles);
   ns = std::min(ns, nkt / 4);
-  if (ns <= 1) return sp;
+  if (ns <= 1) return pl;
   const int tiles_per = (nkt + ns - 1) / ns;
-  sp.klen = tiles_per * bn;
-  sp.nsplit = (Nk + sp.klen - 1) / sp.klen;
-  return sp;
+  pl.klen = tiles_per * bn;
+  pl.nsplit = (Nk + pl.klen - 1) / pl.klen;
+  return pl;
 }
 
-size_t fwd_workspace_bytes(int BH, int Nq, int Nk, int d) {
-  const FwdSplit sp = fwd_split(BH, Nq, Nk, d);
-  if (sp.nsplit <= 1) return 0;
-  const size_t rows = (size_t)sp.nsplit * BH * Nq;
+size_t fwd_workspace_bytes(int BH, int group, int Nq, int Nk, int d) {
+  const FwdPlan pl = fwd_plan(BH, group, Nq, Nk, d, true);
+  if (pl.nsplit <= 1) return 0;
+  const size_t rows = (size_t)pl.nsplit * BH * Nq;
   return (rows * d * 4 + 255) / 256 * 256 + rows * 4;
 }
 
@@ -1292,16 +1510,20 @@ hipError_t launch_fwd_bf16_kv(const void* q, const void* k, const void* v, void*
   a.nqt = (Nq + (d == 256 ? kBM256 : kBM) - 1) / (d == 256 ? kBM256 : kBM);
   a.group = group;
   split_scale(scale, &a.c, &a.negq);
-  FwdSplit sp{1, Nk};
-  if (ws) sp = fwd_split(BH, Nq, Nk, d);
-  a.nsplit = sp.nsplit;
-  a.klen = sp.nsplit > 1 ? sp.klen : (Nk > 0 ? Nk : 1);
+  const FwdPlan pl = fwd_plan(BH, group, Nq, Nk, d, ws != nullptr);
+  a.nsplit = pl.nsplit;
+  a.klen = pl.nsplit > 1 ? pl.klen : (Nk > 0 ? Nk : 1);
   a.Opart = nullptr;
   a.Lpart = nullptr;
   if (a.nsplit > 1) {
     const size_t rows = (size_t)a.nsplit * BH * Nq;
     a.Opart = (float*)ws;
     a.Lpart = (float*)((char*)ws + (rows * d * 4 + 255) / 256 * 256);
+  }
+  if (pl.decode) {
+    if (d == 128)
+      return causal ? launch_decode<128, true>(a, stream) : launch_decode<128, false>(a, stream);
+    return causal ? launch_decode<64, true>(a, stream) : launch_decode<64, false>(a, stream);
   }
   if (d == 256) return causal ? launch_d256<true>(a, stream) : launch_d256<false>(a, stream);
   if (d == 128)

@@ -17,12 +17,13 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
 // Nq query rows against Nk keys (bottom-right causal alignment).  With a
 // workspace of fwd_workspace_bytes(), the keys may be split across
 // workgroups and merged by a second kernel; with ws == nullptr never.
-struct FwdSplit {
-  int nsplit;
-  int klen;
+struct FwdPlan {
+  int decode;   // 1: packed-rows decode kernel
+  int nsplit;   // key ranges (1: none)
+  int klen;     // keys per range
 };
-FwdSplit fwd_split(int BH, int Nq, int Nk, int d);
-size_t fwd_workspace_bytes(int BH, int Nq, int Nk, int d);
+FwdPlan fwd_plan(int BH, int group, int Nq, int Nk, int d, bool has_ws);
+size_t fwd_workspace_bytes(int BH, int group, int Nq, int Nk, int d);
 hipError_t launch_fwd_bf16_kv(const void* q, const void* k, const void* v, void* o, float* lse,
                               void* ws, int BH, int Nq, int Nk, int d, int group, bool causal,
                               float scale, hipStream_t stream);

@@ -122,15 +122,19 @@ int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
  *               for Nq = Nk exactly the rule of fa_fwd).  A query that sees
  *               no key (with causal masking the first Nq - Nk queries when
  *               Nq > Nk; every query when Nk = 0) gets O = 0 and lse = -inf.
- *   workspace   device memory of at least fa_fwd_kv_workspace_size(B, H, Nq,
- *               Nk, d) bytes, 16-byte aligned; may be NULL when that size is 0.
+ *   workspace   device memory of at least fa_fwd_kv_workspace_size(B, H, Hkv,
+ *               Nq, Nk, d) bytes, 16-byte aligned; may be NULL when that size
+ *               is 0.
  *
  * The pages define attention for one length n ("LLM Architecture Refresh
  * [3]", the notes before the references, which also point out that
  * generation splits a sequence into a prompt and new tokens); the alignment
- * above is the reading that places the queries at the end.  When the query
- * tiles alone would leave most of the GPU idle (few heads, small Nq: decode),
- * the keys are split into ranges handled by separate workgroups, each writing
+ * above is the reading that places the queries at the end.  When every query
+ * row that reads a key / value head fits in one wave ((H / Hkv) * Nq <= 32,
+ * d = 64 or 128: decode), one wave computes all of them against a range of
+ * keys, so each key and value byte is read once per key / value head.  When
+ * the work alone would leave most of the GPU idle (decode, few heads, small
+ * Nq), the keys are split into ranges handled by separate workgroups, each writing
  * a normalised partial output and its log-sum-exp to the workspace, and a
  * second kernel merges the ranges by the block law of "Flash Attention, From
  * First Principles", "The scaffold": lse = log sum_r e^{lse_r},
@@ -138,7 +142,7 @@ int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
  * Errors as fa_fwd, plus FA_ERR_WORKSPACE for a workspace that is too small;
  * k and v may be NULL when Nk == 0.
  */
-size_t fa_fwd_kv_workspace_size(int B, int H, int Nq, int Nk, int d);
+size_t fa_fwd_kv_workspace_size(int B, int H, int Hkv, int Nq, int Nk, int d);
 int fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse,
               void* workspace, size_t workspace_bytes, int B, int H, int Hkv,
               int Nq, int Nk, int d, int causal, float scale,

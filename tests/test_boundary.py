@@ -209,17 +209,18 @@ def test_gqa_entry_points_reject_bad_head_counts(lib):
 
 def test_kv_workspace_size(lib):
     # plenty of query tiles: no key split, no workspace
-    assert lib.fa_fwd_kv_workspace_size(1, 32, 4096, 4096, 128) == 0
-    assert lib.fa_fwd_kv_workspace_size(1, 2, 100, -1, 64) == 0
-    assert lib.fa_fwd_kv_workspace_size(1, 2, 100, 100, 96) == 0
+    assert lib.fa_fwd_kv_workspace_size(1, 32, 32, 4096, 4096, 128) == 0
+    assert lib.fa_fwd_kv_workspace_size(1, 2, 2, 100, -1, 64) == 0
+    assert lib.fa_fwd_kv_workspace_size(1, 2, 2, 100, 100, 96) == 0
+    assert lib.fa_fwd_kv_workspace_size(1, 4, 3, 1, 4096, 128) == 0   # 4 heads over 3
     # decode (one query row per head): the keys are split, partials need room
-    ws = lib.fa_fwd_kv_workspace_size(1, 2, 1, 4096, 128)
+    ws = lib.fa_fwd_kv_workspace_size(1, 2, 2, 1, 4096, 128)
     assert ws > 0 and ws % 4 == 0
     assert ws >= 2 * 2 * 1 * (128 + 1) * 4       # at least two ranges of O and lse
 
 
 def test_kv_forward_rejects_bad_arguments(lib):
-    ws_need = lib.fa_fwd_kv_workspace_size(1, 2, 1, 4096, 128)
+    ws_need = lib.fa_fwd_kv_workspace_size(1, 2, 2, 1, 4096, 128)
     W = A + 9 * MB
 
     def f(**kw):

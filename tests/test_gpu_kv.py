@@ -53,7 +53,7 @@ def _run(q, k, v, causal, scale, use_ws=True):
     Nk = k.shape[2]
     o = torch.full_like(qd, float("nan"))
     lse = torch.full((B, H, Nq), float("nan"), dtype=torch.float32, device="cuda")
-    nb = fa.fa_fwd_kv_workspace_size(B, H, Nq, Nk, d)
+    nb = fa.fa_fwd_kv_workspace_size(B, H, k.shape[1], Nq, Nk, d)
     ws = torch.full((nb,), 0xFF, dtype=torch.uint8, device="cuda") if (nb and use_ws) else None
     if nb and not use_ws:
         pytest.skip("this shape needs a workspace")
@@ -201,3 +201,18 @@ def test_kv_backward_no_queries_zeroes_key_gradients():
     torch.cuda.synchronize()
     assert st == fa.FA_OK
     assert torch.all(dk == 0) and torch.all(dv == 0)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("H,Hkv,nq,nk", [(8, 2, 8, 5000), (8, 1, 4, 3001), (8, 1, 5, 3001),
+                                         (4, 4, 32, 900), (2, 1, 1, 1)])
+def test_kv_decode_packed_rows(H, Hkv, nq, nk, causal, d):
+    """The packed-rows decode kernel: group * Nq rows of one key/value head in
+    one wave (exactly 32 rows: 8 x 4; one past: 8 x 5 takes the tile kernel),
+    with key splits and bottom-right causal positions."""
+    _say(f"[kv decode] H={H} Hkv={Hkv} Nq={nq} Nk={nk} d={d} causal={causal}")
+    q, k, v = _inputs(2, H, Hkv, nq, nk, d, seed=3000 + nq + nk)
+    o, lse, nb = _run(q, k, v, causal, 1 / math.sqrt(d))
+    _say(f"   workspace {nb} bytes")
+    _check(q, k, v, causal, 1 / math.sqrt(d), o, lse)
