@@ -68,8 +68,11 @@ template <int D, int BN>
 struct FwdCfg {
   static constexpr int CPR = D / 8;                 // 16-byte chunks per tile row
   static constexpr int TILE_BYTES = BN * D * 2;     // one K or V tile (bf16)
-  static constexpr int SMEM_BYTES = 4 * TILE_BYTES; // K[2], V[2]
-  static constexpr int OFF_V = 2 * TILE_BYTES;
+  static constexpr int OFF_V = 2 * TILE_BYTES;      // K[2] at 0, V[2] at OFF_V
+  static constexpr int OFF_Q = 4 * TILE_BYTES;      // the workgroup's query tile
+  static constexpr int Q_BYTES = kBM * D * 2;
+  static constexpr int SMEM_BYTES = OFF_Q + Q_BYTES;
+  static constexpr int QDMA = Q_BYTES / (1024 * kWaves);     // query-tile DMAs per wave
   static constexpr int NSB = BN / 32;               // 32-key sub-blocks per tile
   static constexpr int NQC = D / 16;                // 16-feature chunks (QK^T k-steps)
   static constexpr int NDB = D / 32;                // 32-feature output blocks
@@ -77,6 +80,7 @@ struct FwdCfg {
   static constexpr int DMA_STRIDE = 16 * 64 * kWaves;          // bytes between them
   static constexpr int ROW_BYTES = CPR * 16;
   static_assert(DMA * DMA_STRIDE == TILE_BYTES, "tile split");
+  static_assert(Q_BYTES == 4 * TILE_BYTES, "the output tile fits the K/V stages");
 };
 
 // Per-lane byte offset (inside one (batch, head) slice, relative to row k0) of
@@ -93,6 +97,16 @@ __device__ __forceinline__ unsigned dma_src_off(int i, int w, int lane, int k0, 
   const int chunk = (slot % C::CPR) ^ swz<C::CPR, KIND>(row);
   const int src_row = full ? row : min(k0 + row, N - 1) - k0;
   return (unsigned)((src_row * D + chunk * 8) * 2);
+}
+
+// One 16-byte global -> LDS DMA per lane through a buffer resource: lane i
+// reads rsrc.base + voff (0 when voff is past the resource's byte count) and
+// writes LDS lds + 16 i.  Inline assembly for the reason given at dma16.
+__device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t rsrc, unsigned voff, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "s"(lds)
+               : "memory", "m0");
 }
 
 // Workgroup barrier that orders the compiler's memory operations but adds no
@@ -204,18 +218,31 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(const FwdArgs a) {
   using tr_t = std::integral_constant<int, SWZ_TR>;
   if (nkt > 0 && grp == 1) issue(0, 0u, Kb, koffA, koffB, rows_t{});
 
-  // Q^T as the B operand: lane holds Q[qrow][16c + 8h .. 16c + 8h + 7].
-  bf16x8 qf[C::NQC];
+  // The query tile (kBM rows) goes HBM -> LDS by DMA in whole 1 KiB rows
+  // (row swizzle, as K) and from there into registers: per-lane 16-byte
+  // loads straight from HBM would touch 32 rows per instruction.  Wave w
+  // fills slots w, w + 8, ..; DMA i + 1 is DMA i shifted by 8 KiB on both
+  // sides, which keeps the swizzle (a multiple of 16 rows).  Rows past Nq
+  // fall outside the buffer resource and read 0.
   {
-    const uint32_t flip = a.negq ? 0x80008000u : 0u;
+    const int slot = w * 64 + lane;
+    const int row = slot / C::CPR;
+    const int chunk = (slot % C::CPR) ^ swz<C::CPR, SWZ_ROWS>(row);
+    const unsigned qoff = (unsigned)((row * D + chunk * 8) * 2);
+    const long long qbytes = (long long)max(0, Nq - q0) * (D * 2);
 #pragma unroll
-    for (int cc = 0; cc < C::NQC; ++cc) {
-      u32x4 raw = {0u, 0u, 0u, 0u};
-      if (qrow < Nq) raw = *reinterpret_cast<const u32x4*>(Qh + (size_t)qrow * D + 16 * cc + 8 * h);
-      raw ^= flip;
-      qf[cc] = __builtin_bit_cast(bf16x8, raw);
+    for (int i = 0; i < C::QDMA; ++i) {
+      const long long b0 = (long long)i * 1024 * kWaves;
+      const long long nrec = qbytes - b0 > 0 ? qbytes - b0 : 0;
+      const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(reinterpret_cast<const char*>(Qh + (size_t)q0 * D) + b0), (short)0, (int)nrec,
+          0x00020000);
+      dma16_buf(rsrc, qoff, ldsb + C::OFF_Q + (unsigned)b0 + w * 1024);
     }
   }
+  // this wave's 32 query rows inside the workgroup's tile
+  const int wblk = 2 * (w & 3) + grp;
+  bf16x8 qf[C::NQC];   // Q^T B operands, read from the query tile below
 
   // Per-lane LDS operand addresses inside a stage, one register per tensor.
   // K (A operand of S^T): row 32sb + n, features 16cc + 8h..  With the row
@@ -432,6 +459,18 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(const FwdArgs a) {
   };
   wait_vmem();
   phase_barrier();
+  // Q^T as the B operand: lane holds Q[qrow][16c + 8h .. 16c + 8h + 7], at
+  // row n of the wave's block in the query tile, chunk (2c + h) ^ (n % 16).
+  {
+    const uint32_t flip = a.negq ? 0x80008000u : 0u;
+    const char* qs = smem_raw + C::OFF_Q + wblk * 32 * C::ROW_BYTES;
+#pragma unroll
+    for (int cc = 0; cc < C::NQC; ++cc) {
+      u32x4 raw = *reinterpret_cast<const u32x4*>(qs + kaddr(cc));
+      raw ^= flip;
+      qf[cc] = __builtin_bit_cast(bf16x8, raw);
+    }
+  }
   if (nkt > 0) {
     if (grp == 0)
       run(std::integral_constant<int, 0>{});
@@ -445,20 +484,31 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(const FwdArgs a) {
   const float lt = lsum + wave_xor32(lsum);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   const float lse = lt > 0.f ? (m + __log2f(lt)) * kLn2 : kNegInf;
-  if (qrow < Nq) {
-    if (a.nsplit == 1) {
-      uint16_t* orow = a.O + base + (size_t)qrow * D;
+  if (a.nsplit == 1) {
+    // O goes through LDS (the K/V stages: every wave is past its last matrix
+    // phase) so the stores are whole rows: the wave writes its 32 x D block
+    // (row swizzle), then stores 16-byte chunks, 4 rows per instruction.
+    char* ost = smem_raw + wblk * 32 * C::ROW_BYTES;
 #pragma unroll
-      for (int db = 0; db < C::NDB; ++db)
+    for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int d0 = 32 * db + 8 * g + 4 * h;
-          u32x2 out = {pack_bf16x2(acc[db][4 * g + 0] * inv, acc[db][4 * g + 1] * inv),
-                       pack_bf16x2(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv)};
-          *reinterpret_cast<u32x2*>(orow + d0) = out;
-        }
-      if (h == 0) a.LSE[(size_t)bh * Nq + qrow] = lse;
-    } else {
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * db + 8 * g + 4 * h;
+        u32x2 out = {pack_bf16x2(acc[db][4 * g + 0] * inv, acc[db][4 * g + 1] * inv),
+                     pack_bf16x2(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv)};
+        *reinterpret_cast<u32x2*>(ost + tile_off<C::CPR, SWZ_ROWS>(n, d0)) = out;
+      }
+    constexpr int PER = 64 / C::CPR;   // rows per store instruction
+#pragma unroll
+    for (int it = 0; it < 32 / PER; ++it) {
+      const int r = it * PER + lane / C::CPR, ch = lane % C::CPR;
+      const u32x4 v16 = *reinterpret_cast<const u32x4*>(ost + tile_off<C::CPR, SWZ_ROWS>(r, 8 * ch));
+      if (wq0 + r < Nq)
+        *reinterpret_cast<u32x4*>(a.O + base + (size_t)(wq0 + r) * D + 8 * ch) = v16;
+    }
+    if (h == 0 && qrow < Nq) a.LSE[(size_t)bh * Nq + qrow] = lse;
+  } else if (qrow < Nq) {
+    {
       const size_t prow = ((size_t)sp * BH + bh) * Nq + qrow;
       float* orow = a.Opart + prow * D;
 #pragma unroll
