@@ -136,7 +136,14 @@ struct BwdCfg {
   static constexpr int OFF_K = 0;
   static constexpr int OFF_ST = DQA ? KTILE : 0;          // two stages
   static constexpr int OFF_DS = OFF_ST + 2 * STAGE;       // two dS buffers
-  static constexpr int SMEM = OFF_DS + (DQA ? 2 * DSTILE : 0);
+  static constexpr int SMEM0 = OFF_DS + (DQA ? 2 * DSTILE : 0);
+  // The K and V tiles go HBM -> LDS by DMA in whole rows and from there into
+  // the operand registers, at OFF_KV (the dS buffers, idle until the first
+  // dS write, or past them); head dimension 256 has no room and loads its
+  // operands per lane.
+  static constexpr int OFF_KV = OFF_DS;
+  static constexpr bool KV_LDS = OFF_KV + 2 * KTILE <= 160 * 1024;
+  static constexpr int SMEM = KV_LDS && OFF_KV + 2 * KTILE > SMEM0 ? OFF_KV + 2 * KTILE : SMEM0;
   static constexpr int QDMA = QTILE / 16 / THREADS;       // DMAs per thread per tile
   static constexpr int KDMA = KTILE / 16 / THREADS;
   // dQ = dS K in 32x32 blocks of the [kBQ, D] tile, each over all the tile's
@@ -246,15 +253,50 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_main_kernel(
 
   // K and V as B operands (lane = key, 8 consecutive features per chunk)
   bf16x8 kf[C::NDC], vf[C::NDC];
+  if constexpr (C::KV_LDS) {
+    // whole-row DMA (row swizzle; rows past Nk fall outside the buffer
+    // resource and read 0), then 16-byte LDS reads: per-lane loads straight
+    // from HBM would touch 32 rows per instruction.  Wave w fills slots
+    // w, w + WAVES, ..; DMA j + 1 is DMA j shifted by WAVES KiB on both sides,
+    // a multiple of the swizzle's 16-row period.
+    static_assert((C::WAVES * 1024 / C::RBD) % 16 == 0, "swizzle period");
+    const int slot = w * 64 + lane;
+    const int row = slot / C::CPRD;
+    const unsigned off =
+        (unsigned)((row * D + ((slot % C::CPRD) ^ swz<C::CPRD, SWZ_ROWS>(row)) * 8) * 2);
+    const long long kbytes = (long long)max(0, Nk - k0) * (D * 2);
 #pragma unroll
-  for (int cc = 0; cc < C::NDC; ++cc) {
-    u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-    if (key < Nk) {
-      a = *reinterpret_cast<const u32x4*>(Kb + ((size_t)key * D + 16 * cc + 8 * h) * 2);
-      b = *reinterpret_cast<const u32x4*>(Vb + ((size_t)key * D + 16 * cc + 8 * h) * 2);
+    for (int j = 0; j < C::KDMA; ++j) {
+      const long long b0 = (long long)j * C::WAVES * 1024;
+      const long long nrec = kbytes - b0 > 0 ? kbytes - b0 : 0;
+      const unsigned dst = lds0 + C::OFF_KV + (unsigned)b0 + w * 1024;
+      dma16_buf(__builtin_amdgcn_make_buffer_rsrc((void*)(Kb + (size_t)k0 * D * 2 + b0), (short)0,
+                                                  (int)nrec, 0x00020000),
+                off, dst);
+      dma16_buf(__builtin_amdgcn_make_buffer_rsrc((void*)(Vb + (size_t)k0 * D * 2 + b0), (short)0,
+                                                  (int)nrec, 0x00020000),
+                off, dst + C::KTILE);
     }
-    kf[cc] = __builtin_bit_cast(bf16x8, a);
-    vf[cc] = __builtin_bit_cast(bf16x8, b);
+    wait_vmem();
+    __syncthreads();
+    const char* kvs = smem + C::OFF_KV + 32 * w * C::RBD;
+#pragma unroll
+    for (int cc = 0; cc < C::NDC; ++cc) {
+      const int o = tile_off<C::CPRD, SWZ_ROWS>(n, 16 * cc + 8 * h);
+      kf[cc] = *reinterpret_cast<const bf16x8*>(kvs + o);
+      vf[cc] = *reinterpret_cast<const bf16x8*>(kvs + C::KTILE + o);
+    }
+  } else {
+#pragma unroll
+    for (int cc = 0; cc < C::NDC; ++cc) {
+      u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+      if (key < Nk) {
+        a = *reinterpret_cast<const u32x4*>(Kb + ((size_t)key * D + 16 * cc + 8 * h) * 2);
+        b = *reinterpret_cast<const u32x4*>(Vb + ((size_t)key * D + 16 * cc + 8 * h) * 2);
+      }
+      kf[cc] = __builtin_bit_cast(bf16x8, a);
+      vf[cc] = __builtin_bit_cast(bf16x8, b);
+    }
   }
 
   // per-lane LDS offsets
@@ -456,22 +498,39 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_main_kernel(
     if (ntot > 0) dq_step(ntot - 1);
   }
 
-  // epilogue: dK = scale * dK^T acc, dV = dV^T acc (lane = key, registers = features)
-  if (key < Nk) {
-    uint16_t* dkrow = dK + kvbase + (size_t)key * D;
-    uint16_t* dvrow = dV + kvbase + (size_t)key * D;
+  // epilogue: dK = scale * dK^T acc, dV = dV^T acc (lane = key, registers =
+  // features), through LDS so the stores are whole rows: every wave writes
+  // its 32 x D blocks (row swizzle), then stores 16-byte chunks.
+  // every wave is past its last LDS read (the dQ atomics may still fly)
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  {
+    char* ks = smem + 32 * w * C::RBD;
+    char* vs = ks + C::KTILE;
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int d0 = 32 * db + 8 * g + 4 * h;
-        *reinterpret_cast<u32x2*>(dkrow + d0) =
+        const int o = tile_off<C::CPRD, SWZ_ROWS>(n, 32 * db + 8 * g + 4 * h);
+        *reinterpret_cast<u32x2*>(ks + o) =
             u32x2{pack_bf16x2(scale * dk[db][4 * g + 0], scale * dk[db][4 * g + 1]),
                   pack_bf16x2(scale * dk[db][4 * g + 2], scale * dk[db][4 * g + 3])};
-        *reinterpret_cast<u32x2*>(dvrow + d0) =
+        *reinterpret_cast<u32x2*>(vs + o) =
             u32x2{pack_bf16x2(dv[db][4 * g + 0], dv[db][4 * g + 1]),
                   pack_bf16x2(dv[db][4 * g + 2], dv[db][4 * g + 3])};
       }
+    constexpr int PER = 64 / C::CPRD;   // rows per store instruction
+#pragma unroll
+    for (int it = 0; it < 32 / PER; ++it) {
+      const int r = it * PER + lane / C::CPRD, ch = lane % C::CPRD;
+      const int o = tile_off<C::CPRD, SWZ_ROWS>(r, 8 * ch);
+      const u32x4 kv16 = *reinterpret_cast<const u32x4*>(ks + o);
+      const u32x4 vv16 = *reinterpret_cast<const u32x4*>(vs + o);
+      if (wk0 + r < Nk) {
+        *reinterpret_cast<u32x4*>(dK + kvbase + (size_t)(wk0 + r) * D + 8 * ch) = kv16;
+        *reinterpret_cast<u32x4*>(dV + kvbase + (size_t)(wk0 + r) * D + 8 * ch) = vv16;
+      }
+    }
   }
 }
 
@@ -547,7 +606,9 @@ struct DqCfg {
   static constexpr int DMA = TILE / (16 * 64 * WAVES);
   static constexpr int OFF_V = 2 * TILE;
   static constexpr int SMEM = 4 * TILE;
+  static constexpr int QTILE = QB * ROW;        // the dQ tile, staged in the K/V stages
   static_assert(DMA * 16 * 64 * WAVES == TILE, "DMA split");
+  static_assert(QTILE <= 4 * TILE, "the dQ tile fits the K/V stages");
 };
 
 template <int D, bool CAUSAL>
@@ -694,17 +755,26 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_direct_kernel(
     }
   }
 
-  if (qrow < Nq) {
-    uint16_t* drow = dQ + qbase + (size_t)qrow * D;
+  // dQ through LDS (the K / V stages) so the stores are whole rows: every
+  // wave writes its 32 x D block (row swizzle), then stores 16-byte chunks
+  wait_vmem();
+  __syncthreads();   // every wave is past its last LDS read
+  char* os = smem + 32 * w * C::ROW;
 #pragma unroll
-    for (int db = 0; db < C::NDB; ++db)
+  for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = 32 * db + 8 * g + 4 * h;
-        u32x2 out = {pack_bf16x2(scale * acc[db][4 * g + 0], scale * acc[db][4 * g + 1]),
-                     pack_bf16x2(scale * acc[db][4 * g + 2], scale * acc[db][4 * g + 3])};
-        *reinterpret_cast<u32x2*>(drow + d0) = out;
-      }
+    for (int g = 0; g < 4; ++g) {
+      const int d0 = 32 * db + 8 * g + 4 * h;
+      *reinterpret_cast<u32x2*>(os + tile_off<C::CPR, SWZ_ROWS>(n, d0)) =
+          u32x2{pack_bf16x2(scale * acc[db][4 * g + 0], scale * acc[db][4 * g + 1]),
+                pack_bf16x2(scale * acc[db][4 * g + 2], scale * acc[db][4 * g + 3])};
+    }
+  constexpr int PER = 64 / C::CPR;   // rows per store instruction
+#pragma unroll
+  for (int it = 0; it < 32 / PER; ++it) {
+    const int r = it * PER + lane / C::CPR, ch = lane % C::CPR;
+    const u32x4 v16 = *reinterpret_cast<const u32x4*>(os + tile_off<C::CPR, SWZ_ROWS>(r, 8 * ch));
+    if (wq0 + r < Nq) *reinterpret_cast<u32x4*>(dQ + qbase + (size_t)(wq0 + r) * D + 8 * ch) = v16;
   }
 }
 

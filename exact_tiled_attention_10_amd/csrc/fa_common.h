@@ -143,6 +143,16 @@ __device__ __forceinline__ void dma16(const void* gbase, unsigned voff, unsigned
                : "memory", "m0");
 }
 
+// One 16-byte global -> LDS DMA per lane through a buffer resource: lane i
+// reads rsrc.base + voff (0 when voff is past the resource's byte count) and
+// writes LDS lds + 16 i.  Inline assembly for the reason given at dma16.
+__device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t rsrc, unsigned voff, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "s"(lds)
+               : "memory", "m0");
+}
+
 // Transposing LDS read (ds_read_b64_tr_b16).  Within each 16-lane group, the
 // lane 4j + c reads 4 bf16 of "row" j; output lane 4c + e receives element e
 // of rows j = 0..3.  So if lane 4j + c points at row (r0 + j), columns

@@ -99,16 +99,6 @@ __device__ __forceinline__ unsigned dma_src_off(int i, int w, int lane, int k0, 
   return (unsigned)((src_row * D + chunk * 8) * 2);
 }
 
-// One 16-byte global -> LDS DMA per lane through a buffer resource: lane i
-// reads rsrc.base + voff (0 when voff is past the resource's byte count) and
-// writes LDS lds + 16 i.  Inline assembly for the reason given at dma16.
-__device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t rsrc, unsigned voff, unsigned lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-               :
-               : "v"(voff), "s"(rsrc), "s"(lds)
-               : "memory", "m0");
-}
-
 // Workgroup barrier that orders the compiler's memory operations but adds no
 // wait for outstanding memory transfers (prefetch DMAs stay in flight).
 __device__ __forceinline__ void phase_barrier() { asm volatile("s_barrier" ::: "memory"); }
