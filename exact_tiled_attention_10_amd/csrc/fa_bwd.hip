@@ -611,8 +611,11 @@ struct DqCfg {
   static_assert(QTILE <= 4 * TILE, "the dQ tile fits the K/V stages");
 };
 
+// d = 128: two waves per SIMD (two workgroups per CU), so one workgroup's
+// vector work overlaps the other's matrix work (297 -> 257 us at
+// [1, 32, 4096, 128] causal); d = 256 needs more than 256 registers.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void bwd_dq_direct_kernel(
+__global__ __launch_bounds__(256, D == 128 ? 2 : 1) void bwd_dq_direct_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ L2, const float* __restrict__ Dv, uint16_t* __restrict__ dQ,
