@@ -343,7 +343,7 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(const FwdArgs a) {
   // of the unrounded p (the saved lse needs the unrounded sum: rounding each p
   // to bf16 first moves ln(l) by up to 2^-9 on short rows).
   auto probs = [&]() __attribute__((always_inline)) {
-    float part[4] = {0.f, 0.f, 0.f, 0.f};   // four partial sums: no serial add chain
+    float part[4];   // four partial sums: no serial add chain
 #pragma unroll
     for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
@@ -351,7 +351,11 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(const FwdArgs a) {
         const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][r], c, -m));
         const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][r + 1], c, -m));
         pk[sb][r >> 1] = pack_bf16x2(p0, p1);
-        part[(r >> 1) & 3] += p0 + p1;
+        // the first pair of each partial sum starts it (no add of 0)
+        if (sb == 0 && r < 8)
+          part[(r >> 1) & 3] = p0 + p1;
+        else
+          part[(r >> 1) & 3] += p0 + p1;
       }
     return (part[0] + part[1]) + (part[2] + part[3]);
   };
