@@ -202,7 +202,8 @@ def run_extra_sweep():
     out["llama8b_gqa32x8_n4096_causal_fwd"] = dict(
         ms=round(ms, 4), tflops=round(tf, 1), pct_of_bf16_peak=round(100 * tf / PEAK_BF16_TFLOPS, 1))
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = torch.empty(fa.fa_bwd_workspace_size(B, H, N, d), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(fa.fa_bwd_kv_workspace_size(B, H, Hkv, N, N, d), dtype=torch.uint8,
+                     device="cuda")
     ms = _time_launches(lambda: fa.fa_bwd_gqa(q, k, v, o, do, lse, dq, dk, dv, ws, True, sc))
     tf = 2.5 * fwd_flops(B, H, N, d, True) / (ms * 1e-3) / 1e12
     out["llama8b_gqa32x8_n4096_causal_bwd"] = dict(

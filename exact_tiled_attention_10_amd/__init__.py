@@ -8,7 +8,8 @@ fallback: if the library is missing, every call raises.
 
 Low-level entry points carry the C names (``fa_fwd``, ``fa_fwd_gqa``,
 ``fa_fwd_kv``, ``fa_fwd_kv_workspace_size``, ``fa_fwd_f32``, ``fa_bwd``,
-``fa_bwd_gqa``, ``fa_bwd_kv``, ``fa_bwd_workspace_size``, ``fa_status_string``) and take
+``fa_bwd_gqa``, ``fa_bwd_kv``, ``fa_bwd_workspace_size``, ``fa_bwd_kv_workspace_size``,
+``fa_status_string``) and take
 preallocated tensors;
 ``forward``/``backward``/``attention`` allocate, and take key / value tensors
 with fewer heads than the queries (grouped-query attention) when the dtype is
@@ -28,7 +29,8 @@ __all__ = [
     "FAError", "library_path", "load_library",
     "fa_fwd", "fa_fwd_gqa", "fa_fwd_kv", "fa_fwd_kv_workspace_size", "fa_fwd_fp8",
     "fa_fwd_f32",
-    "fa_bwd", "fa_bwd_gqa", "fa_bwd_kv", "fa_bwd_workspace_size", "fa_status_string",
+    "fa_bwd", "fa_bwd_gqa", "fa_bwd_kv", "fa_bwd_workspace_size", "fa_bwd_kv_workspace_size",
+    "fa_status_string",
     "fa_bwd_preprocess", "fa_bwd_main", "fa_bwd_finalize",
     "forward", "backward", "attention",
     "FA_OK", "FA_ERR_NULL", "FA_ERR_SHAPE", "FA_ERR_HEADDIM", "FA_ERR_ALIGN",
@@ -89,6 +91,8 @@ def load_library():
     lib.fa_fwd_f32.restype = i
     lib.fa_bwd_workspace_size.argtypes = [i, i, i, i]
     lib.fa_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.fa_bwd_kv_workspace_size.argtypes = [i, i, i, i, i, i]
+    lib.fa_bwd_kv_workspace_size.restype = ctypes.c_size_t
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
                            i, i, i, i, i, f, vp]
     lib.fa_bwd.restype = i
@@ -266,6 +270,10 @@ def fa_bwd_workspace_size(B: int, H: int, N: int, d: int) -> int:
     return int(load_library().fa_bwd_workspace_size(B, H, N, d))
 
 
+def fa_bwd_kv_workspace_size(B: int, H: int, Hkv: int, Nq: int, Nk: int, d: int) -> int:
+    return int(load_library().fa_bwd_kv_workspace_size(B, H, Hkv, Nq, Nk, d))
+
+
 def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, causal: bool, scale: float,
            stream=None) -> None:
     """bf16 backward into preallocated ``dq``, ``dk``, ``dv``; ``workspace`` is a
@@ -415,8 +423,8 @@ def backward(q, k, v, o, lse, do, causal: bool = False, scale: Optional[float] =
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
-    ws = torch.empty(max(1, fa_bwd_workspace_size(B, H, N, d)), dtype=torch.uint8,
-                     device=q.device)
+    ws = torch.empty(max(1, fa_bwd_kv_workspace_size(B, H, k.shape[1], N, k.shape[2], d)),
+                     dtype=torch.uint8, device=q.device)
     if k.dim() == 4 and k.shape[2] != N:
         fa_bwd_kv(q, k, v, o, do, lse, dq, dk, dv, ws, causal, s, stream)
     elif k.dim() == 4 and k.shape[1] != H:

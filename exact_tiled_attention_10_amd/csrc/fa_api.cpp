@@ -107,8 +107,17 @@ int bwd_bf16(const void* q, const void* k, const void* v, const void* o, const v
       misaligned(lse) || misaligned(dq) || misaligned(dk) || misaligned(dv) ||
       misaligned(workspace))
     return FA_ERR_ALIGN;
-  const size_t need = fa::bwd_workspace_bytes(B * H, Nq, d);
+  size_t need = fa::bwd_workspace_bytes(B * H, Nq, d);
   if (workspace_bytes < need) return FA_ERR_WORKSPACE;
+  // a larger workspace lets grouped-query heads split over more workgroups
+  int hsplit = has_q && has_k ? fa::bwd_head_split(B * Hkv, H / Hkv, Nq, Nk, d, causal != 0) : 1;
+  if (hsplit > 1) {
+    const size_t full = need + fa::bwd_split_bytes(B * Hkv, Nk, d, hsplit);
+    if (workspace_bytes >= full)
+      need = full;
+    else
+      hsplit = 1;
+  }
   const size_t tb = te * 2, kvb = kve * 2;
   const Range in[6] = {range_of(q, tb),    range_of(k, kvb),   range_of(v, kvb),
                        range_of(o, tb),    range_of(dout, tb), range_of(lse, re * 4)};
@@ -120,7 +129,7 @@ int bwd_bf16(const void* q, const void* k, const void* v, const void* o, const v
   if (has_q) e = fa::launch_bwd_pre(o, dout, lse, workspace, BH, Nq, d, stream);
   if (e == hipSuccess && has_k) {
     if (has_q)
-      e = fa::launch_bwd_main(q, k, v, dout, dk, dv, workspace, BH, Nq, Nk, d, H / Hkv,
+      e = fa::launch_bwd_main(q, k, v, dout, dk, dv, workspace, BH, Nq, Nk, d, H / Hkv, hsplit,
                               causal != 0, scale, stream);
     else   // no queries: every key's gradient is 0
       e = fa::launch_zero_bf16(dk, dv, kve, stream);
@@ -233,6 +242,14 @@ size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
   return fa::bwd_workspace_bytes(B * H, N, d);
 }
 
+size_t fa_bwd_kv_workspace_size(int B, int H, int Hkv, int Nq, int Nk, int d) {
+  size_t te = 0, re = 0;
+  if (check_common(B, H, Nq, d, 1.0f, &te, &re, true) != FA_OK) return 0;
+  if (Nk < 0 || Nk > FA_MAX_N || check_heads(H, Hkv) != FA_OK) return 0;
+  if (H == 0) return fa::bwd_workspace_bytes(0, Nq, d);
+  return fa::bwd_kv_workspace_bytes(B * H, H / Hkv, Nq, Nk, d);
+}
+
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
            const float* lse, void* dq, void* dk, void* dv, void* workspace,
            size_t workspace_bytes, int B, int H, int N, int d, int causal, float scale,
@@ -292,7 +309,7 @@ int fa_bwd_main(const void* q, const void* k, const void* v, const void* dout, v
   const Range in[4] = {range_of(q, tb), range_of(k, tb), range_of(v, tb), range_of(dout, tb)};
   const Range out[3] = {range_of(dk, tb), range_of(dv, tb), range_of(workspace, need)};
   if (any_alias(in, 4, out, 3)) return FA_ERR_ALIAS;
-  return from_hip(fa::launch_bwd_main(q, k, v, dout, dk, dv, workspace, B * H, N, N, d, 1,
+  return from_hip(fa::launch_bwd_main(q, k, v, dout, dk, dv, workspace, B * H, N, N, d, 1, 1,
                                       causal != 0, scale, stream));
 }
 

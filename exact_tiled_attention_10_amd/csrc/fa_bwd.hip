@@ -40,6 +40,7 @@
 // Every transposed A/B operand (dO^T, Q^T, K^T, dS with queries across lanes)
 // is read from a row-major LDS tile with ds_read_b64_tr_b16; no tile is ever
 // transposed in registers.
+#include <algorithm>
 #include <type_traits>
 
 #include "fa_common.h"
@@ -164,9 +165,8 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_main_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ L2, const float* __restrict__ Dv, float* __restrict__ dQacc,
-    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int BHkv, int Nq, int Nk, int koff,
-    int Npad, int nkt,
-    int group, float scale, float c2) {
+    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, float* __restrict__ part, int BHkv,
+    int Nq, int Nk, int koff, int Npad, int nkt, int group, int hsplit, float scale, float c2) {
   using C = BwdCfg<D>;
   extern __shared__ __attribute__((aligned(1024))) char smem[];
 
@@ -177,16 +177,22 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_main_kernel(
   const int h = lane >> 5;
 
   // The workgroup owns a key tile of one key / value head; with grouped-query
-  // attention the `group` query heads sharing it are processed one after the
-  // other, so dK and dV sum over them in registers (group = 1: plain
-  // multi-head attention).
-  int kvh, kt;
-  map_tile(blockIdx.x, BHkv, nkt, false, &kvh, &kt);
+  // attention the query heads sharing it are processed one after the other,
+  // so dK and dV sum over them in registers (group = 1: plain multi-head
+  // attention).  With hsplit > 1 the group's heads are dealt to hsplit
+  // workgroups (group / hsplit each), which write float32 partial sums for a
+  // reduction kernel instead of dK and dV.
+  int unit, kt;
+  map_tile(blockIdx.x, BHkv * hsplit, nkt, false, &unit, &kt);
+  const int kvh = unit / hsplit;
+  const int hpart = unit - kvh * hsplit;
+  const int gsize = group / hsplit;
   const size_t kvbase = (size_t)kvh * (size_t)Nk * D;
   const char* Kb = reinterpret_cast<const char*>(K + kvbase);
   const char* Vb = reinterpret_cast<const char*>(V + kvbase);
-  // per query head g of the group: its Q, dO, L2, D and dQ accumulator slice
-  auto qhead = [&](int g) { return (size_t)kvh * group + g; };
+  // per query head g of this workgroup's share: its Q, dO, L2, D and dQ
+  // accumulator slice
+  auto qhead = [&](int g) { return (size_t)kvh * group + hpart * gsize + g; };
   auto Qb_of = [&](int g) {
     return reinterpret_cast<const char*>(Q + qhead(g) * (size_t)Nq * D);
   };
@@ -220,7 +226,7 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_main_kernel(
   const int nqb = (Nq + kBQ - 1) / kBQ;
   const int qb0 = CAUSAL ? max(0, k0 - koff) / kBQ : 0;
   const int nit = max(0, nqb - qb0);   // query blocks per query head
-  const int ntot = group * nit;    // iterations: (query head, query block)
+  const int ntot = gsize * nit;    // iterations: (query head, query block)
 
   // DMA of iteration t: query block qb0 + t % nit of query head t / nit (Q, dO
   // rows clamped to N-1; L2 and D padded)
@@ -498,6 +504,27 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_main_kernel(
     if (ntot > 0) dq_step(ntot - 1);
   }
 
+  if (hsplit > 1) {
+    // float32 partials [hsplit][BHkv][Nk][D] (dK, then dV): lane = key,
+    // registers 4g..4g+3 = features 32 db + 8 g + 4 h .. + 3
+    float* pk = part + ((size_t)hpart * BHkv + kvh) * (size_t)Nk * D;
+    float* pv = pk + (size_t)hsplit * BHkv * (size_t)Nk * D;
+    if (key < Nk) {
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const size_t o = (size_t)key * D + 32 * db + 8 * g + 4 * h;
+          *reinterpret_cast<f32x4*>(pk + o) =
+              f32x4{scale * dk[db][4 * g + 0], scale * dk[db][4 * g + 1],
+                    scale * dk[db][4 * g + 2], scale * dk[db][4 * g + 3]};
+          *reinterpret_cast<f32x4*>(pv + o) =
+              f32x4{dv[db][4 * g + 0], dv[db][4 * g + 1], dv[db][4 * g + 2], dv[db][4 * g + 3]};
+        }
+    }
+    return;
+  }
+
   // epilogue: dK = scale * dK^T acc, dV = dV^T acc (lane = key, registers =
   // features), through LDS so the stores are whole rows: every wave writes
   // its 32 x D blocks (row swizzle), then stores 16-byte chunks.
@@ -549,8 +576,8 @@ inline WsLayout ws_layout(void* ws, int BH, int N) {
 
 template <int D, bool CAUSAL>
 hipError_t launch_main(const void* q, const void* k, const void* v, const void* dout,
-                       const WsLayout& w, void* dk, void* dv, int BH, int Nq, int Nk, int group,
-                       float scale, hipStream_t stream) {
+                       const WsLayout& w, void* dk, void* dv, float* part, int BH, int Nq, int Nk,
+                       int group, int hsplit, float scale, hipStream_t stream) {
   using C = BwdCfg<D>;
   const int nkt = (Nk + C::KEYS - 1) / C::KEYS;
   const int BHkv = BH / group;
@@ -558,11 +585,37 @@ hipError_t launch_main(const void* q, const void* k, const void* v, const void* 
   hipError_t e =
       hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::SMEM);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(BHkv * nkt), dim3(C::THREADS), C::SMEM, stream,
+  hipLaunchKernelGGL(kern, dim3(BHkv * hsplit * nkt), dim3(C::THREADS), C::SMEM, stream,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
-                     (const uint16_t*)dout, w.l2, w.dv, w.dq, (uint16_t*)dk, (uint16_t*)dv, BHkv, Nq,
-                     Nk, Nk - Nq, pad_rows(Nq), nkt, group, scale, scale * kLog2e);
+                     (const uint16_t*)dout, w.l2, w.dv, w.dq, (uint16_t*)dk, (uint16_t*)dv, part,
+                     BHkv, Nq, Nk, Nk - Nq, pad_rows(Nq), nkt, group, hsplit, scale,
+                     scale * kLog2e);
   return hipGetLastError();
+}
+
+// dK, dV = bf16(sum of the hsplit float32 partials), summed in partial order
+// (deterministic); one thread per 8 elements of each tensor.
+__global__ __launch_bounds__(256) void bwd_kv_reduce_kernel(const float* __restrict__ part,
+                                                            uint16_t* __restrict__ dK,
+                                                            uint16_t* __restrict__ dV, size_t n8,
+                                                            int hsplit) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const size_t slice = n8 * 8;   // elements per partial
+  const float* pk = part + 8 * i;
+  const float* pv = pk + (size_t)hsplit * slice;
+  f32x4 k0 = *reinterpret_cast<const f32x4*>(pk), k1 = *reinterpret_cast<const f32x4*>(pk + 4);
+  f32x4 v0 = *reinterpret_cast<const f32x4*>(pv), v1 = *reinterpret_cast<const f32x4*>(pv + 4);
+  for (int s = 1; s < hsplit; ++s) {
+    k0 += *reinterpret_cast<const f32x4*>(pk + s * slice);
+    k1 += *reinterpret_cast<const f32x4*>(pk + s * slice + 4);
+    v0 += *reinterpret_cast<const f32x4*>(pv + s * slice);
+    v1 += *reinterpret_cast<const f32x4*>(pv + s * slice + 4);
+  }
+  *reinterpret_cast<u32x4*>(dK + 8 * i) = u32x4{pack_bf16x2(k0[0], k0[1]), pack_bf16x2(k0[2], k0[3]),
+                                                pack_bf16x2(k1[0], k1[1]), pack_bf16x2(k1[2], k1[3])};
+  *reinterpret_cast<u32x4*>(dV + 8 * i) = u32x4{pack_bf16x2(v0[0], v0[1]), pack_bf16x2(v0[2], v0[3]),
+                                                pack_bf16x2(v1[0], v1[1]), pack_bf16x2(v1[2], v1[3])};
 }
 
 // dK = dV = 0 when there are no queries (nothing to differentiate through).
@@ -810,22 +863,74 @@ hipError_t launch_bwd_pre(const void* o, const void* dout, const float* lse, voi
   return hipGetLastError();
 }
 
+int bwd_head_split(int BHkv, int group, int Nq, int Nk, int d, bool causal) {
+  if (group < 2 || BHkv <= 0 || Nq <= 0 || Nk <= 0) return 1;
+  // Workgroups run one per compute unit, so the key-tile kernel takes about
+  // max(heaviest workgroup, total work / CUs).  Under causal masking the
+  // first key tiles see every query block and the last almost none: with
+  // few key / value heads the heaviest workgroup (all `group` heads of key
+  // tile 0) then sets the time.  Take the smallest divisor s of the group
+  // whose share (group / s heads) is no heavier than the average per CU.
+  constexpr int kCUs = 256;
+  const int keys = d == 64 ? BwdCfg<64>::KEYS : BwdCfg<128>::KEYS;
+  static_assert(BwdCfg<128>::KEYS == BwdCfg<256>::KEYS, "key tile");
+  const int nkt = (Nk + keys - 1) / keys;
+  const int nqb = (Nq + kBQ - 1) / kBQ;
+  long long sum = 0;
+  int heaviest = 0;
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int qb0 = causal ? std::max(0, kt * keys - (Nk - Nq)) / kBQ : 0;
+    const int nit = std::max(0, nqb - qb0);
+    sum += nit;
+    heaviest = std::max(heaviest, nit);
+  }
+  const long long per_cu = ((long long)BHkv * group * sum + kCUs - 1) / kCUs;
+  for (int s = 1; s < group; ++s)
+    if (group % s == 0 && (long long)(group / s) * heaviest <= per_cu) return s;
+  return group;
+}
+
+size_t bwd_split_bytes(int BHkv, int Nk, int d, int hsplit) {
+  if (hsplit <= 1) return 0;
+  return round256(2 * (size_t)hsplit * BHkv * (size_t)Nk * d * 4);
+}
+
+size_t bwd_kv_workspace_bytes(int BH, int group, int Nq, int Nk, int d) {
+  const int BHkv = BH / group;
+  const int s = std::max(bwd_head_split(BHkv, group, Nq, Nk, d, true),
+                         bwd_head_split(BHkv, group, Nq, Nk, d, false));
+  return bwd_workspace_bytes(BH, Nq, d) + bwd_split_bytes(BHkv, Nk, d, s);
+}
+
 hipError_t launch_bwd_main(const void* q, const void* k, const void* v, const void* dout,
                            void* dk, void* dv, void* ws, int BH, int Nq, int Nk, int d, int group,
-                           bool causal, float scale, hipStream_t stream) {
+                           int hsplit, bool causal, float scale, hipStream_t stream) {
   if (Nk <= 0) return hipSuccess;   // no keys: no dK / dV rows, dQ stays 0
   const WsLayout w = ws_layout(ws, BH, Nq);
+  float* part = hsplit > 1 ? reinterpret_cast<float*>(reinterpret_cast<char*>(ws) +
+                                                      bwd_workspace_bytes(BH, Nq, d))
+                           : nullptr;
+  hipError_t e;
   if (d == 256)
-    return causal
-               ? launch_main<256, true>(q, k, v, dout, w, dk, dv, BH, Nq, Nk, group, scale, stream)
-               : launch_main<256, false>(q, k, v, dout, w, dk, dv, BH, Nq, Nk, group, scale, stream);
-  if (d == 128)
-    return causal
-               ? launch_main<128, true>(q, k, v, dout, w, dk, dv, BH, Nq, Nk, group, scale, stream)
-               : launch_main<128, false>(q, k, v, dout, w, dk, dv, BH, Nq, Nk, group, scale, stream);
-  return causal
-             ? launch_main<64, true>(q, k, v, dout, w, dk, dv, BH, Nq, Nk, group, scale, stream)
-             : launch_main<64, false>(q, k, v, dout, w, dk, dv, BH, Nq, Nk, group, scale, stream);
+    e = causal ? launch_main<256, true>(q, k, v, dout, w, dk, dv, part, BH, Nq, Nk, group, hsplit,
+                                        scale, stream)
+               : launch_main<256, false>(q, k, v, dout, w, dk, dv, part, BH, Nq, Nk, group,
+                                         hsplit, scale, stream);
+  else if (d == 128)
+    e = causal ? launch_main<128, true>(q, k, v, dout, w, dk, dv, part, BH, Nq, Nk, group, hsplit,
+                                        scale, stream)
+               : launch_main<128, false>(q, k, v, dout, w, dk, dv, part, BH, Nq, Nk, group,
+                                         hsplit, scale, stream);
+  else
+    e = causal ? launch_main<64, true>(q, k, v, dout, w, dk, dv, part, BH, Nq, Nk, group, hsplit,
+                                       scale, stream)
+               : launch_main<64, false>(q, k, v, dout, w, dk, dv, part, BH, Nq, Nk, group, hsplit,
+                                        scale, stream);
+  if (e != hipSuccess || hsplit <= 1) return e;
+  const size_t n8 = (size_t)(BH / group) * Nk * d / 8;
+  hipLaunchKernelGGL(bwd_kv_reduce_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0,
+                     stream, part, (uint16_t*)dk, (uint16_t*)dv, n8, hsplit);
+  return hipGetLastError();
 }
 
 hipError_t launch_zero_bf16(void* a, void* b, size_t elems, hipStream_t stream) {

@@ -46,10 +46,17 @@ hipError_t launch_bwd_pre(const void* o, const void* dout, const float* lse, voi
                           int N, int d, hipStream_t stream);
 // BH = batch * query heads; `group` query heads share each key / value head.
 // Nq query rows (the workspace is sized by them) against Nk keys, causal
-// alignment as in launch_fwd_bf16_kv.
+// alignment as in launch_fwd_bf16_kv.  hsplit > 1 (a divisor of group) deals
+// each group's query heads to hsplit workgroups per key tile; their float32
+// dK / dV partials ([2][hsplit][BH / group][Nk][d], bwd_split_bytes) follow
+// the bwd_workspace_bytes part of `ws` and a reduction kernel sums them.
+int bwd_head_split(int BHkv, int group, int Nq, int Nk, int d, bool causal);
+size_t bwd_split_bytes(int BHkv, int Nk, int d, int hsplit);
+// Workspace for the largest split either masking may choose.
+size_t bwd_kv_workspace_bytes(int BH, int group, int Nq, int Nk, int d);
 hipError_t launch_bwd_main(const void* q, const void* k, const void* v, const void* dout,
                            void* dk, void* dv, void* ws, int BH, int Nq, int Nk, int d, int group,
-                           bool causal, float scale, hipStream_t stream);
+                           int hsplit, bool causal, float scale, hipStream_t stream);
 // Two bf16 tensors of `elems` elements each (a multiple of 8) set to 0.
 hipError_t launch_zero_bf16(void* a, void* b, size_t elems, hipStream_t stream);
 // d = 64: dQ = bf16(accumulator); d = 128, 256: the query-stationary dQ

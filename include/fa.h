@@ -193,6 +193,23 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o,
 size_t fa_bwd_workspace_size(int B, int H, int N, int d);
 
 /*
+ * fa_bwd_kv_workspace_size -- bytes of device workspace with which fa_bwd_gqa
+ * and fa_bwd_kv run at full speed: fa_bwd_workspace_size(B, H, Nq, d) plus,
+ * when grouped-query heads are split (below), room for float32 partial dK
+ * and dV sums.  Returns 0 for invalid shapes (as the fa_bwd_kv checks).
+ *
+ * Under causal masking the first key tiles see every query and the last few
+ * almost none, and with few key / value heads the key tiles holding all H / Hkv
+ * query heads' work would set the backward's time.  Given this workspace, the
+ * key-tile kernel deals each group's query heads to several workgroups (a
+ * divisor of H / Hkv, chosen from the shapes) that write float32 partials,
+ * and a reduction kernel sums them in a fixed order (deterministic).  With
+ * only fa_bwd_workspace_size bytes the split is not used; results agree to
+ * bf16 rounding either way.
+ */
+size_t fa_bwd_kv_workspace_size(int B, int H, int Hkv, int Nq, int Nk, int d);
+
+/*
  * fa_bwd -- backward pass, bfloat16 tensors.
  *
  *   q, k, v, o  [B, H, N, d] bfloat16: the forward's inputs and output.
@@ -223,13 +240,14 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
  *
  *   q, o, dout, dq  [B, H, N, d];  k, v, dk, dv  [B, Hkv, N, d];  lse [B, H, N].
  *   workspace       at least fa_bwd_workspace_size(B, H, N, d) bytes (it is
- *                   sized by the query heads).
+ *                   sized by the query heads); fa_bwd_kv_workspace_size(B, H,
+ *                   Hkv, N, N, d) bytes allow the head split described there.
  *
  * The gradient of fa_fwd_gqa: dK and dV of a key / value head sum the
  * contributions of the H / Hkv query heads that share it (the chain rule
  * through the shared head); each workgroup owns a key tile of one key / value
- * head and walks its query heads in turn, so the sum stays in registers.
- * Otherwise exactly fa_bwd.
+ * head and walks its query heads (or its share of them) in turn, so the sum
+ * stays in registers.  Otherwise exactly fa_bwd.
  */
 int fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o,
                const void* dout, const float* lse, void* dq, void* dk, void* dv,
@@ -242,7 +260,9 @@ int fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o,
  *
  *   q, o, dout, dq  [B, H, Nq, d];  k, v, dk, dv  [B, Hkv, Nk, d];
  *   lse [B, H, Nq] as fa_fwd_kv returned it.
- *   workspace       at least fa_bwd_workspace_size(B, H, Nq, d) bytes.
+ *   workspace       at least fa_bwd_workspace_size(B, H, Nq, d) bytes;
+ *                   fa_bwd_kv_workspace_size(B, H, Hkv, Nq, Nk, d) bytes
+ *                   allow the grouped-query head split described there.
  *
  * Gradients of sum(O * dO) as for fa_bwd: query rows with no visible key get
  * dQ = 0; keys no query sees get dK = dV = 0 (with Nq = 0 every key, and

@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol(lib):
     names = _declared_functions()
     assert set(names) == {"fa_fwd", "fa_fwd_gqa", "fa_fwd_kv", "fa_fwd_kv_workspace_size",
                           "fa_fwd_fp8", "fa_fwd_f32", "fa_bwd", "fa_bwd_gqa", "fa_bwd_kv",
-                          "fa_bwd_workspace_size",
+                          "fa_bwd_workspace_size", "fa_bwd_kv_workspace_size",
                           "fa_status_string", "fa_bwd_preprocess", "fa_bwd_main",
                           "fa_bwd_finalize"}
     for nm in names:
@@ -107,6 +107,27 @@ def test_workspace_size(lib):
         need = 2 * B * H * N * 4 + (B * H * N * d * 4 if d == 64 else 0)
         assert ws >= need
         assert ws % 16 == 0
+
+
+def test_kv_workspace_size(lib):
+    """The grouped-query backward's workspace: the plain one, plus float32
+    partial dK and dV ([2][s][B*Hkv][Nk][d]) when the plan splits each group's
+    query heads over s workgroups."""
+    assert lib.fa_bwd_kv_workspace_size(1, 2, 1, 100, 100, 32) == 0
+    assert lib.fa_bwd_kv_workspace_size(1, 6, 4, 100, 100, 64) == 0    # H % Hkv != 0
+    assert lib.fa_bwd_kv_workspace_size(1, 2, 1, 100, -1, 64) == 0
+    # no grouping, or enough key / value heads to fill the chip: no split
+    for (B, H, Hkv, Nq, Nk, d) in ((1, 2, 2, 100, 100, 64), (4, 16, 16, 2048, 2048, 64),
+                                   (4, 32, 8, 4096, 4096, 128)):
+        assert (lib.fa_bwd_kv_workspace_size(B, H, Hkv, Nq, Nk, d)
+                == lib.fa_bwd_workspace_size(B, H, Nq, d))
+    # Llama-3.1-8B heads at batch 1: key tile 0 holds 4 heads x 64 query
+    # blocks, twice the average per compute unit; halves of the group fit
+    base = lib.fa_bwd_workspace_size(1, 32, 4096, 128)
+    assert lib.fa_bwd_kv_workspace_size(1, 32, 8, 4096, 4096, 128) == base + 2 * 2 * 8 * 4096 * 128 * 4
+    # one key / value head, a short sequence: every head on its own
+    base = lib.fa_bwd_workspace_size(1, 8, 256, 64)
+    assert lib.fa_bwd_kv_workspace_size(1, 8, 1, 256, 256, 64) == base + 2 * 8 * 1 * 256 * 64 * 4
 
 
 def _bwd(lib, ws_bytes=None, **kw):

@@ -71,24 +71,36 @@ def test_gqa_forward(H, Hkv, N, causal, d):
     assert eo <= TOL and el <= TOL_LSE
 
 
-@pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("N", [1, 65, 257, 700])
-@pytest.mark.parametrize("H,Hkv", CASES)
-def test_gqa_backward(H, Hkv, N, causal, d):
-    _say(f"[gqa bwd] H={H} Hkv={Hkv} N={N} d={d} causal={causal}")
-    q, k, v, do = make_gqa_inputs(2, H, Hkv, N, d, seed=400 + N + H + Hkv, with_do=True)
-    scale = 1.0 / math.sqrt(d)
-    o, lse = _fwd(q, k, v, causal, scale)
+def _bwd(q, k, v, do, o, lse, causal, scale, split):
+    """fa_bwd_gqa with the plain workspace (no head split) or the one
+    fa_bwd_kv_workspace_size asks for (the split the plan picks)."""
     qd, kd, vd, dod = (t.cuda() for t in (q, k, v, do))
     dq = torch.full_like(qd, float("nan"))
     dk = torch.full_like(kd, float("nan"))
     dv = torch.full_like(vd, float("nan"))
-    B = q.shape[0]
-    ws = torch.full((fa.fa_bwd_workspace_size(B, H, N, d),), 0xFF, dtype=torch.uint8,
-                    device="cuda")
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    nb = (fa.fa_bwd_kv_workspace_size(B, H, Hkv, N, N, d) if split
+          else fa.fa_bwd_workspace_size(B, H, N, d))
+    ws = torch.full((max(1, nb),), 0xFF, dtype=torch.uint8, device="cuda")
     fa.fa_bwd_gqa(qd, kd, vd, o, dod, lse, dq, dk, dv, ws, causal, scale)
     torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+@pytest.mark.parametrize("split", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 65, 257, 700])
+@pytest.mark.parametrize("H,Hkv", CASES)
+def test_gqa_backward(H, Hkv, N, causal, d, split):
+    """Small shapes, where the plan deals every query head of a group to its
+    own workgroup when the workspace allows (split=True)."""
+    _say(f"[gqa bwd] H={H} Hkv={Hkv} N={N} d={d} causal={causal} split={split}")
+    q, k, v, do = make_gqa_inputs(2, H, Hkv, N, d, seed=400 + N + H + Hkv, with_do=True)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = _fwd(q, k, v, causal, scale)
+    dq, dk, dv = _bwd(q, k, v, do, o, lse, causal, scale, split)
     ref = naive_bwd_gqa(_f64(q), _f64(k), _f64(v), _f64(do), scale, causal)
     tol = max(TOL, 2.0 ** -7 * max(float(np.max(np.abs(r))) for r in ref))
     errs = [float(np.max(np.abs(_f64(g) - r))) for g, r in zip((dq, dk, dv), ref)]
@@ -132,3 +144,40 @@ def test_llama8b_gqa_shape_sampled():
         worst_l = max(worst_l, float(np.max(np.abs(lse[0, h, rows] - rl))))
     _say(f"[llama8b gqa 32/8] max|dO|={worst_o:.3e} max|dlse|={worst_l:.3e}")
     assert worst_o <= TOL and worst_l <= TOL_LSE
+
+
+def test_llama8b_gqa_backward():
+    """Backward at Llama-3.1-8B's attention shape with its head sharing (32
+    query heads over 8 key/value heads, N = 4096, d = 128, causal) in the
+    benchmark's launch configuration (head split on): the last key/value head
+    (query heads 28..31) against the oracle, every element; then, over all
+    heads, the split against the unsplit kernel: dQ bit for bit (the same
+    query-tile kernel), dK and dV within one bf16 ulp of each element plus
+    2^-16 of the tensor's largest magnitude (the split only changes the float32
+    summation order, which moves a sum that cancels by a few float32 ulps of
+    its terms)."""
+    B, H, Hkv, N, d = 1, 32, 8, 4096, 128
+    q, k, v, do = make_gqa_inputs(B, H, Hkv, N, d, seed=6, with_do=True)
+    scale = 1 / math.sqrt(d)
+    assert (fa.fa_bwd_kv_workspace_size(B, H, Hkv, N, N, d)
+            > fa.fa_bwd_workspace_size(B, H, N, d))
+    o, lse = _fwd(q, k, v, True, scale)
+    got = _bwd(q, k, v, do, o, lse, True, scale, True)
+    plain = _bwd(q, k, v, do, o, lse, True, scale, False)
+    assert torch.equal(got[0], plain[0])
+    for a, b in zip(got[1:], plain[1:]):
+        a, b = a.float(), b.float()
+        assert torch.isfinite(a).all()
+        bound = 2.0 ** -7 * torch.maximum(a.abs(), b.abs()) + 2.0 ** -16 * b.abs().max()
+        excess = ((a - b).abs() - bound).max().item()
+        _say(f"   split vs unsplit: max diff {(a - b).abs().max().item():.3e}, "
+             f"worst excess over the bound {excess:.3e}")
+        assert excess <= 0
+    ref = naive_bwd_gqa(_f64(q[:, 28:]), _f64(k[:, 7:]), _f64(v[:, 7:]), _f64(do[:, 28:]),
+                        scale, True)
+    tol = max(TOL, 2.0 ** -7 * max(float(np.max(np.abs(r))) for r in ref))
+    errs = [float(np.max(np.abs(_f64(g) - r)))
+            for g, r in zip((got[0][:, 28:], got[1][:, 7:], got[2][:, 7:]), ref)]
+    _say(f"[llama8b gqa bwd] max|d dQ|={errs[0]:.3e} |d dK|={errs[1]:.3e} "
+         f"|d dV|={errs[2]:.3e} (tol {tol:.3e})")
+    assert max(errs) <= tol

@@ -147,8 +147,9 @@ def _bwd(q, k, v, do, causal, scale):
     dk = torch.full_like(kd, float("nan"))
     dv = torch.full_like(vd, float("nan"))
     B, H, Nq, d = q.shape
-    ws = torch.full((max(1, fa.fa_bwd_workspace_size(B, H, Nq, d)),), 0xFF, dtype=torch.uint8,
-                    device="cuda")
+    Hkv, Nk = k.shape[1], k.shape[2]
+    ws = torch.full((max(1, fa.fa_bwd_kv_workspace_size(B, H, Hkv, Nq, Nk, d)),), 0xFF,
+                    dtype=torch.uint8, device="cuda")
     fa.fa_bwd_kv(qd, kd, vd, o, dod, lse, dq, dk, dv, ws, causal, scale)
     torch.cuda.synchronize()
     return dq, dk, dv
