@@ -756,8 +756,9 @@ __global__ __launch_bounds__(256, 1) void fwd_d256_kernel(const FwdArgs a) {
 //       16 t + 4 h + {0, 1, 2, 3, 8, 9, 10, 11} of that feature.
 // ds_read_b64_tr_b8: in each 16-lane group, lane 2j + c reads 8 bytes of row
 // j (bytes 8c .. 8c + 7 of a 16-byte column chunk); output lane i receives
-// byte i of rows 0..7.  K and V tiles use the row swizzle (r / 2) % 8 on
-// their 16-byte chunks, conflict-free for both read patterns.
+// byte i of rows 0..7.  K tiles use the row swizzle (r / 2) % 8 on their
+// 16-byte chunks (conflict-free for the row reads), V tiles swzv8 below
+// (conflict-free for the transposing reads).
 constexpr int kWavesF8 = 4;
 constexpr int kBMF8 = 32 * kWavesF8;
 constexpr int kBNF8 = 64;
@@ -773,6 +774,12 @@ __device__ __forceinline__ f32x16 mfma_32x32x64_f8(const i32x8& a, const i32x8& 
 }
 
 __device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
+// V tiles: ds_read_b64_tr_b8 reads, per 32 lanes, rows {0..3, 8..11} + c
+// (c a multiple of 4), four lanes (two 8-byte halves of two 16-byte chunks)
+// per row; 2 ((r / 2) % 2) + 4 ((r / 8) % 2) gives each of the four even and
+// four odd rows its own chunk pair, so the 32 reads fill 32 distinct 8-byte
+// bank slots (the row swizzle above maps rows r and r + 2 onto one pair)
+__device__ __forceinline__ int swzv8(int r) { return (((r >> 1) & 1) << 1) | (((r >> 3) & 1) << 2); }
 
 // Two waves per SIMD (two workgroups per CU, each with its own barriers): the
 // kernel issues a tile's matrix and vector work in order, and the other
@@ -833,11 +840,11 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const FwdArgs a, float 
       const int slot = (i * kWavesF8 + w) * 64 + lane;
       const int row = slot / 8;
       const int src_row = min(k0 + row, Nk - 1) - k0;
-      const int chunk = (slot % 8) ^ swz8(row);
-      const unsigned src = (unsigned)(src_row * ROW + chunk * 16);
+      const unsigned srck = (unsigned)(src_row * ROW + ((slot % 8) ^ swz8(row)) * 16);
+      const unsigned srcv = (unsigned)(src_row * ROW + ((slot % 8) ^ swzv8(row)) * 16);
       const unsigned dst = (unsigned)((i * kWavesF8 + w) * 1024);
-      dma16(gk, src, stk + dst);
-      dma16(gv, src, stv + dst);
+      dma16(gk, srck, stk + dst);
+      dma16(gv, srcv, stv + dst);
     }
   };
   if (nkt > 0) issue(0);
@@ -871,7 +878,7 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const FwdArgs a, float 
   const int gv = (lane >> 4) & 1;
   auto voff_of = [&](int db, int t) __attribute__((always_inline)) {
     const int row = 16 * t + 4 * h + 8 * (jv >> 2) + (jv & 3);
-    return row * ROW + (((2 * db + gv) ^ swz8(row)) << 4) + 8 * cv;
+    return row * ROW + (((2 * db + gv) ^ swzv8(row)) << 4) + 8 * cv;
   };
 
   f32x16 acc[4];
