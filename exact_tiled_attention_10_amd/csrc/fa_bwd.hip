@@ -33,7 +33,13 @@
 //                 key tiles are as large as the registers allow.
 //                 Query blocks wholly before the key tile are skipped under
 //                 causal masking ("LLM Architecture Refresh [3]", section 7).
-//   3. bwd_dq:    dQ = bf16(accumulator).
+//                 With grouped-query heads a group's query heads may be dealt
+//                 to several workgroups per key tile, which then write float32
+//                 partial dK, dV that bwd_kv_reduce_kernel sums (after the
+//                 key-tile kernel below).
+//   3. bwd_dq:    dQ = bf16(accumulator) at d = 64; at d = 128 and 256 dQ has
+//                 its own query-stationary pass (section 4) and bwd_main makes
+//                 dK and dV only.
 //
 // The P and dS registers of the S / dP accumulators are already the B
 // operands of dV^T and dK^T (keys across lanes, queries across registers).
