@@ -130,6 +130,33 @@ def test_kv_workspace_size(lib):
     assert lib.fa_bwd_kv_workspace_size(1, 8, 1, 256, 256, 64) == base + 2 * 8 * 1 * 256 * 64 * 4
 
 
+def test_kv_workspace_size_is_a_split_of_the_group(lib):
+    """Over many shapes: the grouped-query workspace is the plain one plus
+    float32 partials [2][s][B*Hkv][Nk][d] for a divisor s of the group (s = 1:
+    nothing added), and the split never goes past the group."""
+    import random
+    rng = random.Random(5)
+    for _ in range(300):
+        d = rng.choice((64, 128, 256))
+        Hkv = rng.choice((1, 2, 4, 8))
+        group = rng.choice((1, 2, 3, 4, 8))
+        B = rng.choice((1, 2, 4))
+        Nq = rng.choice((1, 63, 300, 2048, 4096))
+        Nk = rng.choice((1, 100, 2048, 4096, 8192))
+        H = Hkv * group
+        base = lib.fa_bwd_workspace_size(B, H, Nq, d)
+        kv = lib.fa_bwd_kv_workspace_size(B, H, Hkv, Nq, Nk, d)
+        extra = kv - base
+        assert extra >= 0
+        if extra == 0:
+            continue
+        unit = 2 * B * Hkv * Nk * d * 4
+        splits = [s for s in range(2, group + 1) if group % s == 0
+                  and (s * unit + 255) // 256 * 256 == extra]
+        assert splits, (B, H, Hkv, Nq, Nk, d, extra)
+        assert group > 1
+
+
 def _bwd(lib, ws_bytes=None, **kw):
     B, H, N, d = kw.get("B", 1), kw.get("H", 2), kw.get("N", 100), kw.get("d", 64)
     ptrs = dict(q=A, k=A + MB, v=A + 2 * MB, o=A + 3 * MB, dout=A + 4 * MB, lse=A + 5 * MB,
