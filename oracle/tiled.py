@@ -6,80 +6,143 @@ independent CPU implementation.  It pins the plain-definition oracle in
 module's counters must reproduce the tile, FLOP and traffic tables the source
 pages print.
 
-Steps, in the order the pages give them:
+How it is organised (derived from the equations, not from any printed loop):
 
-* "LLM Architecture Refresh [3]: Flash Attention Is Exact, and Here's the
-  Proof", section 2: the online normaliser -- a running max m and running sum l,
-  with the held sum rebased by exp(m_old - m_new) whenever a block raises the
-  max.
-* same page, section 4: outer loop over query blocks, inner loop streaming
-  key/value blocks; the accumulated output is rescaled by the same factor as l
-  and divided by l once, after the last block.
-* "Flash Attention, From First Principles", "The scaffold": a tile row's local
-  max and local sum merge into the notebook by the same law (a composite
-  newcomer).
-* "LLM Architecture Refresh [3]", section 7: with causal masking a key block
-  that starts after the query block's last row is skipped, not computed; only
-  tiles that straddle the diagonal need a mask.
-* "FlashAttention from scratch", Trade-offs and edge cases: a row whose running
-  max is still -inf would give exp(-inf - (-inf)) = NaN; such a row takes
-  correction 1 and contributes nothing.
-* "FlashAttention from scratch", Follow-up questions: the backward recomputes
-  P = exp(S - L) from the saved L = m + log l; dV += P^T dO; dP = dO V^T;
-  D = rowsum(dO * O); dS = P * (dP - D); dQ += s dS K; dK += s dS^T Q.
-* Counters ("LLM Architecture Refresh [3]", sections 7 and 8): skipped tiles;
-  matmul FLOPs 2 * (2 * batch * heads * rows * cols * d) per computed tile;
-  traffic 2 * batch * heads * cols * d * elem per computed tile for K and V,
-  plus Q read and O written once per query block.
+* The score matrix is cut into a grid of (query block, key block) tiles.
+  ``_tile_plan`` classifies every tile before anything is computed: a tile
+  whose first key comes after its last query is *skipped* under causal
+  masking, a tile that straddles the diagonal is *masked*, every other tile is
+  *full* ("LLM Architecture Refresh [3]: Flash Attention Is Exact, and Here's
+  the Proof", section 7: only diagonal tiles need a mask, tiles wholly in the
+  future are never computed).
+* Every query row keeps a notebook (``_RowNotebook``): a reference exponent m,
+  the mass l = sum exp(s - m) of the keys seen so far, and the unnormalised
+  output u = sum exp(s - m) v.  A computed tile is first summarised on its own
+  -- its local max, its local mass and its local unnormalised output, all
+  measured against that local max -- and the summary then joins the notebook
+  as one composite newcomer: m' = max(m, m~), and both parties are converted
+  to m' by the factors exp(m - m') and exp(m~ - m') before they are added
+  ("Flash Attention, From First Principles", "The scaffold"; "FlashAttention
+  from scratch", Step 2).  A party whose reference is still -inf (nothing
+  visible yet) weighs nothing: the guard of "FlashAttention from scratch",
+  "Trade-offs and edge cases", against exp(-inf - (-inf)) = NaN.
+* The output is u / l, divided once after the last key block ("FlashAttention
+  from scratch", Step 3: deferring the division is exact); the saved
+  statistic is lse = m + log l (same page, Follow-up questions).
+* The single-row normaliser of "LLM Architecture Refresh [3]", section 2, is
+  the same notebook with no output column: ``online_normaliser`` folds the
+  blocks of one row into (m, l) and records every conversion.
+* The recomputing backward ("FlashAttention from scratch", Follow-up
+  questions): P = exp(S - L) rebuilt per tile from the saved L;
+  dV += P^T dO; dP = dO V^T; D = rowsum(dO * O); dS = P * (dP - D);
+  dQ += s dS K; dK += s dS^T Q.
+* Counters, worked out from what a tile touches (they reproduce the tables of
+  "LLM Architecture Refresh [3]", sections 7 and 8): each computed tile runs
+  two products (scores and the value blend) of rows x cols x d multiply-adds,
+  two FLOPs each; it streams its key block and its value block from memory;
+  each query block reads its queries and writes its output once.  Skipped
+  tiles touch nothing.
 """
 
 from __future__ import annotations
 
+from dataclasses import dataclass
+
 import numpy as np
 
+SKIPPED, MASKED, FULL = "skipped", "masked", "full"
 
-def _tile_is_skipped(causal: bool, q0: int, rows: int, k0: int) -> bool:
-    """A key block whose first key lies after the query block's last row."""
-    return causal and k0 > q0 + rows - 1
+
+def _tile_kind(causal: bool, q_first: int, q_last: int, k_first: int, k_last: int) -> str:
+    """Kind of the tile covering queries q_first..q_last and keys
+    k_first..k_last (inclusive), with key j visible to query i iff j <= i."""
+    if not causal or k_last <= q_first:
+        return FULL
+    if k_first > q_last:
+        return SKIPPED
+    return MASKED
+
+
+def _spans(n: int, block: int):
+    """Inclusive (first, last) index pairs of consecutive blocks; the last one
+    may be shorter (a ragged edge)."""
+    return [(s, min(s + block, n) - 1) for s in range(0, n, block)]
+
+
+def _tile_plan(n_q: int, n_k: int, block_q: int, block_k: int, causal: bool):
+    """[(query span, [(key span, kind), ...]), ...] for the whole grid."""
+    return [((qa, qb), [((ka, kb), _tile_kind(causal, qa, qb, ka, kb))
+                        for ka, kb in _spans(n_k, block_k)])
+            for qa, qb in _spans(n_q, block_q)]
 
 
 def causal_tile_counts(n: int, block: int):
-    """(computed, skipped) tile counts of the tiled loop for an n x n causal
-    score matrix cut into square blocks.  Runs the loop's own skip predicate
-    over every tile; no closed form is used."""
-    computed = skipped = 0
-    for q0 in range(0, n, block):
-        rows = min(block, n - q0)
-        for k0 in range(0, n, block):
-            if _tile_is_skipped(True, q0, rows, k0):
-                skipped += 1
-            else:
-                computed += 1
-    return computed, skipped
+    """(computed, skipped) tile counts for an n x n causal score matrix cut
+    into square blocks, from the tile classification (no closed form)."""
+    kinds = [kind for _, row in _tile_plan(n, n, block, block, True) for _, kind in row]
+    skipped = sum(1 for kind in kinds if kind == SKIPPED)
+    return len(kinds) - skipped, skipped
+
+
+def _weight(ref, target):
+    """exp(ref - target), with a party at reference -inf weighing 0."""
+    ref = np.asarray(ref, dtype=np.float64)
+    finite = np.isfinite(ref)
+    with np.errstate(invalid="ignore"):
+        diff = np.where(finite, ref - target, 0.0)
+    return np.where(finite, np.exp(diff), 0.0)
+
+
+@dataclass
+class _RowNotebook:
+    """Running state of a set of query rows: reference m [..., r, 1], mass l
+    [..., r, 1] and unnormalised output u [..., r, dv], all measured against m."""
+    m: np.ndarray
+    l: np.ndarray
+    u: np.ndarray
+
+    @classmethod
+    def empty(cls, lead, rows, dv):
+        return cls(np.full((*lead, rows, 1), -np.inf), np.zeros((*lead, rows, 1)),
+                   np.zeros((*lead, rows, dv)))
+
+    def admit(self, scores, values, rebase_history: bool = True):
+        """Merge one tile (scores [..., r, c], values [..., c, dv]) as a
+        composite newcomer: summarise it against its own max, then convert
+        both the history and the newcomer to the larger reference."""
+        m_tile = np.max(scores, axis=-1, keepdims=True)
+        e = _weight(scores, m_tile)              # exp(s - m~), 0 where masked
+        l_tile = np.sum(e, axis=-1, keepdims=True)
+        u_tile = e @ values
+        m_next = np.maximum(self.m, m_tile)
+        keep = _weight(self.m, m_next) if rebase_history else np.ones_like(self.m)
+        join = _weight(m_tile, m_next)
+        self.l = keep * self.l + join * l_tile
+        self.u = keep * self.u + join * u_tile
+        self.m = m_next
+        return keep
 
 
 def online_normaliser(x, block: int):
     """Stream a 1-D row of logits in blocks; return (m, l, trace).
 
-    "LLM Architecture Refresh [3]", section 2: m_new = max(m_old, max(block));
-    l_new = l_old * exp(m_old - m_new) + sum(exp(block - m_new)).
-    ``trace`` holds one dict per block: m_old, m_new, correction, the rebased
-    history l_old * correction, and l after the block.
+    Each block is summarised by its own max and mass and merged into the row's
+    (m, l) by the conversion law ("LLM Architecture Refresh [3]", section 2;
+    "Flash Attention, From First Principles", "The scaffold").  ``trace``
+    holds one dict per block: m_old, m_new, correction = exp(m_old - m_new)
+    (1 while nothing has been seen), the rebased history l_old * correction,
+    and l after the block.
     """
-    x = np.asarray(x, dtype=np.float64)
-    m = -np.inf
-    l = 0.0
+    row = np.asarray(x, dtype=np.float64)
+    book = _RowNotebook.empty((), 1, 0)
     trace = []
-    for start in range(0, x.shape[0], block):
-        blk = x[start:start + block]
-        m_new = max(m, float(np.max(blk)))
-        correction = 1.0 if m_new == -np.inf else float(np.exp(m - m_new))
-        rebased = l * correction
-        l = rebased + float(np.sum(np.exp(blk - m_new)))
-        trace.append(dict(m_old=m, m_new=m_new, correction=correction,
-                          rebased=rebased, l=l))
-        m = m_new
-    return m, l, trace
+    for first, last in _spans(row.shape[0], block):
+        m_old, l_old = float(book.m[0, 0]), float(book.l[0, 0])
+        keep = book.admit(row[None, first:last + 1], np.zeros((last + 1 - first, 0)))
+        correction = float(keep[0, 0]) if np.isfinite(m_old) else 1.0
+        trace.append(dict(m_old=m_old, m_new=float(book.m[0, 0]), correction=correction,
+                          rebased=l_old * correction, l=float(book.l[0, 0])))
+    return float(book.m[0, 0]), float(book.l[0, 0]), trace
 
 
 def _as_bhnd(x):
@@ -89,6 +152,15 @@ def _as_bhnd(x):
     elif a.ndim == 3:
         a = a[None]
     return a
+
+
+def _masked_scores(q_blk, k_blk, scale, kind, q_first, k_first):
+    s = scale * (q_blk @ np.swapaxes(k_blk, -1, -2))
+    if kind == MASKED:
+        qpos = np.arange(q_first, q_first + q_blk.shape[-2])[:, None]
+        kpos = np.arange(k_first, k_first + k_blk.shape[-2])[None, :]
+        s = np.where(kpos <= qpos, s, -np.inf)
+    return s
 
 
 def tiled_fwd(q, k, v, scale: float, causal: bool = False,
@@ -101,60 +173,43 @@ def tiled_fwd(q, k, v, scale: float, causal: bool = False,
     scores) and counters {tiles_computed, blocks_skipped, matmul_flops,
     hbm_bytes}.  ``elem_bytes`` is only used by the traffic counter.
 
-    If ``trace`` is a list, a snapshot dict(q0, k0, m, l, acc) of the running
-    notebook is appended after every computed tile (for the worked examples).
+    If ``trace`` is a list, a snapshot dict(q0, k0, m, l, acc) of the query
+    block's notebook (acc = the unnormalised output) is appended after every
+    computed tile (for the worked examples).
 
-    ``_no_rescale`` plants the classic bug (history never rebased when the max
-    moves) so a test can show the worked-example pin catches it.
+    ``_no_rescale`` plants the classic bug -- the history is never converted
+    when the reference moves -- so a test can show the worked-example pin
+    catches it.
     """
-    q = _as_bhnd(q)
-    k = _as_bhnd(k)
-    v = _as_bhnd(v)
+    q, k, v = _as_bhnd(q), _as_bhnd(k), _as_bhnd(v)
     scale = float(scale)
-    b, h, n, d = q.shape
-    dv_ = v.shape[-1]
-    out = np.empty((b, h, n, dv_), dtype=np.float64)
-    lse = np.empty((b, h, n), dtype=np.float64)
-    counters = dict(tiles_computed=0, blocks_skipped=0, matmul_flops=0,
-                    hbm_bytes=0)
-    for q0 in range(0, n, block_q):
-        qi = q[:, :, q0:q0 + block_q]
-        rows = qi.shape[2]
-        counters["hbm_bytes"] += 2 * b * h * rows * d * elem_bytes  # Q in, O out
-        m = np.full((b, h, rows, 1), -np.inf)
-        l = np.zeros((b, h, rows, 1))
-        acc = np.zeros((b, h, rows, dv_))
-        qpos = np.arange(q0, q0 + rows)
-        for k0 in range(0, n, block_k):
-            if _tile_is_skipped(causal, q0, rows, k0):
+    lead = q.shape[:2]
+    bh = lead[0] * lead[1]
+    n, d = q.shape[2], q.shape[3]
+    dv = v.shape[-1]
+    out = np.empty((*lead, n, dv))
+    lse = np.empty((*lead, n))
+    counters = dict(tiles_computed=0, blocks_skipped=0, matmul_flops=0, hbm_bytes=0)
+    for (qa, qb), row_tiles in _tile_plan(n, k.shape[2], block_q, block_k, causal):
+        rows = qb + 1 - qa
+        q_blk = q[:, :, qa:qb + 1]
+        book = _RowNotebook.empty(lead, rows, dv)
+        counters["hbm_bytes"] += bh * (rows * d + rows * dv) * elem_bytes   # Q in, O out
+        for (ka, kb), kind in row_tiles:
+            if kind == SKIPPED:
                 counters["blocks_skipped"] += 1
                 continue
-            kj = k[:, :, k0:k0 + block_k]
-            vj = v[:, :, k0:k0 + block_k]
-            cols = kj.shape[2]
+            cols = kb + 1 - ka
             counters["tiles_computed"] += 1
-            counters["matmul_flops"] += 2 * (2 * b * h * rows * cols * d)
-            counters["hbm_bytes"] += 2 * b * h * cols * d * elem_bytes
-            s = scale * (qi @ np.swapaxes(kj, -1, -2))        # score tile
-            if causal and k0 + cols - 1 > q0:                  # straddles diagonal
-                kpos = np.arange(k0, k0 + cols)
-                s = np.where(kpos[None, :] <= qpos[:, None], s, -np.inf)
-            m_tile = np.max(s, axis=-1, keepdims=True)
-            m_new = np.maximum(m, m_tile)
-            dead = ~np.isfinite(m_new)                         # nothing seen yet
-            m_ref = np.where(dead, 0.0, m_new)
-            correction = np.where(dead, 1.0, np.exp(m - m_ref))
-            if _no_rescale:
-                correction = np.ones_like(correction)
-            p = np.where(dead, 0.0, np.exp(s - m_ref))
-            l = l * correction + np.sum(p, axis=-1, keepdims=True)
-            acc = acc * correction + p @ vj                    # rebase, then add
-            m = m_new
+            counters["matmul_flops"] += bh * 2 * (rows * cols * d + rows * cols * dv)
+            counters["hbm_bytes"] += bh * (cols * d + cols * dv) * elem_bytes  # K, V in
+            s = _masked_scores(q_blk, k[:, :, ka:kb + 1], scale, kind, qa, ka)
+            book.admit(s, v[:, :, ka:kb + 1], rebase_history=not _no_rescale)
             if trace is not None:
-                trace.append(dict(q0=q0, k0=k0, m=m.copy(), l=l.copy(),
-                                  acc=acc.copy()))
-        out[:, :, q0:q0 + rows] = acc / l                      # one division
-        lse[:, :, q0:q0 + rows] = (m + np.log(l))[..., 0]
+                trace.append(dict(q0=qa, k0=ka, m=book.m.copy(), l=book.l.copy(),
+                                  acc=book.u.copy()))
+        out[:, :, qa:qb + 1] = book.u / book.l
+        lse[:, :, qa:qb + 1] = (book.m + np.log(book.l))[..., 0]
     return out, lse, counters
 
 
@@ -162,42 +217,30 @@ def tiled_bwd(q, k, v, o, lse, do, scale: float, causal: bool = False,
               block_q: int = 128, block_k: int = 128):
     """Recomputing backward: (dQ, dK, dV) from Q, K, V, O, lse and dO.
 
-    Outer loop over key/value blocks (dK, dV accumulate per block), inner loop
-    over query blocks (dQ accumulates across key blocks).  Tiles wholly in the
-    future are skipped under causal masking.  All arrays [B, H, N, d]; lse
-    [B, H, N].
+    Key blocks on the outside (dK, dV of a key block are complete when its
+    column of tiles is done), query blocks inside (dQ gathers a contribution
+    from every key block).  Skipped tiles contribute nothing; masked tiles
+    rebuild P = 0 for the future keys.  All arrays [B, H, N, d]; lse [B, H, N].
     """
-    q = _as_bhnd(q)
-    k = _as_bhnd(k)
-    v = _as_bhnd(v)
-    o = _as_bhnd(o)
-    do = _as_bhnd(do)
+    q, k, v, o, do = (_as_bhnd(x) for x in (q, k, v, o, do))
     lse = np.asarray(lse, dtype=np.float64).reshape(q.shape[:3])
     scale = float(scale)
     n = q.shape[2]
-    dmat = np.sum(do * o, axis=-1)                              # D = rowsum(dO*O)
-    dq = np.zeros_like(q)
-    dk = np.zeros_like(k)
-    dv = np.zeros_like(v)
-    for k0 in range(0, n, block_k):
-        kj = k[:, :, k0:k0 + block_k]
-        vj = v[:, :, k0:k0 + block_k]
-        cols = kj.shape[2]
-        kpos = np.arange(k0, k0 + cols)
-        for q0 in range(0, n, block_q):
-            rows = min(block_q, n - q0)
-            if _tile_is_skipped(causal, q0, rows, k0):
+    delta = np.sum(do * o, axis=-1)[..., None]                  # D = rowsum(dO * O)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    plan = _tile_plan(n, k.shape[2], block_q, block_k, causal)
+    for kcol, (ka, kb) in enumerate(_spans(k.shape[2], block_k)):
+        k_blk, v_blk = k[:, :, ka:kb + 1], v[:, :, ka:kb + 1]
+        for (qa, qb), row_tiles in plan:
+            kind = row_tiles[kcol][1]
+            if kind == SKIPPED:
                 continue
-            qi = q[:, :, q0:q0 + rows]
-            doi = do[:, :, q0:q0 + rows]
-            s = scale * (qi @ np.swapaxes(kj, -1, -2))
-            if causal and k0 + cols - 1 > q0:
-                qpos = np.arange(q0, q0 + rows)
-                s = np.where(kpos[None, :] <= qpos[:, None], s, -np.inf)
-            p = np.exp(s - lse[:, :, q0:q0 + rows, None])       # P = exp(S - L)
-            dv[:, :, k0:k0 + cols] += np.swapaxes(p, -1, -2) @ doi
-            dp = doi @ np.swapaxes(vj, -1, -2)
-            ds = p * (dp - dmat[:, :, q0:q0 + rows, None])
-            dq[:, :, q0:q0 + rows] += scale * (ds @ kj)
-            dk[:, :, k0:k0 + cols] += scale * (np.swapaxes(ds, -1, -2) @ qi)
+            q_blk, do_blk = q[:, :, qa:qb + 1], do[:, :, qa:qb + 1]
+            s = _masked_scores(q_blk, k_blk, scale, kind, qa, ka)
+            p = np.exp(s - lse[:, :, qa:qb + 1, None])              # P = exp(S - L)
+            dp = do_blk @ np.swapaxes(v_blk, -1, -2)
+            ds = p * (dp - delta[:, :, qa:qb + 1])
+            dv[:, :, ka:kb + 1] += np.swapaxes(p, -1, -2) @ do_blk
+            dk[:, :, ka:kb + 1] += scale * (np.swapaxes(ds, -1, -2) @ q_blk)
+            dq[:, :, qa:qb + 1] += scale * (ds @ k_blk)
     return dq, dk, dv
