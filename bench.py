@@ -3,19 +3,32 @@
 
 A step is one pass of the whole hot path over one batch of synthetic input:
 the forward (fa_fwd: O and lse) and the backward (fa_bwd's three stages: D,
-the key-tile kernel, dQ conversion) of causal attention at the training-step
-shape [4, 16, 2048, 64] in bf16.  Inputs are resident in HBM before timing.
+the key-tile kernel, dQ) of causal attention at the training-step shape
+[4, 16, 2048, 64] in bf16.  Inputs are resident in HBM before timing.
+
+Timing protocol (every figure is a steady-state one): a time-based settle
+phase of untimed steps first (the shader clock takes a fraction of a second
+of sustained matrix-core load to settle), then the counted warm-up steps,
+then repeats of exactly --steps steps, each repeat bracketed by device
+synchronisation and HIP events, until at least --min-timed-ms of GPU time is
+covered; ms_per_step is the median repeat, with the minimum beside it.  A
+second pass of the same kind records HIP events around every kernel of the
+step on its launch stream, for the per-kernel durations of the roofline.
 
 Prints ONE JSON line.  Throughput counts 4*N^2*d FLOP per (batch, head) for
 the forward, halved when causal, and 2.5x that for the backward.
 
 Extra modes (each prints its own JSON):
+  --only NAME              run just one workload (the step, or one forward or
+                           extra shape) a few times: the target of per-shape
+                           rocprofv3 counter runs
   --copy-calibration MIB   time a plain device copy of MIB MiB (used to scale
                            rocprofv3 FETCH_SIZE / WRITE_SIZE counters)
-  --pmc-summary FETCH_CSV WRITE_CSV
-                           turn two rocprofv3 --pmc counter CSVs into
-                           profiles/traffic.json (HBM bytes per launch of the
-                           dominant kernel, scaled by the copy calibration)
+  --pmc-summary FETCH_CSV WRITE_CSV --kernel K --workload W
+                           turn two rocprofv3 --pmc counter CSVs into an entry
+                           of profiles/traffic.json (HBM bytes per launch of
+                           kernel K on workload W, scaled by the copy
+                           calibration)
 """
 
 from __future__ import annotations
@@ -27,6 +40,7 @@ import json
 import math
 import os
 import platform
+import statistics
 import sys
 import time
 
@@ -36,26 +50,40 @@ if ROOT not in sys.path:
 
 METRIC = "attention fwd/bwd TFLOP/s and % of bf16 MFMA peak at N=1k-32k, d=64/128"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+PEAK_FP32_TFLOPS = 157.3       # MI355X dense fp32 (matrix and vector), published
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+CSRC = "exact_tiled_attention_10_amd/csrc/"
 # sources each kernel is built from: counter-derived traffic is used only while
 # they are unchanged
 KERNEL_SOURCES = {
-    "bwd_main_kernel": ["exact_tiled_attention_10_amd/csrc/fa_bwd.hip",
-                        "exact_tiled_attention_10_amd/csrc/fa_common.h"],
-    "fwd_bf16_kernel": ["exact_tiled_attention_10_amd/csrc/fa_fwd.hip",
-                        "exact_tiled_attention_10_amd/csrc/fa_common.h"],
+    "bwd_main_kernel": [CSRC + "fa_bwd.hip", CSRC + "fa_common.h"],
+    "fwd_bf16_kernel": [CSRC + "fa_fwd.hip", CSRC + "fa_common.h"],
 }
 STEP_WORKLOAD = "train_step_n2048"
-SWEEP = [("gpt2_medium_n1024", False), ("gpt2_medium_n1024", True),
-         ("llama8b_n4096", True), ("long_context_n16384", True),
-         ("long_context_n32768", True)]
+# forward shapes: (key, workload, causal)
+SWEEP = [("single_head_fp32_n256", "single_head_fp32_n256", False),
+         ("gpt2_medium_n1024", "gpt2_medium_n1024", False),
+         ("gpt2_medium_n1024_causal", "gpt2_medium_n1024", True),
+         ("llama8b_n4096_causal", "llama8b_n4096", True),
+         ("long_context_n16384_causal", "long_context_n16384", True),
+         ("long_context_n32768_causal", "long_context_n32768", True)]
 
 
 def fwd_flops(B, H, N, d, causal):
     f = 4.0 * N * N * d * B * H
     return f / 2 if causal else f
+
+
+def fwd_algorithmic_bytes(B, H, N, d, elem=2):
+    """Read Q, K, V; write O and the float32 lse."""
+    return 4 * B * H * N * d * elem + B * H * N * 4
+
+
+def bwd_algorithmic_bytes(B, H, N, d, elem=2):
+    """Read Q, K, V, O, dO and lse; write dQ, dK, dV."""
+    return 8 * B * H * N * d * elem + B * H * N * 4
 
 
 def source_hash(kernel: str) -> str:
@@ -70,12 +98,16 @@ def source_hash(kernel: str) -> str:
 # GPU timing
 # ---------------------------------------------------------------------------
 
-def run_step_bench(steps: int, warmup: int):
+def make_step(workload: str = STEP_WORKLOAD):
+    """Device tensors of the training-step workload and ``step(ev=None)``, one
+    pass of fa_fwd -> fa_bwd_preprocess -> fa_bwd_main -> fa_bwd_finalize on
+    the current stream.  ``ev``, a list of five HIP events, brackets the four
+    launches.  Returns (step, tensors); the parity tests call this same step."""
     import torch
     import exact_tiled_attention_10_amd as fa
     from workloads import WORKLOADS, workload_inputs
 
-    w = WORKLOADS[STEP_WORKLOAD]
+    w = WORKLOADS[workload]
     causal = True
     q, k, v, do = (t.cuda() for t in workload_inputs(w, with_do=True))
     B, H, N, d = q.shape
@@ -98,100 +130,148 @@ def run_step_bench(steps: int, warmup: int):
         if ev is not None:
             ev[3].record(stream)
         fa.fa_bwd_finalize(dq, ws, q, k, v, do, causal, w.scale)
+        if ev is not None:
+            ev[4].record(stream)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    # the timed steps carry no events of their own: an event recorded between
-    # two launches holds the next one until the previous has drained (four per
-    # step added ~12 us to a ~195 us step)
-    torch.cuda.synchronize()
-    t0.record(stream)
-    for _ in range(steps):
-        step()
-    t1.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t0.elapsed_time(t1)
-    ms = total_ms / steps
-    # then the same number of steps again with events around each kernel on
-    # its launch stream: the forward and key-tile kernel durations
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
-    torch.cuda.synchronize()
-    t0.record(stream)
-    for i in range(steps):
-        step(evs[i])
-    t1.record(stream)
-    torch.cuda.synchronize()
-    inst_ms = t0.elapsed_time(t1) / steps
-    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
-    main_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / steps
-    ff = fwd_flops(B, H, N, d, causal)
-    bf = 2.5 * ff
-    return dict(workload=w, ms_per_step=ms, step_flops=ff + bf, fwd_ms=fwd_ms, main_ms=main_ms,
-                fwd_flops=ff, bwd_flops=bf, instrumented_ms_per_step=inst_ms)
+    tensors = dict(q=q, k=k, v=v, do=do, o=o, lse=lse, dq=dq, dk=dk, dv=dv, ws=ws,
+                   workload=w, causal=causal)
+    return step, tensors
 
 
-def run_fwd_sweep(reps: int = 20, warm_s: float = 0.05):
+def _settle(fn, seconds: float) -> int:
+    """Run ``fn`` untimed for at least ``seconds`` of wall time (synchronising
+    every 16 calls so the queue stays short); returns the call count."""
     import torch
-    import exact_tiled_attention_10_amd as fa
-    from workloads import WORKLOADS, workload_inputs
-
-    out = {}
-    for name, causal in SWEEP:
-        w = WORKLOADS[name]
-        q, k, v = (t.cuda() for t in workload_inputs(w, with_do=False))
-        o = torch.empty_like(q)
-        lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
-        t_end = time.perf_counter() + warm_s
-        n_warm = 0
-        while n_warm < 3 or time.perf_counter() < t_end:
-            fa.fa_fwd(q, k, v, o, lse, causal, w.scale)
-            n_warm += 1
-            if n_warm % 16 == 0:
-                torch.cuda.synchronize()
-        s = torch.cuda.Event(enable_timing=True)
-        e = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        s.record()
-        for _ in range(reps):
-            fa.fa_fwd(q, k, v, o, lse, causal, w.scale)
-        e.record()
-        torch.cuda.synchronize()
-        ms = s.elapsed_time(e) / reps
-        tf = fwd_flops(w.B, w.H, w.N, w.d, causal) / (ms * 1e-3) / 1e12
-        out[f"{name}{'_causal' if causal else ''}"] = dict(
-            fwd_ms=round(ms, 4), tflops=round(tf, 1),
-            pct_of_bf16_peak=round(100 * tf / PEAK_BF16_TFLOPS, 1))
-        del q, k, v, o, lse
-    torch.cuda.empty_cache()
-    return out
-
-
-def _time_launches(fn, reps: int = 20, warm_s: float = 0.05):
-    """Mean ms per call of ``fn`` (HIP events on the current stream) after
-    ``warm_s`` seconds of warm-up."""
-    import torch
-    t_end = time.perf_counter() + warm_s
+    t_end = time.perf_counter() + seconds
     n = 0
     while n < 3 or time.perf_counter() < t_end:
         fn()
         n += 1
         if n % 16 == 0:
             torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return n
+
+
+def _repeats(fn, per_repeat: int, min_ms: float, min_repeats: int = 5):
+    """Per-call ms of repeats of ``per_repeat`` calls of ``fn`` (HIP events on
+    the current stream, device synchronised around each repeat) until at
+    least ``min_ms`` of GPU time is covered."""
+    import torch
+    stream = torch.cuda.current_stream()
     s = torch.cuda.Event(enable_timing=True)
     e = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    s.record()
-    for _ in range(reps):
-        fn()
-    e.record()
-    torch.cuda.synchronize()
-    return s.elapsed_time(e) / reps
+    out, total = [], 0.0
+    while len(out) < min_repeats or total < min_ms:
+        torch.cuda.synchronize()
+        s.record(stream)
+        for _ in range(per_repeat):
+            fn()
+        e.record(stream)
+        torch.cuda.synchronize()
+        ms = s.elapsed_time(e)
+        total += ms
+        out.append(ms / per_repeat)
+    return out
 
 
-def run_extra_sweep():
+def run_step_bench(steps: int, warmup: int, settle_s: float, min_timed_ms: float):
+    import torch
+
+    step, t = make_step()
+    w = t["workload"]
+    B, H, N, d = t["q"].shape
+    n_settle = _settle(step, settle_s)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    # the timed steps carry no events of their own: an event recorded between
+    # two launches holds the next one until the previous has drained
+    reps = _repeats(step, steps, min_timed_ms)
+    # then repeats with events around each kernel on its launch stream
+    kernel_ms = {"fwd": [], "pre": [], "main": [], "fin": []}
+    inst = []
+    timed = 0.0
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    while len(inst) < 5 or timed < min_timed_ms:
+        torch.cuda.synchronize()
+        for i in range(steps):
+            step(evs[i])
+        torch.cuda.synchronize()
+        span = evs[0][0].elapsed_time(evs[-1][4])
+        timed += span
+        inst.append(span / steps)
+        for e in evs:
+            for j, key in enumerate(("fwd", "pre", "main", "fin")):
+                kernel_ms[key].append(e[j].elapsed_time(e[j + 1]))
+    ff = fwd_flops(B, H, N, d, True)
+    bf = 2.5 * ff
+    med = {k: statistics.median(v) for k, v in kernel_ms.items()}
+    return dict(workload=w, ms_per_step=statistics.median(reps), ms_min=min(reps),
+                ms_mean=statistics.fmean(reps), repeats=len(reps),
+                timed_ms=sum(reps) * steps, settle_steps=n_settle, settle_s=settle_s,
+                step_flops=ff + bf, fwd_flops=ff, bwd_flops=bf,
+                instrumented_ms_per_step=statistics.median(inst), kernel_ms=med)
+
+
+def _roofline_mfma(flops, ms, kernel, workload, peak=PEAK_BF16_TFLOPS, unit_bytes=None):
+    achieved = flops / (ms * 1e-3) / 1e12
+    r = dict(bound="mfma", achieved=round(achieved, 1), peak=peak, unit="TFLOP/s",
+             frac=round(achieved / peak, 4), traffic=load_traffic(kernel, workload),
+             kernel=kernel, kernel_ms=round(ms, 5))
+    if unit_bytes is not None:
+        r["algorithmic_bytes"] = unit_bytes
+    return r
+
+
+def run_fwd_sweep(settle_s: float = 0.2, min_ms: float = 150.0, only: str = None):
+    import torch
+    import exact_tiled_attention_10_amd as fa
+    from workloads import WORKLOADS, workload_inputs
+
+    out = {}
+    for key, name, causal in SWEEP:
+        if only is not None and key != only:
+            continue
+        w = WORKLOADS[name]
+        q, k, v = (t.cuda() for t in workload_inputs(w, with_do=False))
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+        f32 = w.dtype == "f32"
+        call = (lambda: fa.fa_fwd_f32(q, k, v, o, lse, causal, w.scale)) if f32 else \
+               (lambda: fa.fa_fwd(q, k, v, o, lse, causal, w.scale))
+        _settle(call, settle_s)
+        reps = _repeats(call, 10, min_ms)
+        ms = statistics.median(reps)
+        flops = fwd_flops(w.B, w.H, w.N, w.d, causal)
+        tf = flops / (ms * 1e-3) / 1e12
+        ent = dict(B=w.B, H=w.H, N=w.N, d=w.d, causal=causal, dtype=w.dtype,
+                   fwd_ms=round(ms, 5), fwd_ms_min=round(min(reps), 5),
+                   repeats=len(reps), launches_per_repeat=10, tflops=round(tf, 1))
+        if f32:
+            # two workgroups: a latency-bound correctness shape, no roofline claim
+            ent["pct_of_fp32_peak"] = round(100 * tf / PEAK_FP32_TFLOPS, 2)
+            ent["roofline"] = None
+            ent["note"] = "2 workgroups on 256 CUs: launch- and latency-bound"
+        else:
+            ent["pct_of_bf16_peak"] = round(100 * tf / PEAK_BF16_TFLOPS, 1)
+            ent["roofline"] = _roofline_mfma(
+                flops, ms, "fwd_bf16_kernel", key,
+                unit_bytes=fwd_algorithmic_bytes(w.B, w.H, w.N, w.d))
+        out[key] = ent
+        del q, k, v, o, lse
+    torch.cuda.empty_cache()
+    return out
+
+
+def _time_launches(fn, settle_s: float = 0.2, min_ms: float = 150.0, per_repeat: int = 10):
+    """(median, min) ms per call of ``fn`` after a settle phase."""
+    _settle(fn, settle_s)
+    reps = _repeats(fn, per_repeat, min_ms)
+    return statistics.median(reps), min(reps)
+
+
+def run_extra_sweep(only: str = None):
     """Grouped-query, head-dimension-256 and different-length shapes:
     Llama-3.1-8B's real head sharing (32 query heads over 8 key/value heads)
     for the causal N = 4096 forward and backward, the d = 256 causal forward at
@@ -201,63 +281,78 @@ def run_extra_sweep():
     HBM (every key and value byte is read once per key/value head)."""
     import torch
     import exact_tiled_attention_10_amd as fa
-    from workloads import make_gqa_inputs
+    from workloads import make_fp8_inputs, make_gqa_inputs
+
+    def want(key):
+        return only is None or only == key
+
+    def entry(ms, ms_min, flops, peak=PEAK_BF16_TFLOPS, extra=None):
+        tf = flops / (ms * 1e-3) / 1e12
+        e = dict(ms=round(ms, 5), ms_min=round(ms_min, 5), tflops=round(tf, 1),
+                 pct_of_bf16_peak=round(100 * tf / PEAK_BF16_TFLOPS, 1))
+        if peak != PEAK_BF16_TFLOPS:
+            e["pct_of_fp8_peak"] = round(100 * tf / peak, 1)
+        e.update(extra or {})
+        return e
 
     out = {}
     B, H, Hkv, N, d = 1, 32, 8, 4096, 128
-    q, k, v, do = (t.cuda() for t in make_gqa_inputs(B, H, Hkv, N, d, seed=6, with_do=True))
-    o = torch.empty_like(q)
-    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
     sc = 1 / math.sqrt(d)
-    ms = _time_launches(lambda: fa.fa_fwd_gqa(q, k, v, o, lse, True, sc))
-    tf = fwd_flops(B, H, N, d, True) / (ms * 1e-3) / 1e12
-    out["llama8b_gqa32x8_n4096_causal_fwd"] = dict(
-        ms=round(ms, 4), tflops=round(tf, 1), pct_of_bf16_peak=round(100 * tf / PEAK_BF16_TFLOPS, 1))
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = torch.empty(fa.fa_bwd_kv_workspace_size(B, H, Hkv, N, N, d), dtype=torch.uint8,
-                     device="cuda")
-    ms = _time_launches(lambda: fa.fa_bwd_gqa(q, k, v, o, do, lse, dq, dk, dv, ws, True, sc))
-    tf = 2.5 * fwd_flops(B, H, N, d, True) / (ms * 1e-3) / 1e12
-    out["llama8b_gqa32x8_n4096_causal_bwd"] = dict(
-        ms=round(ms, 4), tflops=round(tf, 1), pct_of_bf16_peak=round(100 * tf / PEAK_BF16_TFLOPS, 1))
-    del q, k, v, do, o, lse, dq, dk, dv, ws
+    if want("llama8b_gqa32x8_n4096_causal_fwd") or want("llama8b_gqa32x8_n4096_causal_bwd"):
+        q, k, v, do = (t.cuda() for t in make_gqa_inputs(B, H, Hkv, N, d, seed=6, with_do=True))
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+        fa.fa_fwd_gqa(q, k, v, o, lse, True, sc)
+        if want("llama8b_gqa32x8_n4096_causal_fwd"):
+            ms, mn = _time_launches(lambda: fa.fa_fwd_gqa(q, k, v, o, lse, True, sc))
+            out["llama8b_gqa32x8_n4096_causal_fwd"] = entry(ms, mn, fwd_flops(B, H, N, d, True))
+        if want("llama8b_gqa32x8_n4096_causal_bwd"):
+            dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+            ws = torch.empty(fa.fa_bwd_kv_workspace_size(B, H, Hkv, N, N, d),
+                             dtype=torch.uint8, device="cuda")
+            ms, mn = _time_launches(
+                lambda: fa.fa_bwd_gqa(q, k, v, o, do, lse, dq, dk, dv, ws, True, sc),
+                per_repeat=4)
+            out["llama8b_gqa32x8_n4096_causal_bwd"] = entry(
+                ms, mn, 2.5 * fwd_flops(B, H, N, d, True))
+            del dq, dk, dv, ws
+        del q, k, v, do, o, lse
 
-    B, H2, N2, d2 = 1, 16, 4096, 256
-    q, k, v = (t.cuda() for t in make_gqa_inputs(B, H2, H2, N2, d2, seed=9))
-    o = torch.empty_like(q)
-    lse = torch.empty((B, H2, N2), dtype=torch.float32, device="cuda")
-    ms = _time_launches(lambda: fa.fa_fwd(q, k, v, o, lse, True, 1 / 16.0))
-    tf = fwd_flops(B, H2, N2, d2, True) / (ms * 1e-3) / 1e12
-    out["d256_n4096_causal_fwd"] = dict(
-        ms=round(ms, 4), tflops=round(tf, 1), pct_of_bf16_peak=round(100 * tf / PEAK_BF16_TFLOPS, 1))
-    del q, k, v, o, lse
+    if want("d256_n4096_causal_fwd"):
+        B2, H2, N2, d2 = 1, 16, 4096, 256
+        q, k, v = (t.cuda() for t in make_gqa_inputs(B2, H2, H2, N2, d2, seed=9))
+        o = torch.empty_like(q)
+        lse = torch.empty((B2, H2, N2), dtype=torch.float32, device="cuda")
+        ms, mn = _time_launches(lambda: fa.fa_fwd(q, k, v, o, lse, True, 1 / 16.0))
+        out["d256_n4096_causal_fwd"] = entry(ms, mn, fwd_flops(B2, H2, N2, d2, True))
+        del q, k, v, o, lse
 
-    from workloads import make_fp8_inputs
-    q8, k8, v8, sq, sk, sv = make_fp8_inputs(1, 32, 4096, 128, seed=10)
-    q8, k8, v8 = q8.cuda(), k8.cuda(), v8.cuda()
-    o = torch.empty((1, 32, 4096, 128), dtype=torch.bfloat16, device="cuda")
-    lse = torch.empty((1, 32, 4096), dtype=torch.float32, device="cuda")
-    ms = _time_launches(lambda: fa.fa_fwd_fp8(q8, k8, v8, o, lse, sq, sk, sv, True, sc))
-    tf = fwd_flops(1, 32, 4096, 128, True) / (ms * 1e-3) / 1e12
-    out["fp8_llama8b_n4096_causal_fwd"] = dict(
-        ms=round(ms, 4), tflops=round(tf, 1), pct_of_fp8_peak=round(100 * tf / PEAK_FP8_TFLOPS, 1),
-        pct_of_bf16_peak=round(100 * tf / PEAK_BF16_TFLOPS, 1))
-    del q8, k8, v8, o, lse
+    if want("fp8_llama8b_n4096_causal_fwd"):
+        q8, k8, v8, sq, sk, sv = make_fp8_inputs(1, 32, 4096, 128, seed=10)
+        q8, k8, v8 = q8.cuda(), k8.cuda(), v8.cuda()
+        o = torch.empty((1, 32, 4096, 128), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((1, 32, 4096), dtype=torch.float32, device="cuda")
+        ms, mn = _time_launches(lambda: fa.fa_fwd_fp8(q8, k8, v8, o, lse, sq, sk, sv, True, sc))
+        out["fp8_llama8b_n4096_causal_fwd"] = entry(ms, mn, fwd_flops(1, 32, 4096, 128, True),
+                                                    peak=PEAK_FP8_TFLOPS)
+        del q8, k8, v8, o, lse
 
-    B, Nk = 8, 32768
-    q = make_gqa_inputs(B, H, Hkv, 1, d, seed=7)[0].cuda()
-    k, v = (t.cuda() for t in make_gqa_inputs(B, H, Hkv, Nk, d, seed=8)[1:])
-    o = torch.empty_like(q)
-    lse = torch.empty((B, H, 1), dtype=torch.float32, device="cuda")
-    nb = fa.fa_fwd_kv_workspace_size(B, H, Hkv, 1, Nk, d)
-    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
-    ms = _time_launches(lambda: fa.fa_fwd_kv(q, k, v, o, lse, ws, True, sc), reps=50)
-    nbytes = 2 * B * Hkv * Nk * d * 2 + 2 * B * H * d * 2 + B * H * 4
-    gbs = nbytes / (ms * 1e-3) / 1e9
-    out["llama8b_decode_b8_gqa32x8_nk32768"] = dict(
-        ms=round(ms, 4), algorithmic_bytes=nbytes, gbs=round(gbs, 1),
-        frac_of_hbm_peak=round(gbs / PEAK_HBM_GBS, 4), workspace_bytes=nb)
-    del q, k, v, o, lse, ws
+    if want("llama8b_decode_b8_gqa32x8_nk32768"):
+        Bd, Nk = 8, 32768
+        q = make_gqa_inputs(Bd, H, Hkv, 1, d, seed=7)[0].cuda()
+        k, v = (t.cuda() for t in make_gqa_inputs(Bd, H, Hkv, Nk, d, seed=8)[1:])
+        o = torch.empty_like(q)
+        lse = torch.empty((Bd, H, 1), dtype=torch.float32, device="cuda")
+        nb = fa.fa_fwd_kv_workspace_size(Bd, H, Hkv, 1, Nk, d)
+        ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
+        ms, mn = _time_launches(lambda: fa.fa_fwd_kv(q, k, v, o, lse, ws, True, sc),
+                                per_repeat=20)
+        nbytes = 2 * Bd * Hkv * Nk * d * 2 + 2 * Bd * H * d * 2 + Bd * H * 4
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out["llama8b_decode_b8_gqa32x8_nk32768"] = dict(
+            ms=round(ms, 5), ms_min=round(mn, 5), algorithmic_bytes=nbytes, gbs=round(gbs, 1),
+            frac_of_hbm_peak=round(gbs / PEAK_HBM_GBS, 4), workspace_bytes=nb)
+        del q, k, v, o, lse, ws
     torch.cuda.empty_cache()
     return out
 
@@ -308,23 +403,72 @@ def run_cpu_baseline(budget_s: float):
                 host_logical_cpus=os.cpu_count())
 
 
+def run_cpu_sweep(budget_s: float, rows: int = 256, only: str = None):
+    """The float64 oracle timed beside each forward shape: query rows of head
+    (0, 0), ``rows`` at a time spread evenly over the sequence, until
+    ``budget_s`` of wall time per shape; counted FLOP pro rata (each row of a
+    causal head counts 2*N*d, of a non-causal one 4*N*d, the convention's
+    average), so the figure scales to the whole workload."""
+    import numpy as np
+    from oracle import naive_fwd_rows
+    from workloads import WORKLOADS, workload_inputs
+
+    out = {}
+    for key, name, causal in SWEEP:
+        if only is not None and key != only:
+            continue
+        w = WORKLOADS[name]
+        q, k, v = workload_inputs(w, with_do=False)
+        qq = q[0, 0].float().numpy().astype(np.float64)
+        kk = k[0, 0].float().numpy().astype(np.float64)
+        vv = v[0, 0].float().numpy().astype(np.float64)
+        r = min(rows, w.N)
+        done = 0
+        start = 0
+        t0 = time.perf_counter()
+        while True:
+            pos = (np.arange(r) * (w.N // r) + start) % w.N
+            naive_fwd_rows(qq[pos], kk, vv, w.scale, causal, pos)
+            done += r
+            start += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        dt = time.perf_counter() - t0
+        flops = fwd_flops(1, 1, w.N, w.d, causal) * done / w.N
+        out[key] = dict(value=round(flops / dt / 1e12, 6), unit="TFLOP/s",
+                        cores=_blas_threads(), kind="oracle",
+                        sample=f"{done} query rows of head (0, 0) of {w.name} "
+                               f"({'causal' if causal else 'non-causal'}), float64, "
+                               f"{dt:.1f} s wall; counted FLOP pro rata")
+    return out
+
+
 # ---------------------------------------------------------------------------
 # traffic (rocprofv3 counters) bookkeeping
 # ---------------------------------------------------------------------------
 
-def load_traffic(kernel_name: str):
+def _load_traffic_file():
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
-        return None
-    if t.get("kernel") != kernel_name or t.get("source_hash") != source_hash(kernel_name):
-        return None
-    return t.get("bytes_per_launch")
+        return {"entries": []}
+    return t if isinstance(t, dict) and "entries" in t else {"entries": []}
+
+
+def load_traffic(kernel: str, workload: str):
+    """Counter-derived HBM bytes per launch of ``kernel`` on ``workload``, or
+    None when none were taken or the kernel's sources changed since."""
+    for e in _load_traffic_file()["entries"]:
+        if e.get("kernel") == kernel and e.get("workload") == workload:
+            if e.get("source_hash") != source_hash(kernel):
+                return None
+            return e.get("bytes_per_launch")
+    return None
 
 
 def _read_counter_csv(path, counter):
-    """{kernel-name-substring -> list of per-dispatch values} from a rocprofv3
+    """{kernel name -> list of per-dispatch values} from a rocprofv3
     counter_collection.csv."""
     rows = {}
     with open(path) as f:
@@ -335,7 +479,8 @@ def _read_counter_csv(path, counter):
     return rows
 
 
-def pmc_summary(fetch_csv: str, write_csv: str, copy_mib: float) -> dict:
+def pmc_summary(fetch_csv: str, write_csv: str, copy_mib: float, kernel: str,
+                workload: str, algorithmic_bytes: float = None) -> dict:
     fetch = _read_counter_csv(fetch_csv, "FETCH_SIZE")
     write = _read_counter_csv(write_csv, "WRITE_SIZE")
 
@@ -343,27 +488,35 @@ def pmc_summary(fetch_csv: str, write_csv: str, copy_mib: float) -> dict:
         ks = [k for k in table if needle in k]
         if not ks:
             raise SystemExit(f"no kernel matching {needle!r} in counters")
-        vals = table[ks[0]]
-        return ks[0], sum(vals) / len(vals)
+        vals = [x for k in ks for x in table[k]]
+        return ks[0], sum(vals) / len(vals), len(vals)
 
     copy_bytes = copy_mib * 2 ** 20
-    _, cf = pick(fetch, "copy")           # KiB read by the copy kernel
-    _, cw = pick(write, "copy")
+    _, cf, _ = pick(fetch, "copy")           # KiB read by the copy kernel
+    _, cw, _ = pick(write, "copy")
     f_scale = copy_bytes / (cf * 1024.0)
     w_scale = copy_bytes / (cw * 1024.0)
-    name, kf = pick(fetch, "bwd_main_kernel")
-    _, kw = pick(write, "bwd_main_kernel")
+    name, kf, nd = pick(fetch, kernel)
+    _, kw, _ = pick(write, kernel)
     bytes_per_launch = kf * 1024.0 * f_scale + kw * 1024.0 * w_scale
-    out = dict(kernel="bwd_main_kernel", kernel_symbol=name,
-               source_hash=source_hash("bwd_main_kernel"),
+    ent = dict(kernel=kernel, workload=workload, kernel_symbol=name,
+               source_hash=source_hash(kernel), dispatches=nd,
                fetch_kib_raw=kf, write_kib_raw=kw, copy_mib=copy_mib,
                copy_fetch_kib_raw=cf, copy_write_kib_raw=cw,
                fetch_scale=f_scale, write_scale=w_scale,
+               fetch_bytes=kf * 1024.0 * f_scale, write_bytes=kw * 1024.0 * w_scale,
                bytes_per_launch=bytes_per_launch)
+    if algorithmic_bytes:
+        ent["algorithmic_bytes"] = algorithmic_bytes
+        ent["traffic_over_algorithmic"] = bytes_per_launch / algorithmic_bytes
+    t = _load_traffic_file()
+    t["entries"] = [e for e in t["entries"]
+                    if not (e.get("kernel") == kernel and e.get("workload") == workload)]
+    t["entries"].append(ent)
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as f:
-        json.dump(out, f, indent=1)
-    return out
+        json.dump(t, f, indent=1)
+    return ent
 
 
 def copy_calibration(mib: float):
@@ -377,22 +530,50 @@ def copy_calibration(mib: float):
     return dict(copy_mib=mib, bytes=n)
 
 
+def run_only(name: str, launches: int):
+    """A few launches of one workload, nothing else: counter runs use it so
+    each kernel's dispatches belong to one shape."""
+    import torch
+    if name == "step":
+        step, _ = make_step()
+        for _ in range(launches):
+            step()
+        torch.cuda.synchronize()
+        return dict(only=name, launches=launches)
+    if name in {k for k, _, _ in SWEEP}:
+        r = run_fwd_sweep(settle_s=0.0, min_ms=0.0, only=name)
+    else:
+        r = run_extra_sweep(only=name)
+        if not r:
+            raise SystemExit(f"unknown workload {name!r}")
+    return dict(only=name, result=r)
+
+
 # ---------------------------------------------------------------------------
 
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__,
                                  formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    # The clock settles only after ~0.1 s of sustained matrix-core load, so the
-    # default warm-up is long enough to time the steady state.
-    ap.add_argument("--warmup", type=int, default=400)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--settle-s", type=float, default=0.5,
+                    help="seconds of untimed steps before the counted warm-up")
+    ap.add_argument("--min-timed-ms", type=float, default=250.0,
+                    help="GPU time the timed repeats must cover")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="wall-time budget of the oracle CPU baseline")
+    ap.add_argument("--cpu-sweep-seconds", type=float, default=2.0,
+                    help="wall-time budget of the oracle beside each forward shape")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--only", default=None, metavar="NAME")
+    ap.add_argument("--launches", type=int, default=5)
     ap.add_argument("--copy-calibration", type=float, default=None, metavar="MIB")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--kernel", default="bwd_main_kernel")
+    ap.add_argument("--workload", default=STEP_WORKLOAD)
+    ap.add_argument("--algorithmic-bytes", type=float, default=None)
     ap.add_argument("--copy-mib", type=float, default=256.0)
     args = ap.parse_args(argv)
 
@@ -405,7 +586,8 @@ def main(argv=None):
 
     if args.pmc_summary:
         print(json.dumps(pmc_summary(args.pmc_summary[0], args.pmc_summary[1],
-                                     args.copy_mib)))
+                                     args.copy_mib, args.kernel, args.workload,
+                                     args.algorithmic_bytes)))
         return 0
 
     import torch
@@ -414,22 +596,22 @@ def main(argv=None):
         return 1
     if args.copy_calibration:
         print(json.dumps(copy_calibration(args.copy_calibration)), flush=True)
+    if args.only:
+        print(json.dumps(run_only(args.only, args.launches)), flush=True)
+        return 0
 
-    r = run_step_bench(args.steps, args.warmup)
+    r = run_step_bench(args.steps, args.warmup, args.settle_s, args.min_timed_ms)
     w = r["workload"]
     ms = r["ms_per_step"]
     value = r["step_flops"] / (ms * 1e-3) / 1e12
+    km = r["kernel_ms"]
 
     # dominant kernel of the step: the longer of the forward and backward main kernels
-    if r["main_ms"] >= r["fwd_ms"]:
-        kname, kms, kflops = "bwd_main_kernel", r["main_ms"], r["bwd_flops"]
+    if km["main"] >= km["fwd"]:
+        roofline = _roofline_mfma(r["bwd_flops"], km["main"], "bwd_main_kernel", STEP_WORKLOAD)
     else:
-        kname, kms, kflops = "fwd_bf16_kernel", r["fwd_ms"], r["fwd_flops"]
-    achieved = kflops / (kms * 1e-3) / 1e12
-    roofline = dict(bound="mfma", achieved=round(achieved, 1), peak=PEAK_BF16_TFLOPS,
-                    unit="TFLOP/s", frac=round(achieved / PEAK_BF16_TFLOPS, 4),
-                    traffic=load_traffic(kname), kernel=kname,
-                    kernel_ms=round(kms, 5))
+        roofline = _roofline_mfma(r["fwd_flops"], km["fwd"], "fwd_bf16_kernel", STEP_WORKLOAD)
+    roofline["algorithmic_bytes_whole_backward"] = bwd_algorithmic_bytes(w.B, w.H, w.N, w.d)
 
     line = dict(
         metric=METRIC, value=round(value, 2), unit="TFLOP/s", n_gpus=1,
@@ -438,11 +620,18 @@ def main(argv=None):
         data="synthetic",
         config=dict(workload=w.name, B=w.B, H=w.H, N=w.N, d=w.d, causal=True,
                     step="fa_fwd + fa_bwd (preprocess, main, finalize)",
-                    pct_of_bf16_peak=round(100 * value / PEAK_BF16_TFLOPS, 2),
-                    fwd_ms=round(r["fwd_ms"], 5), bwd_main_ms=round(r["main_ms"], 5),
-                    kernel_timing="HIP events around each kernel in a second pass of the "
-                                  "same steps (the timed steps carry no events)",
-                    instrumented_ms_per_step=round(r["instrumented_ms_per_step"], 5)),
+                    pct_of_bf16_peak=round(100 * value / PEAK_BF16_TFLOPS, 2)),
+        timing=dict(settle_s=r["settle_s"], settle_steps=r["settle_steps"],
+                    repeats=r["repeats"], steps_per_repeat=args.steps,
+                    timed_ms=round(r["timed_ms"], 2),
+                    ms_per_step_median=round(ms, 5), ms_per_step_min=round(r["ms_min"], 5),
+                    ms_per_step_mean=round(r["ms_mean"], 5),
+                    value_at_min=round(r["step_flops"] / (r["ms_min"] * 1e-3) / 1e12, 2),
+                    instrumented_ms_per_step=round(r["instrumented_ms_per_step"], 5),
+                    kernel_ms_median={k: round(v, 5) for k, v in km.items()},
+                    kernel_timing="HIP events around each kernel on its launch stream, in "
+                                  "a second pass of the same repeats (the timed steps "
+                                  "carry no events)"),
         roofline=roofline,
     )
     if not args.no_sweep:
@@ -450,6 +639,10 @@ def main(argv=None):
         line["extra_sweep"] = run_extra_sweep()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = run_cpu_baseline(args.cpu_seconds)
+        if not args.no_sweep:
+            cs = run_cpu_sweep(args.cpu_sweep_seconds)
+            for key, ent in cs.items():
+                line["fwd_sweep"][key]["cpu_baseline"] = ent
     print(json.dumps(line), flush=True)
     return 0
 

@@ -61,7 +61,9 @@ class FAError(RuntimeError):
 
 
 def library_path() -> str:
-    return os.path.join(_PKG, "libfa.so")
+    """The in-tree libfa.so, or the library named by the FA_LIBRARY
+    environment variable (e.g. the host-only sanitizer build of the C ABI)."""
+    return os.environ.get("FA_LIBRARY") or os.path.join(_PKG, "libfa.so")
 
 
 def load_library():

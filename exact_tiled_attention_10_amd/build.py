@@ -18,7 +18,11 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfa.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_api.cpp"]
+SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_device.hip", "fa_plan.cpp", "fa_api.cpp"]
+# host-only sources of the sanitizer build (no device code; fa_host_stub.cpp
+# stands in for the launchers)
+ASAN_SOURCES = ["fa_api.cpp", "fa_plan.cpp", "fa_host_stub.cpp"]
+ASAN_LIB = os.path.join(BUILD_DIR, "libfa_asan.so")
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -77,5 +81,32 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_host_asan(verbose: bool = False) -> str:
+    """Build the C ABI layer alone (argument checks, size queries, plans) as
+    a host library under AddressSanitizer and UBSan, with the kernel
+    launchers stubbed out: for exercising the boundary on a CPU-only machine.
+    Returns the library's path; load it with the ASan runtime preloaded."""
+    gxx = shutil.which("g++")
+    if gxx is None:
+        raise RuntimeError("g++ not found; the sanitizer build needs it")
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    tmp = ASAN_LIB + ".tmp"
+    cmd = [gxx, "-std=c++17", "-O1", "-g", "-fPIC", "-shared",
+           "-fsanitize=address,undefined", "-fno-omit-frame-pointer",
+           "-fno-sanitize-recover=undefined", "-D__HIP_PLATFORM_AMD__",
+           "-I", "/opt/rocm/include", "-I", INCLUDE, "-I", CSRC,
+           *[os.path.join(CSRC, s) for s in ASAN_SOURCES], "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"sanitizer build failed:\n{r.stdout}")
+    os.replace(tmp, ASAN_LIB)
+    return ASAN_LIB
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--asan" in sys.argv:
+        print(build_host_asan(verbose="-v" in sys.argv))
+    else:
+        print(build(verbose="-v" in sys.argv))

@@ -1,7 +1,10 @@
 // C ABI of libfa.so: argument validation, then the kernel launchers.
 //
-// Every check runs before any HIP call, so a rejected call never touches the
-// device or the stream (and can be exercised on a machine without a GPU).
+// Every check runs before any work is enqueued, so a rejected call never
+// touches the stream or device memory (and can be exercised on a machine
+// without a GPU).  The only HIP calls a call makes before its checks pass are
+// reads of the current device and its compute-unit count, which size the
+// launch plans and workspaces.
 #include "fa.h"
 
 #include <limits.h>
@@ -83,8 +86,33 @@ int fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, i
   const Range in[3] = {range_of(q, tb), range_of(k, kvb), range_of(v, kvb)};
   const Range out[2] = {range_of(o, tb), range_of(lse, re * 4)};
   if (any_alias(in, 3, out, 2)) return FA_ERR_ALIAS;
-  return from_hip(
-      fa::launch_fwd_bf16(q, k, v, o, lse, B * H, N, d, H / Hkv, causal != 0, scale, stream));
+  const fa::FwdPlan pl = fa::fwd_plan(B * H, H / Hkv, N, N, d, false, fa::device_cus());
+  return from_hip(fa::launch_fwd_bf16_kv(q, k, v, o, lse, nullptr, B * H, N, N, d, H / Hkv,
+                                         causal != 0, scale, pl, stream));
+}
+
+// The three backward stages on validated arguments.  hsplit > 1 needs the
+// split partials after the plain workspace (grouped-query heads only).
+int bwd_launch(const void* q, const void* k, const void* v, const void* o, const void* dout,
+               const float* lse, void* dq, void* dk, void* dv, void* workspace, int B, int H,
+               int Hkv, int Nq, int Nk, int d, int hsplit, int causal, float scale,
+               hipStream_t stream) {
+  const bool has_q = (size_t)B * H * Nq > 0;
+  const size_t kve = H > 0 ? (size_t)B * (size_t)Hkv * (size_t)Nk * (size_t)d : 0;
+  const int BH = B * H;
+  hipError_t e = hipSuccess;
+  if (has_q) e = fa::launch_bwd_pre(o, dout, lse, workspace, BH, Nq, d, stream);
+  if (e == hipSuccess && kve > 0) {
+    if (has_q)
+      e = fa::launch_bwd_main(q, k, v, dout, dk, dv, workspace, BH, Nq, Nk, d, H / Hkv, hsplit,
+                              causal != 0, scale, stream);
+    else   // no queries: every key's gradient is 0
+      e = fa::launch_zero_bf16(dk, dv, kve, stream);
+  }
+  if (e == hipSuccess && has_q)
+    e = fa::launch_bwd_finalize(q, k, v, dout, dq, workspace, BH, Nq, Nk, d, H / Hkv,
+                                causal != 0, scale, stream);
+  return from_hip(e);
 }
 
 int bwd_bf16(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -110,7 +138,10 @@ int bwd_bf16(const void* q, const void* k, const void* v, const void* o, const v
   size_t need = fa::bwd_workspace_bytes(B * H, Nq, d);
   if (workspace_bytes < need) return FA_ERR_WORKSPACE;
   // a larger workspace lets grouped-query heads split over more workgroups
-  int hsplit = has_q && has_k ? fa::bwd_head_split(B * Hkv, H / Hkv, Nq, Nk, d, causal != 0) : 1;
+  int hsplit = has_q && has_k && H != Hkv
+                   ? fa::bwd_head_split(B * Hkv, H / Hkv, Nq, Nk, d, causal != 0,
+                                        fa::device_cus())
+                   : 1;
   if (hsplit > 1) {
     const size_t full = need + fa::bwd_split_bytes(B * Hkv, Nk, d, hsplit);
     if (workspace_bytes >= full)
@@ -124,20 +155,8 @@ int bwd_bf16(const void* q, const void* k, const void* v, const void* o, const v
   const Range out[4] = {range_of(dq, tb), range_of(dk, kvb), range_of(dv, kvb),
                         range_of(workspace, need)};
   if (any_alias(in, 6, out, 4)) return FA_ERR_ALIAS;
-  const int BH = B * H;
-  hipError_t e = hipSuccess;
-  if (has_q) e = fa::launch_bwd_pre(o, dout, lse, workspace, BH, Nq, d, stream);
-  if (e == hipSuccess && has_k) {
-    if (has_q)
-      e = fa::launch_bwd_main(q, k, v, dout, dk, dv, workspace, BH, Nq, Nk, d, H / Hkv, hsplit,
-                              causal != 0, scale, stream);
-    else   // no queries: every key's gradient is 0
-      e = fa::launch_zero_bf16(dk, dv, kve, stream);
-  }
-  if (e == hipSuccess && has_q)
-    e = fa::launch_bwd_finalize(q, k, v, dout, dq, workspace, BH, Nq, Nk, d, H / Hkv,
-                                causal != 0, scale, stream);
-  return from_hip(e);
+  return bwd_launch(q, k, v, o, dout, lse, dq, dk, dv, workspace, B, H, Hkv, Nq, Nk, d, hsplit,
+                    causal, scale, stream);
 }
 
 // Nq query rows against Nk keys: sizes of q / o ([B, H, Nq, d]), k / v
@@ -164,7 +183,7 @@ size_t fa_fwd_kv_workspace_size(int B, int H, int Hkv, int Nq, int Nk, int d) {
   size_t te = 0, re = 0;
   if (check_common(B, H, Nq, d, 1.f, &te, &re, true) != FA_OK) return 0;
   if (Nk < 0 || Nk > FA_MAX_N || re == 0 || check_heads(H, Hkv) != FA_OK) return 0;
-  return fa::fwd_workspace_bytes(B * H, H / Hkv, Nq, Nk, d);
+  return fa::fwd_workspace_bytes(B * H, H / Hkv, Nq, Nk, d, fa::device_cus());
 }
 
 int fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
@@ -178,15 +197,17 @@ int fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse, 
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(lse) ||
       misaligned(workspace))
     return FA_ERR_ALIGN;
-  const size_t need = fa::fwd_workspace_bytes(B * H, H / Hkv, Nq, Nk, d);
+  const int cus = fa::device_cus();
+  const size_t need = fa::fwd_workspace_bytes(B * H, H / Hkv, Nq, Nk, d, cus);
   if (need > 0 && workspace_bytes < need) return FA_ERR_WORKSPACE;
   if (need > 0 && !workspace) return FA_ERR_NULL;
   const Range in[3] = {range_of(q, qe * 2), range_of(k, kve * 2), range_of(v, kve * 2)};
   const Range out[3] = {range_of(o, qe * 2), range_of(lse, re * 4),
                         range_of(workspace, need)};
   if (any_alias(in, 3, out, 3)) return FA_ERR_ALIAS;
+  const fa::FwdPlan pl = fa::fwd_plan(B * H, H / Hkv, Nq, Nk, d, need > 0, cus);
   return from_hip(fa::launch_fwd_bf16_kv(q, k, v, o, lse, need > 0 ? workspace : nullptr, B * H,
-                                         Nq, Nk, d, H / Hkv, causal != 0, scale, stream));
+                                         Nq, Nk, d, H / Hkv, causal != 0, scale, pl, stream));
 }
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
@@ -247,7 +268,7 @@ size_t fa_bwd_kv_workspace_size(int B, int H, int Hkv, int Nq, int Nk, int d) {
   if (check_common(B, H, Nq, d, 1.0f, &te, &re, true) != FA_OK) return 0;
   if (Nk < 0 || Nk > FA_MAX_N || check_heads(H, Hkv) != FA_OK) return 0;
   if (H == 0) return fa::bwd_workspace_bytes(0, Nq, d);
-  return fa::bwd_kv_workspace_bytes(B * H, H / Hkv, Nq, Nk, d);
+  return fa::bwd_kv_workspace_bytes(B * H, H / Hkv, Nq, Nk, d, fa::device_cus());
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -349,7 +370,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_ALIAS: return "an output overlaps an input or another output";
     case FA_ERR_SCALE: return "scale is not finite";
     case FA_ERR_HIP: return "HIP kernel launch failed";
-    case FA_ERR_WORKSPACE: return "backward workspace too small";
+    case FA_ERR_WORKSPACE: return "workspace too small";
     default: return "unknown status";
   }
 }

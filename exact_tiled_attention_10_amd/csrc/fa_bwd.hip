@@ -56,7 +56,7 @@ namespace fa {
 
 namespace {
 
-constexpr int kBQ = 64;  // queries per streamed block
+constexpr int kBQ = kBwdQueryBlock;  // queries per streamed block
 
 inline size_t round256(size_t b) { return (b + 255) / 256 * 256; }
 inline int pad_rows(int N) { return (N + kBQ - 1) / kBQ * kBQ; }
@@ -164,6 +164,7 @@ struct BwdCfg {
   static_assert(QDMA * THREADS * 16 == QTILE && KDMA * THREADS * 16 == KTILE, "DMA split");
   static_assert(BPW * DQW == NBLK, "dQ block split");
   static_assert(SMEM <= 160 * 1024, "LDS budget");
+  static_assert(KEYS == bwd_keys_per_tile(D), "plan geometry");
 };
 
 template <int D, bool CAUSAL>
@@ -842,12 +843,6 @@ __global__ __launch_bounds__(256, D == 128 ? 2 : 1) void bwd_dq_direct_kernel(
 
 }  // namespace
 
-size_t bwd_workspace_bytes(int BH, int N, int d) {
-  // L2 and D rows; the fp32 dQ accumulator only where dQ is accumulated by
-  // atomics (d = 64)
-  return 2 * round256((size_t)BH * pad_rows(N) * 4) + (d == 64 ? (size_t)BH * N * d * 4 : 0);
-}
-
 hipError_t launch_bwd_pre(const void* o, const void* dout, const float* lse, void* ws, int BH,
                           int N, int d, hipStream_t stream) {
   const WsLayout w = ws_layout(ws, BH, N);
@@ -867,45 +862,6 @@ hipError_t launch_bwd_pre(const void* o, const void* dout, const float* lse, voi
     hipLaunchKernelGGL(bwd_pre_kernel<64>, dim3(blocks), dim3(256), 0, stream, o16, g16, lse,
                        w.l2, w.dv, w.dq, N, Npad, prow);
   return hipGetLastError();
-}
-
-int bwd_head_split(int BHkv, int group, int Nq, int Nk, int d, bool causal) {
-  if (group < 2 || BHkv <= 0 || Nq <= 0 || Nk <= 0) return 1;
-  // Workgroups run one per compute unit, so the key-tile kernel takes about
-  // max(heaviest workgroup, total work / CUs).  Under causal masking the
-  // first key tiles see every query block and the last almost none: with
-  // few key / value heads the heaviest workgroup (all `group` heads of key
-  // tile 0) then sets the time.  Take the smallest divisor s of the group
-  // whose share (group / s heads) is no heavier than the average per CU.
-  constexpr int kCUs = 256;
-  const int keys = d == 64 ? BwdCfg<64>::KEYS : BwdCfg<128>::KEYS;
-  static_assert(BwdCfg<128>::KEYS == BwdCfg<256>::KEYS, "key tile");
-  const int nkt = (Nk + keys - 1) / keys;
-  const int nqb = (Nq + kBQ - 1) / kBQ;
-  long long sum = 0;
-  int heaviest = 0;
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int qb0 = causal ? std::max(0, kt * keys - (Nk - Nq)) / kBQ : 0;
-    const int nit = std::max(0, nqb - qb0);
-    sum += nit;
-    heaviest = std::max(heaviest, nit);
-  }
-  const long long per_cu = ((long long)BHkv * group * sum + kCUs - 1) / kCUs;
-  for (int s = 1; s < group; ++s)
-    if (group % s == 0 && (long long)(group / s) * heaviest <= per_cu) return s;
-  return group;
-}
-
-size_t bwd_split_bytes(int BHkv, int Nk, int d, int hsplit) {
-  if (hsplit <= 1) return 0;
-  return round256(2 * (size_t)hsplit * BHkv * (size_t)Nk * d * 4);
-}
-
-size_t bwd_kv_workspace_bytes(int BH, int group, int Nq, int Nk, int d) {
-  const int BHkv = BH / group;
-  const int s = std::max(bwd_head_split(BHkv, group, Nq, Nk, d, true),
-                         bwd_head_split(BHkv, group, Nq, Nk, d, false));
-  return bwd_workspace_bytes(BH, Nq, d) + bwd_split_bytes(BHkv, Nk, d, s);
 }
 
 hipError_t launch_bwd_main(const void* q, const void* k, const void* v, const void* dout,

@@ -34,14 +34,6 @@ __device__ __forceinline__ f32x16 mfma_32x32x16_bf16(const bf16x8& a,
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-//   v_mfma_f32_16x16x32_bf16: D[16x16] += A[16x32] * B[32x16]; A lane l holds
-//   row l % 16, B lane l column l % 16, both with 8 k-values chosen by
-//   (l / 16, t); D lane l, register r holds D[4*(l/16) + r][l % 16].
-__device__ __forceinline__ f32x4 mfma_16x16x32_bf16(const bf16x8& a, const bf16x8& b,
-                                                   const f32x4& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
 __device__ __forceinline__ f32x16 mfma_32x32x2_f32(float a, float b,
                                                    const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);

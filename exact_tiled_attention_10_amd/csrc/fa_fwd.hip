@@ -52,6 +52,7 @@ namespace {
 // w % 4, so every SIMD runs one wave of each group.
 constexpr int kWaves = 8;
 constexpr int kBM = 32 * kWaves;  // queries per workgroup
+static_assert(kBM == fwd_rows_per_tile(64) && kBM == fwd_rows_per_tile(128), "plan geometry");
 // The fp32 kernel keeps the 4-wave, 128-query tiling.
 constexpr int kWavesF32 = 4;
 constexpr int kBMF32 = 32 * kWavesF32;
@@ -538,6 +539,7 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(const FwdArgs a) {
 // one barrier per tile.  Workgroup: 4 waves x 32 queries = 128 queries.
 constexpr int kWaves256 = 4;
 constexpr int kBM256 = 32 * kWaves256;
+static_assert(kBM256 == fwd_rows_per_tile(256), "plan geometry");
 constexpr int kBN256 = 32;
 
 template <bool CAUSAL>
@@ -1511,53 +1513,9 @@ hipError_t launch_f32(const float* q, const float* k, const float* v, float* o, 
 
 }  // namespace
 
-// Plan of a forward launch.  Decode: when all query rows that read a key /
-// value head fit one wave (group * Nq <= 32, d = 64 or 128) the packed-rows
-// kernel runs, its keys split into ranges of at least 128 keys aiming at four
-// one-wave workgroups per CU.  Otherwise the tile kernels, whose keys are
-// split only when the query tiles alone leave the chip idle (fewer than 256
-// workgroups): ranges of at least four 64-key tiles, two workgroups per CU.
-// Splitting needs the caller's workspace (has_ws).
-FwdPlan fwd_plan(int BH, int group, int Nq, int Nk, int d, bool has_ws) {
-  FwdPlan pl{0, 1, Nk};
-  if (Nk <= 0 || BH <= 0 || Nq <= 0) return pl;
-  const int bn = 64;   // a multiple of every kernel's key tile
-  const int nkt = (Nk + bn - 1) / bn;
-  if ((d == 64 || d == 128) && (long long)group * Nq <= 32) {
-    pl.decode = 1;
-    if (!has_ws) return pl;
-    const long long heads = BH / group;
-    int ns = (int)((1024 + heads - 1) / heads);
-    ns = std::min(ns, std::max(1, Nk / 128));
-    if (ns <= 1) return pl;
-    const int tiles_per = (nkt + ns - 1) / ns;
-    pl.klen = tiles_per * bn;
-    pl.nsplit = (Nk + pl.klen - 1) / pl.klen;
-    return pl;
-  }
-  if (!has_ws) return pl;
-  const int bm = d == 256 ? kBM256 : kBM;
-  const long long tiles = (long long)BH * ((Nq + bm - 1) / bm);
-  if (tiles >= 256) return pl;
-  int ns = (int)((512 + tiles - 1) / tiles);
-  ns = std::min(ns, nkt / 4);
-  if (ns <= 1) return pl;
-  const int tiles_per = (nkt + ns - 1) / ns;
-  pl.klen = tiles_per * bn;
-  pl.nsplit = (Nk + pl.klen - 1) / pl.klen;
-  return pl;
-}
-
-size_t fwd_workspace_bytes(int BH, int group, int Nq, int Nk, int d) {
-  const FwdPlan pl = fwd_plan(BH, group, Nq, Nk, d, true);
-  if (pl.nsplit <= 1) return 0;
-  const size_t rows = (size_t)pl.nsplit * BH * Nq;
-  return (rows * d * 4 + 255) / 256 * 256 + rows * 4;
-}
-
 hipError_t launch_fwd_bf16_kv(const void* q, const void* k, const void* v, void* o, float* lse,
                               void* ws, int BH, int Nq, int Nk, int d, int group, bool causal,
-                              float scale, hipStream_t stream) {
+                              float scale, const FwdPlan& pl, hipStream_t stream) {
   FwdArgs a;
   a.Q = (const uint16_t*)q;
   a.K = (const uint16_t*)k;
@@ -1568,10 +1526,10 @@ hipError_t launch_fwd_bf16_kv(const void* q, const void* k, const void* v, void*
   a.Nq = Nq;
   a.Nk = Nk;
   a.koff = Nk - Nq;
-  a.nqt = (Nq + (d == 256 ? kBM256 : kBM) - 1) / (d == 256 ? kBM256 : kBM);
+  const int bm = fwd_rows_per_tile(d);
+  a.nqt = (Nq + bm - 1) / bm;
   a.group = group;
   split_scale(scale, &a.c, &a.negq);
-  const FwdPlan pl = fwd_plan(BH, group, Nq, Nk, d, ws != nullptr);
   a.nsplit = pl.nsplit;
   a.klen = pl.nsplit > 1 ? pl.klen : (Nk > 0 ? Nk : 1);
   a.Opart = nullptr;
@@ -1614,12 +1572,6 @@ hipError_t launch_fwd_fp8(const void* q, const void* k, const void* v, void* o, 
   a.group = 1;
   split_scale(score_scale, &a.c, &a.negq);
   return causal ? launch_fp8<true>(a, v_scale, stream) : launch_fp8<false>(a, v_scale, stream);
-}
-
-hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
-                           int BH, int N, int d, int group, bool causal, float scale,
-                           hipStream_t stream) {
-  return launch_fwd_bf16_kv(q, k, v, o, lse, nullptr, BH, N, N, d, group, causal, scale, stream);
 }
 
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,

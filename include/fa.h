@@ -34,9 +34,11 @@
  *          returns without waiting.  Faults during execution surface at the
  *          caller's next synchronisation on that stream.
  * Errors   Every call returns an int status (FA_OK == 0).  Arguments are
- *          validated before any HIP call is made, so a rejected call touches
- *          neither the device nor the stream.  B*H*N == 0 is a valid no-op.
- *          Nothing is thrown across the ABI.
+ *          validated before any work is enqueued, so a rejected call touches
+ *          neither the stream nor device memory; the only HIP calls made
+ *          before the checks pass read the current device and its compute-
+ *          unit count (which size the launch plans and workspaces).
+ *          B*H*N == 0 is a valid no-op.  Nothing is thrown across the ABI.
  * Sizes    d must be 64 or 128; the bfloat16 entry points (the forwards
  *          fa_fwd, fa_fwd_gqa, fa_fwd_kv and the backwards) also take
  *          d = 256; fa_fwd_fp8 takes 128 only.  B, H >= 0; 0 <= N <= FA_MAX_N.

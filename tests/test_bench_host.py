@@ -45,8 +45,8 @@ def _counter_csv(path, counter, rows):
 def test_pmc_summary_scales_by_the_copy(tmp_path, monkeypatch):
     """Bytes per launch = each counter's KiB scaled by what it reads for a copy
     of known size (FETCH_SIZE counting half of the copy's bytes: factor 2),
-    averaged over the kernel's dispatches; the summary is keyed by the
-    sources' hash and dropped once they differ."""
+    averaged over the kernel's dispatches; entries are keyed by kernel and
+    workload and by the sources' hash, and dropped once the sources differ."""
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic.json"))
     copy_kib = 256 * 1024
     fetch = tmp_path / "fetch.csv"
@@ -56,18 +56,38 @@ def test_pmc_summary_scales_by_the_copy(tmp_path, monkeypatch):
                                        (main, 1000.0), (main, 3000.0)])
     _counter_csv(write, "WRITE_SIZE", [("__amd_rocclr_copyBuffer", copy_kib),
                                        (main, 500.0), (main, 500.0)])
-    out = bench.pmc_summary(str(fetch), str(write), 256.0)
+    out = bench.pmc_summary(str(fetch), str(write), 256.0, "bwd_main_kernel",
+                            "train_step_n2048", algorithmic_bytes=1e6)
     assert out["fetch_scale"] == pytest.approx(2.0)
     assert out["write_scale"] == pytest.approx(1.0)
+    assert out["dispatches"] == 2
     assert out["bytes_per_launch"] == pytest.approx(2000.0 * 1024 * 2 + 500.0 * 1024)
+    assert out["traffic_over_algorithmic"] == pytest.approx(out["bytes_per_launch"] / 1e6)
+    # a second kernel / workload lands beside the first
+    fwd = "void fa::fwd_bf16_kernel<128, 64, true>(...)"
+    _counter_csv(fetch, "FETCH_SIZE", [("__amd_rocclr_copyBuffer", copy_kib / 2), (fwd, 10.0)])
+    _counter_csv(write, "WRITE_SIZE", [("__amd_rocclr_copyBuffer", copy_kib), (fwd, 4.0)])
+    bench.pmc_summary(str(fetch), str(write), 256.0, "fwd_bf16_kernel", "llama8b_n4096_causal")
     with open(bench.TRAFFIC_FILE) as fh:
         stored = json.load(fh)
-    assert stored["source_hash"] == bench.source_hash("bwd_main_kernel")
-    assert bench.load_traffic("bwd_main_kernel") == pytest.approx(out["bytes_per_launch"])
-    stored["source_hash"] = "0" * 16
+    assert len(stored["entries"]) == 2
+    assert stored["entries"][0]["source_hash"] == bench.source_hash("bwd_main_kernel")
+    assert bench.load_traffic("bwd_main_kernel", "train_step_n2048") == \
+        pytest.approx(out["bytes_per_launch"])
+    assert bench.load_traffic("fwd_bf16_kernel", "llama8b_n4096_causal") == \
+        pytest.approx(10.0 * 1024 * 2 + 4.0 * 1024)
+    assert bench.load_traffic("fwd_bf16_kernel", "train_step_n2048") is None
+    stored["entries"][0]["source_hash"] = "0" * 16
     with open(bench.TRAFFIC_FILE, "w") as fh:
         json.dump(stored, fh)
-    assert bench.load_traffic("bwd_main_kernel") is None
+    assert bench.load_traffic("bwd_main_kernel", "train_step_n2048") is None
+
+
+def test_algorithmic_bytes():
+    """Forward: Q, K, V in and O out (2 bytes each) plus a 4-byte lse per row;
+    backward: Q, K, V, O, dO, lse in and dQ, dK, dV out."""
+    assert bench.fwd_algorithmic_bytes(1, 32, 4096, 128) == 4 * 32 * 4096 * 128 * 2 + 32 * 4096 * 4
+    assert bench.bwd_algorithmic_bytes(4, 16, 2048, 64) == 8 * 64 * 2048 * 64 * 2 + 64 * 2048 * 4
 
 
 def test_more_than_one_gpu_is_refused():

@@ -24,6 +24,11 @@ from workloads import WORKLOADS, make_inputs, workload_inputs
 
 pytestmark = pytest.mark.gpu
 
+
+def _s32(x):
+    """The scale as the kernels receive it: a float32, widened for the oracle."""
+    return float(np.float32(x))
+
 TOL = 2e-2
 
 
@@ -83,7 +88,7 @@ def test_bwd_small_and_ragged(N, causal, d):
     q, k, v, do = make_inputs(1, 2, N, d, torch.bfloat16, seed=300 + N, with_do=True)
     scale = 1.0 / math.sqrt(d)
     got = _gpu_fwd_bwd(q, k, v, do, causal, scale)
-    ref = naive_bwd(_f64(q), _f64(k), _f64(v), _f64(do), scale, causal)
+    ref = naive_bwd(_f64(q), _f64(k), _f64(v), _f64(do), _s32(scale), causal)
     _compare(got, ref, f"N={N}")
 
 
@@ -92,7 +97,7 @@ def _heads(w, causal, heads, magnitude_tol=False):
     got = _gpu_fwd_bwd(q, k, v, do, causal, w.scale)
     worst = 0.0
     for (b, h) in heads:
-        ref = naive_bwd(_f64(q[b, h]), _f64(k[b, h]), _f64(v[b, h]), _f64(do[b, h]), w.scale,
+        ref = naive_bwd(_f64(q[b, h]), _f64(k[b, h]), _f64(v[b, h]), _f64(do[b, h]), _s32(w.scale),
                         causal)
         tol = ulp_tol(ref) if magnitude_tol else TOL
         errs = _compare([g[b, h] for g in got], ref, f"head ({b},{h})", tol)
@@ -100,12 +105,56 @@ def _heads(w, causal, heads, magnitude_tol=False):
     _say(f"   worst over {len(heads)} heads: {worst:.3e}")
 
 
-def test_train_step_workload_every_head():
-    """Training-step workload (4 x 16 x 2048 x 64, causal) in the bench's launch
-    configuration: every element of every head against the oracle, 2e-2."""
+_TRAIN_REF = {}
+
+
+def _train_step_reference():
+    """Oracle gradients of every head of the training-step workload (computed
+    once per session: both tests below compare against them)."""
     w = WORKLOADS["train_step_n2048"]
+    if not _TRAIN_REF:
+        q, k, v, do = workload_inputs(w, with_do=True)
+        for b in range(w.B):
+            for h in range(w.H):
+                _TRAIN_REF[(b, h)] = naive_bwd(_f64(q[b, h]), _f64(k[b, h]), _f64(v[b, h]),
+                                               _f64(do[b, h]), _s32(w.scale), True)
+    return w, _TRAIN_REF
+
+
+def test_train_step_workload_every_head():
+    """Training-step workload (4 x 16 x 2048 x 64, causal) through fa_bwd:
+    every element of every head against the oracle, 2e-2."""
+    w, ref = _train_step_reference()
     _say(f"[{w.name}]")
-    _heads(w, True, [(b, h) for b in range(w.B) for h in range(w.H)])
+    q, k, v, do = workload_inputs(w, with_do=True)
+    got = _gpu_fwd_bwd(q, k, v, do, True, w.scale)
+    worst = 0.0
+    for (b, h), r in ref.items():
+        worst = max(worst, max(_compare([g[b, h] for g in got], r, f"head ({b},{h})")))
+    _say(f"   worst over {len(ref)} heads: {worst:.3e}")
+
+
+def test_train_step_staged_sequence_the_bench_times():
+    """The exact sequence bench.py times -- fa_fwd, fa_bwd_preprocess,
+    fa_bwd_main, fa_bwd_finalize on the training-step workload, from the
+    bench's own step function -- with NaN-prefilled dQ, dK, dV and workspace
+    bytes 0xFF: every element of every head against the oracle, 2e-2.  Two
+    passes, as the bench repeats the step on the same buffers."""
+    import bench
+    w, ref = _train_step_reference()
+    step, t = bench.make_step()
+    for x in (t["dq"], t["dk"], t["dv"], t["o"], t["lse"]):
+        x.fill_(float("nan"))
+    t["ws"].fill_(0xFF)
+    for it in range(2):
+        step()
+        torch.cuda.synchronize()
+        got = (t["dq"], t["dk"], t["dv"])
+        worst = 0.0
+        for (b, h), r in ref.items():
+            worst = max(worst, max(_compare([g[b, h] for g in got], r,
+                                            f"pass {it} head ({b},{h})")))
+        _say(f"   pass {it}: worst over {len(ref)} heads: {worst:.3e}")
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -130,7 +179,7 @@ def test_bwd_unusual_scales(scale):
     q, k, v, do = make_inputs(1, 2, 150, 64, torch.bfloat16, seed=17, with_do=True)
     for causal in (False, True):
         got = _gpu_fwd_bwd(q, k, v, do, causal, scale)
-        ref = naive_bwd(_f64(q), _f64(k), _f64(v), _f64(do), scale, causal)
+        ref = naive_bwd(_f64(q), _f64(k), _f64(v), _f64(do), _s32(scale), causal)
         _compare(got, ref, f"scale={scale} causal={causal}", ulp_tol(ref))
 
 
@@ -149,7 +198,7 @@ def test_autograd_function_matches_oracle():
     qd, kd, vd = (t.cuda().requires_grad_(True) for t in (q, k, v))
     o = fa.attention(qd, kd, vd, True, 0.125)
     o.backward(do.cuda())
-    ref = naive_bwd(_f64(q), _f64(k), _f64(v), _f64(do), 0.125, True)
+    ref = naive_bwd(_f64(q), _f64(k), _f64(v), _f64(do), _s32(0.125), True)
     _compare([qd.grad, kd.grad, vd.grad], ref, "autograd")
 
 

@@ -18,6 +18,11 @@ from workloads import make_gqa_inputs, make_inputs
 
 pytestmark = pytest.mark.gpu
 
+
+def _s32(x):
+    """The scale as the kernels receive it: a float32, widened for the oracle."""
+    return float(np.float32(x))
+
 TOL = 2e-2
 TOL_LSE = 1e-3
 D = 256
@@ -54,7 +59,7 @@ def test_d256_forward(N, causal):
     scale = 1 / math.sqrt(D)
     o, lse = fa.forward(q.cuda(), k.cuda(), v.cuda(), causal, scale)
     torch.cuda.synchronize()
-    _cmp(o, lse, *naive_fwd(_f64(q), _f64(k), _f64(v), scale, causal))
+    _cmp(o, lse, *naive_fwd(_f64(q), _f64(k), _f64(v), _s32(scale), causal))
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -62,7 +67,7 @@ def test_d256_forward_gqa(causal):
     q, k, v = make_gqa_inputs(1, 8, 2, 300, D, seed=1100)
     o, lse = fa.forward(q.cuda(), k.cuda(), v.cuda(), causal, 0.07)
     torch.cuda.synchronize()
-    _cmp(o, lse, *naive_fwd_gqa(_f64(q), _f64(k), _f64(v), 0.07, causal))
+    _cmp(o, lse, *naive_fwd_gqa(_f64(q), _f64(k), _f64(v), _s32(0.07), causal))
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -73,7 +78,7 @@ def test_d256_forward_kv(nq, nk, causal):
     k, v = make_gqa_inputs(1, 4, 2, nk, D, seed=1300 + nk)[1:]
     o, lse = fa.forward(q.cuda(), k.cuda(), v.cuda(), causal, 1 / math.sqrt(D))
     torch.cuda.synchronize()
-    ro, rl = naive_fwd_kv(_f64(q), _f64(k), _f64(v), 1 / math.sqrt(D), causal)
+    ro, rl = naive_fwd_kv(_f64(q), _f64(k), _f64(v), _s32(1 / math.sqrt(D)), causal)
     live = np.isfinite(rl)
     go, gl = _f64(o), _f64(lse)
     assert np.all(go[~live] == 0) and np.all(gl[~live] == -np.inf)
@@ -95,7 +100,7 @@ def test_d256_large_sampled():
     wo = wl = 0.0
     for h in range(16):
         rows = np.unique(np.concatenate([[0, 127, 128, 4095], rng.integers(0, 4096, 12)]))
-        ro, rl = naive_fwd_rows(_f64(q[0, h, rows]), _f64(k[0, h]), _f64(v[0, h]), scale, True,
+        ro, rl = naive_fwd_rows(_f64(q[0, h, rows]), _f64(k[0, h]), _f64(v[0, h]), _s32(scale), True,
                                 rows)
         wo = max(wo, float(np.max(np.abs(go[0, h, rows] - ro))))
         wl = max(wl, float(np.max(np.abs(gl[0, h, rows] - rl))))
@@ -111,7 +116,7 @@ def _bwd_check(q, k, v, do, causal, scale):
     o, lse = fa.forward(qd, kd, vd, causal, scale)
     dq, dk, dv = fa.backward(qd, kd, vd, o, lse, dod, causal, scale)
     torch.cuda.synchronize()
-    ref = naive_bwd_kv(_f64(q), _f64(k), _f64(v), _f64(do), scale, causal)
+    ref = naive_bwd_kv(_f64(q), _f64(k), _f64(v), _f64(do), _s32(scale), causal)
     tol = max(TOL, 2.0 ** -7 * max(float(np.max(np.abs(r))) for r in ref))
     errs = [float(np.max(np.abs(_f64(g) - r))) for g, r in zip((dq, dk, dv), ref)]
     _say(f"   max|d dQ|={errs[0]:.3e} |d dK|={errs[1]:.3e} |d dV|={errs[2]:.3e} (tol {tol:.3e})")

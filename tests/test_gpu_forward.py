@@ -17,6 +17,11 @@ from workloads import WORKLOADS, make_inputs, workload_inputs
 
 pytestmark = pytest.mark.gpu
 
+
+def _s32(x):
+    """The scale as the kernels receive it: a float32, widened for the oracle."""
+    return float(np.float32(x))
+
 TOL_BF16 = 2e-2
 TOL_F32 = 1e-5
 TOL_LSE = 1e-3
@@ -64,7 +69,7 @@ def test_bf16_small_and_ragged(N, causal, d):
     q, k, v = make_inputs(2, 3, N, d, torch.bfloat16, seed=100 + N)
     scale = 1.0 / math.sqrt(d)
     o, lse = _run(q, k, v, causal, scale)
-    ro, rl = naive_fwd(_f64(q), _f64(k), _f64(v), scale, causal)
+    ro, rl = naive_fwd(_f64(q), _f64(k), _f64(v), _s32(scale), causal)
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
     eo = np.max(np.abs(o - ro))
     el = np.max(np.abs(lse - rl))
@@ -80,7 +85,7 @@ def test_f32_small_and_ragged(N, causal, d):
     q, k, v = make_inputs(1, 2, N, d, torch.float32, seed=200 + N)
     scale = 1.0 / math.sqrt(d)
     o, lse = _run(q, k, v, causal, scale)
-    ro, rl = naive_fwd(_f64(q), _f64(k), _f64(v), scale, causal)
+    ro, rl = naive_fwd(_f64(q), _f64(k), _f64(v), _s32(scale), causal)
     eo = np.max(np.abs(o - ro))
     el = np.max(np.abs(lse - rl))
     _say(f"   max|dO|={eo:.3e} max|dlse|={el:.3e}")
@@ -92,7 +97,7 @@ def test_single_head_fp32_workload_full():
     w = WORKLOADS["single_head_fp32_n256"]
     q, k, v = workload_inputs(w)
     o, lse = _run(q, k, v, False, w.scale)
-    ro, rl = naive_fwd(_f64(q), _f64(k), _f64(v), w.scale, False)
+    ro, rl = naive_fwd(_f64(q), _f64(k), _f64(v), _s32(w.scale), False)
     eo = np.max(np.abs(o - ro))
     _say(f"[{w.name}] max|dO|={eo:.3e} max|dlse|={np.max(np.abs(lse - rl)):.3e}")
     assert eo <= TOL_F32
@@ -107,7 +112,7 @@ def test_gpt2_medium_workload_full(causal):
     q, k, v = workload_inputs(w)
     _say(f"[{w.name}] causal={causal}")
     o, lse = _run(q, k, v, causal, w.scale)
-    ro, rl = naive_fwd(_f64(q), _f64(k), _f64(v), w.scale, causal)
+    ro, rl = naive_fwd(_f64(q), _f64(k), _f64(v), _s32(w.scale), causal)
     eo = np.max(np.abs(o - ro))
     el = np.max(np.abs(lse - rl))
     _say(f"   max|dO|={eo:.3e} max|dlse|={el:.3e}")
@@ -126,7 +131,7 @@ def _sampled_check(w, causal, heads, rows_per_head=48, seed=0):
             [0, 1, 63, 64, 127, 128, N - 1],
             rng.integers(0, N, size=rows_per_head)]))
         ro, rl = naive_fwd_rows(_f64(q[b, h, pos]), _f64(k[b, h]), _f64(v[b, h]),
-                                w.scale, causal, pos)
+                                _s32(w.scale), causal, pos)
         worst_o = max(worst_o, float(np.max(np.abs(o[b, h, pos] - ro))))
         worst_l = max(worst_l, float(np.max(np.abs(lse[b, h, pos] - rl))))
     _say(f"   sampled max|dO|={worst_o:.3e} max|dlse|={worst_l:.3e}")
@@ -140,6 +145,39 @@ def test_llama8b_workload_sampled():
     w = WORKLOADS["llama8b_n4096"]
     _say(f"[{w.name}]")
     _sampled_check(w, True, [(0, 0), (0, 7), (0, 19), (0, 31)])
+
+
+def _full_heads_check(w, causal, heads):
+    """Every element of the listed heads against the oracle, in the bench's
+    launch configuration (the whole workload in one call)."""
+    q, k, v = workload_inputs(w)
+    o, lse = _run(q, k, v, causal, w.scale)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    worst_o = worst_l = 0.0
+    for (b, h) in heads:
+        ro, rl = naive_fwd(_f64(q[b, h]), _f64(k[b, h]), _f64(v[b, h]), _s32(w.scale), causal)
+        eo = float(np.max(np.abs(o[b, h] - ro)))
+        el = float(np.max(np.abs(lse[b, h] - rl)))
+        _say(f"   head ({b},{h}) max|dO|={eo:.3e} max|dlse|={el:.3e}")
+        worst_o, worst_l = max(worst_o, eo), max(worst_l, el)
+    assert worst_o <= TOL_BF16 and worst_l <= TOL_LSE
+
+
+def test_llama8b_workload_full_heads_one_per_xcd():
+    """Llama-3.1-8B shape (1 x 32 x 4096 x 128, causal): every element of eight
+    whole heads, 0, 4, .., 28 -- the grid order gives XCD x the heads 4x..4x+3,
+    so these run on eight different XCDs."""
+    w = WORKLOADS["llama8b_n4096"]
+    _say(f"[{w.name}] full heads")
+    _full_heads_check(w, True, [(0, h) for h in range(0, 32, 4)])
+
+
+def test_long_context_n16384_full_head():
+    """Long-context shape (1 x 8 x 16384 x 128, causal): every element of one
+    whole head (head 5, the one XCD 5 owns)."""
+    w = WORKLOADS["long_context_n16384"]
+    _say(f"[{w.name}] full head")
+    _full_heads_check(w, True, [(0, 5)])
 
 
 @pytest.mark.parametrize("name", ["long_context_n16384", "long_context_n32768"])
@@ -214,7 +252,7 @@ def test_unusual_scales(scale):
     q, k, v = make_inputs(1, 2, 200, 64, torch.bfloat16, seed=13)
     for causal in (False, True):
         o, lse = _run(q, k, v, causal, scale)
-        ro, rl = naive_fwd(_f64(q), _f64(k), _f64(v), scale, causal)
+        ro, rl = naive_fwd(_f64(q), _f64(k), _f64(v), _s32(scale), causal)
         assert np.max(np.abs(o - ro)) <= TOL_BF16
         assert np.max(np.abs(lse - rl)) <= TOL_LSE
 

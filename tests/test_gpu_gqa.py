@@ -22,6 +22,11 @@ from workloads import make_gqa_inputs
 
 pytestmark = pytest.mark.gpu
 
+
+def _s32(x):
+    """The scale as the kernels receive it: a float32, widened for the oracle."""
+    return float(np.float32(x))
+
 TOL = 2e-2
 TOL_LSE = 1e-3
 
@@ -63,7 +68,7 @@ def test_gqa_forward(H, Hkv, N, causal, d):
     q, k, v = make_gqa_inputs(2, H, Hkv, N, d, seed=300 + N + H + Hkv)
     scale = 1.0 / math.sqrt(d)
     o, lse = _fwd(q, k, v, causal, scale)
-    ro, rl = naive_fwd_gqa(_f64(q), _f64(k), _f64(v), scale, causal)
+    ro, rl = naive_fwd_gqa(_f64(q), _f64(k), _f64(v), _s32(scale), causal)
     eo = float(np.max(np.abs(_f64(o) - ro)))
     el = float(np.max(np.abs(_f64(lse) - rl)))
     _say(f"   max|dO|={eo:.3e} max|dlse|={el:.3e}")
@@ -101,7 +106,7 @@ def test_gqa_backward(H, Hkv, N, causal, d, split):
     scale = 1.0 / math.sqrt(d)
     o, lse = _fwd(q, k, v, causal, scale)
     dq, dk, dv = _bwd(q, k, v, do, o, lse, causal, scale, split)
-    ref = naive_bwd_gqa(_f64(q), _f64(k), _f64(v), _f64(do), scale, causal)
+    ref = naive_bwd_gqa(_f64(q), _f64(k), _f64(v), _f64(do), _s32(scale), causal)
     tol = max(TOL, 2.0 ** -7 * max(float(np.max(np.abs(r))) for r in ref))
     errs = [float(np.max(np.abs(_f64(g) - r))) for g, r in zip((dq, dk, dv), ref)]
     _say(f"   max|d dQ|={errs[0]:.3e} |d dK|={errs[1]:.3e} |d dV|={errs[2]:.3e} (tol {tol:.3e})")
@@ -138,7 +143,7 @@ def test_llama8b_gqa_shape_sampled():
         g = h // (H // Hkv)
         rows = np.unique(np.concatenate([[0, 1, 255, 256, N - 1],
                                          rng.integers(0, N, 24)]))
-        ro, rl = naive_fwd_rows(_f64(q[0, h, rows]), _f64(k[0, g]), _f64(v[0, g]), scale,
+        ro, rl = naive_fwd_rows(_f64(q[0, h, rows]), _f64(k[0, g]), _f64(v[0, g]), _s32(scale),
                                 True, rows)
         worst_o = max(worst_o, float(np.max(np.abs(o[0, h, rows] - ro))))
         worst_l = max(worst_l, float(np.max(np.abs(lse[0, h, rows] - rl))))
@@ -174,7 +179,7 @@ def test_llama8b_gqa_backward():
              f"worst excess over the bound {excess:.3e}")
         assert excess <= 0
     ref = naive_bwd_gqa(_f64(q[:, 28:]), _f64(k[:, 7:]), _f64(v[:, 7:]), _f64(do[:, 28:]),
-                        scale, True)
+                        _s32(scale), True)
     tol = max(TOL, 2.0 ** -7 * max(float(np.max(np.abs(r))) for r in ref))
     errs = [float(np.max(np.abs(_f64(g) - r)))
             for g, r in zip((got[0][:, 28:], got[1][:, 7:], got[2][:, 7:]), ref)]

@@ -21,6 +21,11 @@ from workloads import make_gqa_inputs
 
 pytestmark = pytest.mark.gpu
 
+
+def _s32(x):
+    """The scale as the kernels receive it: a float32, widened for the oracle."""
+    return float(np.float32(x))
+
 TOL = 2e-2
 TOL_LSE = 1e-3
 
@@ -63,7 +68,7 @@ def _run(q, k, v, causal, scale, use_ws=True):
 
 
 def _check(q, k, v, causal, scale, o, lse):
-    ro, rl = naive_fwd_kv(_f64(q), _f64(k), _f64(v), scale, causal)
+    ro, rl = naive_fwd_kv(_f64(q), _f64(k), _f64(v), _s32(scale), causal)
     go, gl = _f64(o), _f64(lse)
     live = visible_mask_kv(q.shape[2], k.shape[2], causal).any(axis=1)
     assert np.all(go[..., ~live, :] == 0) and np.all(gl[..., ~live] == -np.inf)
@@ -157,7 +162,7 @@ def _bwd(q, k, v, do, causal, scale):
 
 def _check_grads(q, k, v, do, causal, scale, got):
     from oracle import naive_bwd_kv
-    ref = naive_bwd_kv(_f64(q), _f64(k), _f64(v), _f64(do), scale, causal)
+    ref = naive_bwd_kv(_f64(q), _f64(k), _f64(v), _f64(do), _s32(scale), causal)
     # one bf16 ulp of the largest reference magnitude, never below 2e-2 (the
     # summed gradients of shared key/value heads can pass O(1))
     tol = max(TOL, 2.0 ** -7 * max(float(np.max(np.abs(r))) if r.size else 0.0 for r in ref))
