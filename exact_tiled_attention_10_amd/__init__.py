@@ -31,10 +31,12 @@ __all__ = [
     "fa_fwd_f32",
     "fa_bwd", "fa_bwd_gqa", "fa_bwd_kv", "fa_bwd_workspace_size", "fa_bwd_kv_workspace_size",
     "fa_status_string",
-    "fa_bwd_preprocess", "fa_bwd_main", "fa_bwd_finalize",
+    "fa_bwd_preprocess", "fa_bwd_main", "fa_bwd_finalize", "fa_bwd_noalloc",
+    "FA_STATIC_SCRATCH_BYTES",
     "forward", "backward", "attention",
     "FA_OK", "FA_ERR_NULL", "FA_ERR_SHAPE", "FA_ERR_HEADDIM", "FA_ERR_ALIGN",
-    "FA_ERR_ALIAS", "FA_ERR_SCALE", "FA_ERR_HIP", "FA_ERR_WORKSPACE", "FA_MAX_N",
+    "FA_ERR_ALIAS", "FA_ERR_SCALE", "FA_ERR_HIP", "FA_ERR_WORKSPACE", "FA_ERR_SCRATCH",
+    "FA_MAX_N",
 ]
 
 FA_OK = 0
@@ -46,7 +48,9 @@ FA_ERR_ALIAS = 5
 FA_ERR_SCALE = 6
 FA_ERR_HIP = 7
 FA_ERR_WORKSPACE = 8
+FA_ERR_SCRATCH = 9
 FA_MAX_N = 1 << 22
+FA_STATIC_SCRATCH_BYTES = 64 << 20
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -104,6 +108,8 @@ def load_library():
     lib.fa_bwd_kv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
                               i, i, i, i, i, i, i, f, vp]
     lib.fa_bwd_kv.restype = i
+    lib.fa_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
+    lib.fa_bwd_noalloc.restype = i
     lib.fa_bwd_preprocess.argtypes = [vp, vp, vp, vp, ctypes.c_size_t, i, i, i, i, vp]
     lib.fa_bwd_preprocess.restype = i
     lib.fa_bwd_main.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
@@ -334,6 +340,24 @@ def fa_bwd_kv(q, k, v, o, dout, lse, dq, dk, dv, workspace, causal: bool, scale:
                                   B, H, Hkv, Nq, Nk, d, int(bool(causal)), float(scale),
                                   _stream_handle(q.device, stream))
     _raise(st, "fa_bwd_kv")
+
+
+def fa_bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, causal: bool, scale: float,
+                   stream=None) -> None:
+    """bf16 backward into preallocated ``dq``, ``dk``, ``dv`` with no workspace
+    argument: the library's static per-GPU scratch (FA_STATIC_SCRATCH_BYTES)
+    stands in for it, so the call allocates nothing.  Calls that overlap on
+    one GPU race on that buffer."""
+    B, H, N, d = _dims(q)
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout"), (dq, "dq"),
+                  (dk, "dk"), (dv, "dv")):
+        _check(t, nm, (B, H, N, d), torch.bfloat16, q.device)
+    _check(lse, "lse", (B, H, N), torch.float32, q.device)
+    st = load_library().fa_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout),
+                                       _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d,
+                                       int(bool(causal)), float(scale),
+                                       _stream_handle(q.device, stream))
+    _raise(st, "fa_bwd_noalloc")
 
 
 def _ws_bytes(workspace, device):

@@ -13,6 +13,8 @@
 
 #include "fa_internal.h"
 
+static_assert(FA_STATIC_SCRATCH_BYTES == fa::kStaticScratchBytes, "scratch size");
+
 namespace {
 
 struct Range {
@@ -295,6 +297,29 @@ int fa_bwd_kv(const void* q, const void* k, const void* v, const void* o, const 
                   Nk, d, causal, scale, stream);
 }
 
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                   const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+                   int causal, float scale, hipStream_t stream) {
+  size_t te = 0, re = 0;
+  int st = check_common(B, H, N, d, scale, &te, &re, true);
+  if (st != FA_OK) return st;
+  if (re == 0) return FA_OK;
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_NULL;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(dout) ||
+      misaligned(lse) || misaligned(dq) || misaligned(dk) || misaligned(dv))
+    return FA_ERR_ALIGN;
+  if (fa::bwd_workspace_bytes(B * H, N, d) > fa::kStaticScratchBytes) return FA_ERR_SCRATCH;
+  const size_t tb = te * 2;
+  const Range in[6] = {range_of(q, tb), range_of(k, tb),    range_of(v, tb),
+                       range_of(o, tb), range_of(dout, tb), range_of(lse, re * 4)};
+  const Range out[3] = {range_of(dq, tb), range_of(dk, tb), range_of(dv, tb)};
+  if (any_alias(in, 6, out, 3)) return FA_ERR_ALIAS;
+  void* scratch = nullptr;
+  if (fa::static_scratch(&scratch) != hipSuccess) return FA_ERR_HIP;
+  return bwd_launch(q, k, v, o, dout, lse, dq, dk, dv, scratch, B, H, H, N, N, d, 1, causal,
+                    scale, stream);
+}
+
 int fa_bwd_preprocess(const void* o, const void* dout, const float* lse, void* workspace,
                       size_t workspace_bytes, int B, int H, int N, int d, hipStream_t stream) {
   size_t te = 0, re = 0;
@@ -371,6 +396,9 @@ const char* fa_status_string(int status) {
     case FA_ERR_SCALE: return "scale is not finite";
     case FA_ERR_HIP: return "HIP kernel launch failed";
     case FA_ERR_WORKSPACE: return "workspace too small";
+    case FA_ERR_SCRATCH:
+      return "problem needs more scratch than the library's static buffer holds "
+             "(fa_bwd_noalloc: at most FA_STATIC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }

@@ -9,6 +9,11 @@ namespace fa {
 
 int device_cus() { return 256; }
 
+hipError_t static_scratch(void** ptr) {
+  *ptr = nullptr;
+  return hipErrorNotSupported;
+}
+
 hipError_t launch_fwd_bf16_kv(const void*, const void*, const void*, void*, float*, void*, int,
                               int, int, int, int, bool, float, const FwdPlan&, hipStream_t) {
   return hipErrorNotSupported;

@@ -32,6 +32,13 @@ constexpr int bwd_keys_per_tile(int d) { return d == 64 ? 256 : 128; }
 // count, when no device can be queried, e.g. on a host without a GPU).
 int device_cus();
 
+// The no-allocation backward's scratch: a static device array of
+// kStaticScratchBytes per device.  Writes the current device's address of it
+// to *ptr (looked up with hipGetSymbolAddress once per device, with that
+// device current).
+constexpr size_t kStaticScratchBytes = (size_t)64 << 20;
+hipError_t static_scratch(void** ptr);
+
 // ---------------------------------------------------------------------------
 // plans (fa_plan.cpp)
 // ---------------------------------------------------------------------------

@@ -65,7 +65,9 @@ enum {
   FA_ERR_ALIAS = 5,     /* an output overlaps an input or another output      */
   FA_ERR_SCALE = 6,     /* scale is NaN or infinite                           */
   FA_ERR_HIP = 7,       /* a kernel launch was rejected by the HIP runtime    */
-  FA_ERR_WORKSPACE = 8  /* backward workspace smaller than required           */
+  FA_ERR_WORKSPACE = 8, /* workspace smaller than required                    */
+  FA_ERR_SCRATCH = 9    /* fa_bwd_noalloc: the problem needs more scratch than
+                           the static buffer holds (FA_STATIC_SCRATCH_BYTES)  */
 };
 
 /* Largest supported sequence length (keeps every per-head offset in 31 bits). */
@@ -274,6 +276,36 @@ int fa_bwd_kv(const void* q, const void* k, const void* v, const void* o,
               const void* dout, const float* lse, void* dq, void* dk, void* dv,
               void* workspace, size_t workspace_bytes, int B, int H, int Hkv,
               int Nq, int Nk, int d, int causal, float scale, hipStream_t stream);
+
+/*
+ * fa_bwd_noalloc -- fa_bwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, operation, results and errors as fa_bwd minus
+ * the workspace: the library uses its own static device buffer of
+ * FA_STATIC_SCRATCH_BYTES instead (a file-scope device array, one per GPU,
+ * held from the library's first use on that GPU until the process ends).
+ * The call allocates nothing: no hipMalloc, no hipFree, no allocating library
+ * routine.
+ *
+ *   Limit       fa_bwd_workspace_size(B, H, N, d) must not exceed
+ *               FA_STATIC_SCRATCH_BYTES, else FA_ERR_SCRATCH (nothing is
+ *               launched).  64 MiB holds about 254 thousand rows (B*H*N) at
+ *               d = 64, whose workspace carries the float32 dQ accumulator
+ *               ([4, 16, 2048, 64] uses 33 MiB), and about 8.3 million rows at
+ *               d = 128 and 256 (two floats per row).
+ *   Sharing     every call on one GPU uses that GPU's one buffer, which keeps
+ *               the last call's contents (each call clears what must start at
+ *               zero with a kernel, not a memset).  Calls that overlap on one
+ *               GPU -- on different streams, or from different host threads
+ *               without ordering -- RACE on the buffer; serialise them.
+ *   First call  on a GPU, looks the buffer's address up on that device (the
+ *               device current at the call) and keeps it.
+ */
+#define FA_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                   const void* dout, const float* lse, void* dq, void* dk,
+                   void* dv, int B, int H, int N, int d, int causal, float scale,
+                   hipStream_t stream);
 
 /*
  * The three stages fa_bwd runs, in order, on the same stream.  Calling them in

@@ -45,7 +45,7 @@ def test_exports_every_declared_symbol(lib):
                           "fa_fwd_fp8", "fa_fwd_f32", "fa_bwd", "fa_bwd_gqa", "fa_bwd_kv",
                           "fa_bwd_workspace_size", "fa_bwd_kv_workspace_size",
                           "fa_status_string", "fa_bwd_preprocess", "fa_bwd_main",
-                          "fa_bwd_finalize"}
+                          "fa_bwd_finalize", "fa_bwd_noalloc"}
     for nm in names:
         assert hasattr(lib, nm), nm
 
@@ -355,3 +355,35 @@ def test_fp8_forward_rejects_bad_arguments(lib):
     # q holds 2 x 100 x 128 bytes = 25600: an o starting inside it aliases
     assert f(o=A + 25600 - 16) == fa.FA_ERR_ALIAS
     assert f(N=0, q=None) == fa.FA_OK
+
+
+def test_noalloc_backward_rejects_bad_arguments(lib):
+    """fa_bwd_noalloc checks like fa_bwd, and refuses (before any HIP call) a
+    problem whose workspace would not fit the static scratch buffer."""
+    m = re.search(r"#define FA_STATIC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)",
+                  open(HEADER).read())
+    assert fa.FA_STATIC_SCRATCH_BYTES == int(m.group(1)) << int(m.group(2))
+
+    def b(**kw):
+        g = dict(q=A, k=A + MB, v=A + 2 * MB, o=A + 3 * MB, dout=A + 4 * MB, lse=A + 5 * MB,
+                 dq=A + 6 * MB, dk=A + 7 * MB, dv=A + 8 * MB, B=1, H=2, N=100, d=64,
+                 causal=1, scale=0.125)
+        g.update(kw)
+        return lib.fa_bwd_noalloc(g["q"], g["k"], g["v"], g["o"], g["dout"], g["lse"],
+                                  g["dq"], g["dk"], g["dv"], g["B"], g["H"], g["N"], g["d"],
+                                  g["causal"], g["scale"], None)
+    assert b(d=96) == fa.FA_ERR_HEADDIM
+    assert b(N=-1) == fa.FA_ERR_SHAPE
+    assert b(scale=math.nan) == fa.FA_ERR_SCALE
+    assert b(dq=None) == fa.FA_ERR_NULL
+    assert b(lse=A + 5 * MB + 4) == fa.FA_ERR_ALIGN
+    assert b(dk=A + 4 * MB) == fa.FA_ERR_ALIAS               # dk is dout
+    assert b(dv=A + 7 * MB + 16) == fa.FA_ERR_ALIAS          # dv inside dk
+    assert b(N=0, q=None) == fa.FA_OK
+    # d = 64 keeps a float32 dQ accumulator: 4 x 16 x 8192 rows need 129 MiB
+    big = dict(B=4, H=16, N=8192, d=64, q=A, k=A + (1 << 30), v=A + (2 << 30),
+               o=A + (3 << 30), dout=A + (4 << 30), lse=A + (5 << 30), dq=A + (6 << 30),
+               dk=A + (7 << 30), dv=A + (8 << 30))
+    assert lib.fa_bwd_workspace_size(4, 16, 8192, 64) > fa.FA_STATIC_SCRATCH_BYTES
+    assert b(**big) == fa.FA_ERR_SCRATCH
+    assert "static" in fa.fa_status_string(fa.FA_ERR_SCRATCH)

@@ -1,0 +1,73 @@
+"""fa_bwd_noalloc (no workspace argument; the library's static per-GPU scratch)
+against fa_bwd (caller's workspace) through the C ABI, on three calls in a
+row: the training-step shape, then a smaller d = 64 problem (the scratch then
+holds the first call's accumulator and must be cleared), then a d = 128 one.
+
+dK and dV have no atomics (bit-equal); at d = 64 dQ sums float atomics in an
+order that varies between runs, so it is held to the parity bar of the bf16
+outputs, 2e-2 absolute (in practice a few bf16 ulps at most); at d = 128 dQ
+has no atomics either (bit-equal)."""
+
+import math
+
+import pytest
+import torch
+
+import exact_tiled_attention_10_amd as fa
+from workloads import make_inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU on this host")
+    fa.load_library()
+
+
+def _pair(B, H, N, d, causal, seed):
+    q, k, v, do = (t.cuda() for t in make_inputs(B, H, N, d, torch.bfloat16, seed=seed,
+                                                  with_do=True))
+    scale = 1.0 / math.sqrt(d)
+    o, lse = fa.forward(q, k, v, causal, scale)
+    ref = [torch.full_like(q, float("nan")) for _ in range(3)]
+    got = [torch.full_like(q, float("nan")) for _ in range(3)]
+    ws = torch.full((fa.fa_bwd_workspace_size(B, H, N, d),), 0xFF, dtype=torch.uint8,
+                    device="cuda")
+    fa.fa_bwd(q, k, v, o, do, lse, *ref, ws, causal, scale)
+    fa.fa_bwd_noalloc(q, k, v, o, do, lse, *got, causal, scale)
+    torch.cuda.synchronize()
+    return ref, got
+
+
+@pytest.mark.parametrize("calls", [[(4, 16, 2048, 64, True, 5), (1, 2, 300, 64, False, 6),
+                                    (1, 3, 257, 128, True, 7)]])
+def test_noalloc_matches_workspace_backward(calls):
+    for (B, H, N, d, causal, seed) in calls:
+        print(f"[noalloc] B={B} H={H} N={N} d={d} causal={causal}", flush=True)
+        assert fa.fa_bwd_workspace_size(B, H, N, d) <= fa.FA_STATIC_SCRATCH_BYTES
+        ref, got = _pair(B, H, N, d, causal, seed)
+        for g in got:
+            assert torch.isfinite(g).all()
+        assert torch.equal(got[1], ref[1]) and torch.equal(got[2], ref[2])
+        err_dq = (got[0].float() - ref[0].float()).abs().max().item()
+        print(f"   max |dQ noalloc - dQ workspace| = {err_dq:.3e}", flush=True)
+        if d == 64:
+            assert err_dq <= TOL
+        else:
+            assert torch.equal(got[0], ref[0])
+
+
+def test_noalloc_refuses_a_problem_past_the_scratch():
+    B, H, N, d = 4, 16, 8192, 64
+    assert fa.fa_bwd_workspace_size(B, H, N, d) > fa.FA_STATIC_SCRATCH_BYTES
+    z = torch.zeros((B, H, N, d), dtype=torch.bfloat16, device="cuda")
+    outs = [torch.empty_like(z) for _ in range(6)]
+    lse = torch.zeros((B, H, N), dtype=torch.float32, device="cuda")
+    with pytest.raises(fa.FAError) as e:
+        fa.fa_bwd_noalloc(outs[0], outs[1], outs[2], outs[3], outs[4], lse, z, outs[5],
+                          torch.empty_like(z), True, 0.125)
+    assert e.value.status == fa.FA_ERR_SCRATCH
