@@ -52,7 +52,7 @@ namespace {
 // w % 4, so every SIMD runs one wave of each group.
 constexpr int kWaves = 8;
 constexpr int kBM = 32 * kWaves;  // queries per workgroup
-static_assert(kBM == fwd_rows_per_tile(64) && kBM == fwd_rows_per_tile(128), "plan geometry");
+static_assert(kBM == fwd_rows_per_tile(128), "plan geometry");
 // The fp32 kernel keeps the 4-wave, 128-query tiling.
 constexpr int kWavesF32 = 4;
 constexpr int kBMF32 = 32 * kWavesF32;
@@ -119,6 +119,7 @@ struct FwdArgs {
   float* Lpart;   // [nsplit, BH, Nq]
   int BH, Nq, Nk, koff, nqt, nsplit, klen, group, negq;
   float c;
+  int prio1, prio2, prio3;   // remaining-round thresholds of the issue priorities
 };
 
 template <int D, int BN, bool CAUSAL>
@@ -523,6 +524,295 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(const FwdArgs a) {
         }
       if (h == 0) a.Lpart[prow] = lse;
     }
+  }
+}
+
+// In-order forward for head dimension 64 ("Flash Attention, From First
+// Principles", "The rent arithmetic": at d = 64 a score costs half the matrix
+// work of d = 128 while its softmax costs the same, so the vector ALU, not the
+// matrix core, sets the pace).  Measured on this chip: a wave64 v_fma_f32
+// occupies a SIMD's vector ALU ~4 cycles and a v_exp_f32 ~8, so the softmax
+// of a 32 x 64 tile (32 exponentials and ~80 other vector instructions per
+// lane) costs about as much vector time as the tile's 16 matrix instructions
+// cost matrix time, and one wave alone issues vector instructions well below
+// the ALU's rate (an FMA every ~7 cycles).  The ping-pong kernel above lets
+// only one wave per SIMD run softmax at a time; here every wave simply runs
+//   S^T = K Q^T (MFMA) -> mask -> probabilities (lazy rebase) -> O^T += V^T P^T
+// on its own 32 queries, a 64-key tile per round in two halves of 32 keys
+// (half the score registers live at once: 4 workgroups fit a CU), and four
+// workgroups of 4 waves x 32 queries share each CU, so at any time some waves
+// of a SIMD keep its vector ALU busy while others feed its matrix core.  K and
+// V tiles arrive by DMA, two stages deep, one barrier per round; the query
+// tile arrives by DMA into the second stage (free until the first prefetch)
+// and goes into registers from there.  A wave skips key tiles (and halves)
+// wholly in the future of all its queries.
+constexpr int kWavesIO = 4;
+constexpr int kBMIO = 32 * kWavesIO;
+constexpr int kBNIO = 64;
+static_assert(kBMIO == fwd_rows_per_tile(64), "plan geometry");
+
+template <int D>
+struct IoCfg {
+  static constexpr int CPR = D / 8;                  // 16-byte chunks per row
+  static constexpr int ROW = CPR * 16;               // bytes per row
+  static constexpr int TILE = kBNIO * ROW;           // one K or V tile
+  static constexpr int STAGE = 2 * TILE;             // K then V
+  static constexpr int NQC = D / 16;                 // k-steps of the score product
+  static constexpr int NDB = D / 32;                 // 32-feature output blocks
+  static constexpr int NSB = kBNIO / 32;             // 32-key sub-blocks
+  static constexpr int DMA = TILE / (16 * 64 * kWavesIO);       // DMAs per lane per tile
+  static constexpr int QDMA = kBMIO * ROW / (16 * 64 * kWavesIO);
+  static constexpr int SMEM = 2 * STAGE;
+  static_assert(kBMIO * ROW == STAGE, "the query tile fills the second stage");
+  static_assert(DMA * 16 * 64 * kWavesIO == TILE, "DMA split");
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 4) void fwd_inorder_kernel(const FwdArgs a) {
+  using C = IoCfg<D>;
+  constexpr int BN = kBNIO;
+  constexpr int NSB = C::NSB;
+  extern __shared__ __attribute__((aligned(1024))) char smem_raw[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 31;
+  const int h = lane >> 5;
+  const int BH = a.BH, Nq = a.Nq, Nk = a.Nk, koff = a.koff;
+  const float c = a.c;
+
+  int bh, qt, sp = 0;
+  {
+    int bid = blockIdx.x;
+    if (a.nsplit > 1) {
+      sp = bid % a.nsplit;
+      bid /= a.nsplit;
+    }
+    map_tile(bid, BH, a.nqt, CAUSAL, &bh, &qt);
+  }
+  const size_t base = (size_t)bh * (size_t)Nq * D;
+  const size_t kvbase = (size_t)(bh / a.group) * (size_t)Nk * D;
+  const char* Kb = reinterpret_cast<const char*>(a.K + kvbase);
+  const char* Vb = reinterpret_cast<const char*>(a.V + kvbase);
+  const int q0 = qt * kBMIO;
+  const int wq0 = q0 + 32 * w;
+  const int qrow = wq0 + n;
+
+  const int kb = sp * a.klen;
+  int ke = min(Nk, kb + a.klen);
+  if (CAUSAL) ke = min(ke, q0 + kBMIO + koff);
+  const int nkt = ke > kb ? (ke - kb + BN - 1) / BN : 0;
+
+  // stage s holds K tile t (t & 1 == s) at s * STAGE and V tile t at
+  // s * STAGE + TILE.  DMA slot (i * WAVES + w) * 64 + lane; rows past Nk are
+  // clamped to row Nk - 1 (finite data; those keys are masked to -inf)
+  const unsigned ldsb = __builtin_amdgcn_readfirstlane(lds_addr(smem_raw));
+  auto issue = [&](int t) __attribute__((always_inline)) {
+    const int k0 = kb + t * BN;
+    const char* gk = Kb + (size_t)k0 * C::ROW;
+    const char* gv = Vb + (size_t)k0 * C::ROW;
+    const unsigned st = ldsb + (t & 1) * C::STAGE;
+#pragma unroll
+    for (int i = 0; i < C::DMA; ++i) {
+      const int slot = (i * kWavesIO + w) * 64 + lane;
+      const int row = slot / C::CPR;
+      const int src_row = min(k0 + row, Nk - 1) - k0;
+      const int ck = (slot % C::CPR) ^ swz<C::CPR, SWZ_ROWS>(row);
+      const int cv = (slot % C::CPR) ^ swz<C::CPR, SWZ_TR>(row);
+      const unsigned dst = (unsigned)((i * kWavesIO + w) * 1024);
+      dma16(gk, (unsigned)(src_row * C::ROW + ck * 16), st + dst);
+      dma16(gv, (unsigned)(src_row * C::ROW + cv * 16), st + C::TILE + dst);
+    }
+  };
+  if (nkt > 0) issue(0);
+
+  // the query tile by whole-row DMA into stage 1 (row swizzle; rows past Nq
+  // fall outside the buffer resource and read 0).  Wave w fills slots w,
+  // w + 4, ..; DMA i + 1 is DMA i shifted by 4 KiB on both sides (a multiple
+  // of the swizzle's 16-row period).
+  {
+    static_assert((kWavesIO * 1024 / C::ROW) % 16 == 0, "swizzle period");
+    const int slot = w * 64 + lane;
+    const int row = slot / C::CPR;
+    const int chunk = (slot % C::CPR) ^ swz<C::CPR, SWZ_ROWS>(row);
+    const unsigned qoff = (unsigned)((row * D + chunk * 8) * 2);
+    const long long qbytes = (long long)max(0, Nq - q0) * (D * 2);
+    const char* Qt = reinterpret_cast<const char*>(a.Q + base + (size_t)q0 * D);
+#pragma unroll
+    for (int i = 0; i < C::QDMA; ++i) {
+      const long long b0 = (long long)i * 1024 * kWavesIO;
+      const long long nrec = qbytes - b0 > 0 ? qbytes - b0 : 0;
+      const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(Qt + b0), (short)0, (int)nrec, 0x00020000);
+      dma16_buf(rsrc, qoff, ldsb + C::STAGE + (unsigned)b0 + w * 1024);
+    }
+  }
+  // K operand (A of S^T): row 32 sb + n, features 16 cc + 8 h; V^T operand
+  // through transposing reads (the ping-pong kernel's patterns)
+  const int ka = tile_off<C::CPR, SWZ_ROWS>(n, 8 * h);
+  const int vrow0 = 4 * (lane >> 5) + ((lane & 15) >> 2);
+  const int vcol0 = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int va = tile_off<C::CPR, SWZ_TR>(vrow0, vcol0);
+
+  wait_vmem();
+  __syncthreads();
+  bf16x8 qf[C::NQC];
+  {
+    const uint32_t flip = a.negq ? 0x80008000u : 0u;
+    const char* qs = smem_raw + C::STAGE + 32 * w * C::ROW;
+#pragma unroll
+    for (int cc = 0; cc < C::NQC; ++cc) {
+      u32x4 raw = *reinterpret_cast<const u32x4*>(qs + (ka ^ (32 * cc)));
+      raw ^= flip;
+      qf[cc] = __builtin_bit_cast(bf16x8, raw);
+    }
+  }
+
+  f32x16 acc[C::NDB];
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+  float m = kMInit;
+  float lsum = 0.f;
+
+  for (int j = 0; j < nkt; ++j) {
+    // tile j landed for every wave; every wave is done with tile j - 1 (and,
+    // at j = 0, with the query tile in stage 1)
+    wait_vmem();
+    __syncthreads();
+    if (j + 1 < nkt) issue(j + 1);
+    // issue priority by remaining work: workgroups that have more rounds
+    // left go first (the issue arbiter otherwise favours the oldest waves,
+    // which then finish long before the rest and leave the SIMDs half idle)
+    {
+      const int rem = nkt - j;
+      if (rem > a.prio3) __builtin_amdgcn_s_setprio(3);
+      else if (rem > a.prio2) __builtin_amdgcn_s_setprio(2);
+      else if (rem > a.prio1) __builtin_amdgcn_s_setprio(1);
+      else __builtin_amdgcn_s_setprio(0);
+    }
+    const int k0 = kb + j * BN;
+    if (CAUSAL && k0 > wq0 + 31 + koff) continue;   // every key after every query
+    const char* ks = smem_raw + (j & 1) * C::STAGE;
+    const char* vs = ks + C::TILE;
+
+    const bool need_mask = (k0 + BN > ke) || (CAUSAL && k0 + BN - 1 > wq0 + koff);
+    // the tile in two halves of 32 keys (half the score and probability
+    // registers of a whole tile live at once): per half S^T (lane = query;
+    // register r holds key k0 + 32 sb + 8 (r / 4) + 4 h + r % 4), mask,
+    // probabilities against the running max (lazy rebase), O^T += V^T P^T
+#pragma unroll
+    for (int sb = 0; sb < NSB; ++sb) {
+      if (CAUSAL && k0 + 32 * sb > wq0 + 31 + koff) break;   // the rest is all future
+      f32x16 s = {};
+#pragma unroll
+      for (int cc = 0; cc < C::NQC; ++cc) {
+        const bf16x8 kf =
+            *reinterpret_cast<const bf16x8*>(ks + (ka ^ (32 * cc)) + sb * 32 * C::ROW);
+        s = mfma_32x32x16_bf16(kf, qf[cc], s);
+      }
+      if (need_mask) {
+        int lim = ke - 1 - k0 - 32 * sb - 4 * h;
+        if (CAUSAL) lim = min(lim, qrow + koff - k0 - 32 * sb - 4 * h);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int off = 8 * (r >> 2) + (r & 3);
+          s[r] = off > lim ? kNegInf : s[r];
+        }
+      }
+      uint32_t pk[8];
+      auto probs = [&]() __attribute__((always_inline)) {
+        float part[4];
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -m));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r + 1], c, -m));
+          pk[r >> 1] = pack_bf16x2(p0, p1);
+          if (r < 8)
+            part[(r >> 1) & 3] = p0 + p1;
+          else
+            part[(r >> 1) & 3] += p0 + p1;
+        }
+        return (part[0] + part[1]) + (part[2] + part[3]);
+      };
+      float ps = probs();
+      if (__any(ps > kSumBound)) {
+        float mx = kNegInf;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+        mx = fmaxf(mx, wave_xor32(mx));
+        const float m_new = fmaxf(m, mx * c);
+        const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+        lsum *= alpha;
+        m = m_new;
+        ps = probs();
+      }
+      lsum += ps;
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const bf16x8 b = __builtin_bit_cast(
+            bf16x8, u32x4{pk[4 * half], pk[4 * half + 1], pk[4 * half + 2], pk[4 * half + 3]});
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db) {
+          const char* vp = vs + (va ^ (64 * db)) + (32 * sb + 16 * half) * C::ROW;
+          const u32x2 lo = lds_read_tr16(vp);
+          const u32x2 hi = lds_read_tr16(vp + 8 * C::ROW);
+          acc[db] = mfma_32x32x16_bf16(__builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y}),
+                                       b, acc[db]);
+        }
+      }
+    }
+  }
+
+  // epilogue: one deferred division, then O and the log-sum-exp.  A row that
+  // saw no key has l = 0: O = 0 and lse = -inf, the merge law's empty block.
+  const float lt = lsum + wave_xor32(lsum);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  const float lse = lt > 0.f ? (m + __log2f(lt)) * kLn2 : kNegInf;
+  if (a.nsplit == 1) {
+    // O through LDS (stage 0, after every wave's last read) as whole rows:
+    // the wave writes its 32 x D block (row swizzle), then stores 16-byte
+    // chunks, 64 / CPR rows per instruction
+    __syncthreads();
+    char* ost = smem_raw + 32 * w * C::ROW;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * db + 8 * g + 4 * h;
+        u32x2 out = {pack_bf16x2(acc[db][4 * g + 0] * inv, acc[db][4 * g + 1] * inv),
+                     pack_bf16x2(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv)};
+        *reinterpret_cast<u32x2*>(ost + tile_off<C::CPR, SWZ_ROWS>(n, d0)) = out;
+      }
+    constexpr int PER = 64 / C::CPR;
+#pragma unroll
+    for (int it = 0; it < 32 / PER; ++it) {
+      const int r = it * PER + lane / C::CPR, ch = lane % C::CPR;
+      const u32x4 v16 =
+          *reinterpret_cast<const u32x4*>(ost + tile_off<C::CPR, SWZ_ROWS>(r, 8 * ch));
+      if (wq0 + r < Nq)
+        *reinterpret_cast<u32x4*>(a.O + base + (size_t)(wq0 + r) * D + 8 * ch) = v16;
+    }
+    if (h == 0 && qrow < Nq) a.LSE[(size_t)bh * Nq + qrow] = lse;
+  } else if (qrow < Nq) {
+    const size_t prow = ((size_t)sp * BH + bh) * Nq + qrow;
+    float* orow = a.Opart + prow * D;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * db + 8 * g + 4 * h;
+        f32x4 out = {acc[db][4 * g + 0] * inv, acc[db][4 * g + 1] * inv,
+                     acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv};
+        *reinterpret_cast<f32x4*>(orow + d0) = out;
+      }
+    if (h == 0) a.Lpart[prow] = lse;
   }
 }
 
@@ -1467,6 +1757,26 @@ hipError_t launch_decode(const FwdArgs& a, hipStream_t stream) {
   return launch_merge(a, D, stream);
 }
 
+template <int D, bool CAUSAL>
+hipError_t launch_inorder(FwdArgs a, hipStream_t stream) {
+  using C = IoCfg<D>;
+  // issue-priority thresholds at a quarter, a half and three quarters of the
+  // longest workgroup's rounds
+  const int most = (min(a.Nk, a.klen) + kBNIO - 1) / kBNIO;
+  a.prio1 = most / 4;
+  a.prio2 = most / 2;
+  a.prio3 = 3 * most / 4;
+  auto kern = fwd_inorder_kernel<D, CAUSAL>;
+  hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, C::SMEM);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(a.BH * a.nqt * a.nsplit), dim3(64 * kWavesIO), C::SMEM, stream,
+                     a);
+  e = hipGetLastError();
+  if (e != hipSuccess || a.nsplit == 1) return e;
+  return launch_merge(a, D, stream);
+}
+
 template <bool CAUSAL>
 hipError_t launch_d256(const FwdArgs& a, hipStream_t stream) {
   constexpr int smem = 4 * kBN256 * 256 * 2;
@@ -1547,7 +1857,7 @@ hipError_t launch_fwd_bf16_kv(const void* q, const void* k, const void* v, void*
   if (d == 256) return causal ? launch_d256<true>(a, stream) : launch_d256<false>(a, stream);
   if (d == 128)
     return causal ? launch_bf16<128, 64, true>(a, stream) : launch_bf16<128, 64, false>(a, stream);
-  return causal ? launch_bf16<64, 64, true>(a, stream) : launch_bf16<64, 64, false>(a, stream);
+  return causal ? launch_inorder<64, true>(a, stream) : launch_inorder<64, false>(a, stream);
 }
 
 hipError_t launch_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,

@@ -13,9 +13,9 @@ namespace fa {
 // ---------------------------------------------------------------------------
 // tile geometry shared by the kernels and the plans
 // ---------------------------------------------------------------------------
-// Queries per forward workgroup: 256 (8 waves x 32) for d = 64 and 128, 128
-// for d = 256 (4 waves x 32).
-constexpr int fwd_rows_per_tile(int d) { return d == 256 ? 128 : 256; }
+// Queries per forward workgroup: 256 (8 waves x 32) for d = 128, 128 (4 waves
+// x 32) for d = 64 and 256.
+constexpr int fwd_rows_per_tile(int d) { return d == 128 ? 256 : 128; }
 // Keys per forward key tile of the plans' split arithmetic (a multiple of
 // every forward kernel's key tile).
 constexpr int kFwdSplitKeys = 64;
