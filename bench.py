@@ -19,9 +19,11 @@ Prints ONE JSON line.  Throughput counts 4*N^2*d FLOP per (batch, head) for
 the forward, halved when causal, and 2.5x that for the backward.
 
 Extra modes (each prints its own JSON):
-  --only NAME              run just one workload (the step, or one forward or
-                           extra shape) a few times: the target of per-shape
-                           rocprofv3 counter runs
+  --only NAME              run just one workload: the step (--launches steps
+                           after --only-settle-s seconds of untimed ones), or
+                           one forward or extra shape timed as in the full run
+                           (settle phase, then >= 150 ms of repeats): the
+                           target of per-shape rocprofv3 runs
   --copy-calibration MIB   time a plain device copy of MIB MiB (used to scale
                            rocprofv3 FETCH_SIZE / WRITE_SIZE counters)
   --pmc-summary FETCH_CSV WRITE_CSV --kernel K --workload W
@@ -59,8 +61,18 @@ CSRC = "exact_tiled_attention_10_amd/csrc/"
 # they are unchanged
 KERNEL_SOURCES = {
     "bwd_main_kernel": [CSRC + "fa_bwd.hip", CSRC + "fa_common.h"],
+    "bwd_dq_direct_kernel": [CSRC + "fa_bwd.hip", CSRC + "fa_common.h"],
     "fwd_bf16_kernel": [CSRC + "fa_fwd.hip", CSRC + "fa_common.h"],
+    "fwd_inorder_kernel": [CSRC + "fa_fwd.hip", CSRC + "fa_common.h"],
+    "fwd_fp8_kernel": [CSRC + "fa_fwd.hip", CSRC + "fa_common.h"],
+    "fwd_d256_kernel": [CSRC + "fa_fwd.hip", CSRC + "fa_common.h"],
+    "fwd_decode_kernel": [CSRC + "fa_fwd.hip", CSRC + "fa_common.h"],
 }
+
+
+def fwd_kernel(d: int) -> str:
+    """The forward kernel fa_fwd launches for bf16 inputs of head dimension d."""
+    return {64: "fwd_inorder_kernel", 128: "fwd_bf16_kernel", 256: "fwd_d256_kernel"}[d]
 STEP_WORKLOAD = "train_step_n2048"
 # forward shapes: (key, workload, causal)
 SWEEP = [("single_head_fp32_n256", "single_head_fp32_n256", False),
@@ -256,7 +268,7 @@ def run_fwd_sweep(settle_s: float = 0.2, min_ms: float = 150.0, only: str = None
         else:
             ent["pct_of_bf16_peak"] = round(100 * tf / PEAK_BF16_TFLOPS, 1)
             ent["roofline"] = _roofline_mfma(
-                flops, ms, "fwd_bf16_kernel", key,
+                flops, ms, fwd_kernel(w.d), key,
                 unit_bytes=fwd_algorithmic_bytes(w.B, w.H, w.N, w.d))
         out[key] = ent
         del q, k, v, o, lse
@@ -286,12 +298,17 @@ def run_extra_sweep(only: str = None):
     def want(key):
         return only is None or only == key
 
-    def entry(ms, ms_min, flops, peak=PEAK_BF16_TFLOPS, extra=None):
+    def entry(ms, ms_min, flops, peak=PEAK_BF16_TFLOPS, extra=None, kernel=None, key=None,
+              unit_bytes=None):
         tf = flops / (ms * 1e-3) / 1e12
         e = dict(ms=round(ms, 5), ms_min=round(ms_min, 5), tflops=round(tf, 1),
                  pct_of_bf16_peak=round(100 * tf / PEAK_BF16_TFLOPS, 1))
         if peak != PEAK_BF16_TFLOPS:
             e["pct_of_fp8_peak"] = round(100 * tf / peak, 1)
+        if kernel is not None:
+            # one kernel per call: the call's time is the kernel's
+            e["roofline"] = _roofline_mfma(flops, ms, kernel, key, peak=peak,
+                                           unit_bytes=unit_bytes)
         e.update(extra or {})
         return e
 
@@ -305,7 +322,10 @@ def run_extra_sweep(only: str = None):
         fa.fa_fwd_gqa(q, k, v, o, lse, True, sc)
         if want("llama8b_gqa32x8_n4096_causal_fwd"):
             ms, mn = _time_launches(lambda: fa.fa_fwd_gqa(q, k, v, o, lse, True, sc))
-            out["llama8b_gqa32x8_n4096_causal_fwd"] = entry(ms, mn, fwd_flops(B, H, N, d, True))
+            out["llama8b_gqa32x8_n4096_causal_fwd"] = entry(
+                ms, mn, fwd_flops(B, H, N, d, True), kernel="fwd_bf16_kernel",
+                key="llama8b_gqa32x8_n4096_causal_fwd",
+                unit_bytes=2 * B * (H + Hkv) * N * d * 2 + B * H * N * 4)
         if want("llama8b_gqa32x8_n4096_causal_bwd"):
             dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
             ws = torch.empty(fa.fa_bwd_kv_workspace_size(B, H, Hkv, N, N, d),
@@ -324,7 +344,9 @@ def run_extra_sweep(only: str = None):
         o = torch.empty_like(q)
         lse = torch.empty((B2, H2, N2), dtype=torch.float32, device="cuda")
         ms, mn = _time_launches(lambda: fa.fa_fwd(q, k, v, o, lse, True, 1 / 16.0))
-        out["d256_n4096_causal_fwd"] = entry(ms, mn, fwd_flops(B2, H2, N2, d2, True))
+        out["d256_n4096_causal_fwd"] = entry(ms, mn, fwd_flops(B2, H2, N2, d2, True),
+                                             kernel="fwd_d256_kernel", key="d256_n4096_causal_fwd",
+                                             unit_bytes=fwd_algorithmic_bytes(B2, H2, N2, d2))
         del q, k, v, o, lse
 
     if want("fp8_llama8b_n4096_causal_fwd"):
@@ -333,8 +355,10 @@ def run_extra_sweep(only: str = None):
         o = torch.empty((1, 32, 4096, 128), dtype=torch.bfloat16, device="cuda")
         lse = torch.empty((1, 32, 4096), dtype=torch.float32, device="cuda")
         ms, mn = _time_launches(lambda: fa.fa_fwd_fp8(q8, k8, v8, o, lse, sq, sk, sv, True, sc))
-        out["fp8_llama8b_n4096_causal_fwd"] = entry(ms, mn, fwd_flops(1, 32, 4096, 128, True),
-                                                    peak=PEAK_FP8_TFLOPS)
+        out["fp8_llama8b_n4096_causal_fwd"] = entry(
+            ms, mn, fwd_flops(1, 32, 4096, 128, True), peak=PEAK_FP8_TFLOPS,
+            kernel="fwd_fp8_kernel", key="fp8_llama8b_n4096_causal_fwd",
+            unit_bytes=3 * 32 * 4096 * 128 + 32 * 4096 * 128 * 2 + 32 * 4096 * 4)
         del q8, k8, v8, o, lse
 
     if want("llama8b_decode_b8_gqa32x8_nk32768"):
@@ -351,7 +375,13 @@ def run_extra_sweep(only: str = None):
         gbs = nbytes / (ms * 1e-3) / 1e9
         out["llama8b_decode_b8_gqa32x8_nk32768"] = dict(
             ms=round(ms, 5), ms_min=round(mn, 5), algorithmic_bytes=nbytes, gbs=round(gbs, 1),
-            frac_of_hbm_peak=round(gbs / PEAK_HBM_GBS, 4), workspace_bytes=nb)
+            frac_of_hbm_peak=round(gbs / PEAK_HBM_GBS, 4), workspace_bytes=nb,
+            roofline=dict(bound="hbm", achieved=round(gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                          frac=round(gbs / PEAK_HBM_GBS, 4),
+                          traffic=load_traffic("fwd_decode_kernel",
+                                               "llama8b_decode_b8_gqa32x8_nk32768"),
+                          kernel="fwd_decode_kernel + split merge", kernel_ms=round(ms, 5),
+                          algorithmic_bytes=nbytes))
         del q, k, v, o, lse, ws
     torch.cuda.empty_cache()
     return out
@@ -530,18 +560,22 @@ def copy_calibration(mib: float):
     return dict(copy_mib=mib, bytes=n)
 
 
-def run_only(name: str, launches: int):
-    """A few launches of one workload, nothing else: counter runs use it so
-    each kernel's dispatches belong to one shape."""
+def run_only(name: str, launches: int, settle_s: float = 0.0):
+    """One workload, nothing else, so each kernel's dispatches in a profiler
+    run belong to one shape: the step (``settle_s`` of untimed steps, then
+    ``launches`` more), or one sweep shape timed as the full run times it
+    (a settle phase, then repeats covering at least 150 ms)."""
     import torch
     if name == "step":
         step, _ = make_step()
+        if settle_s > 0:
+            _settle(step, settle_s)
         for _ in range(launches):
             step()
         torch.cuda.synchronize()
-        return dict(only=name, launches=launches)
+        return dict(only=name, launches=launches, settle_s=settle_s)
     if name in {k for k, _, _ in SWEEP}:
-        r = run_fwd_sweep(settle_s=0.0, min_ms=0.0, only=name)
+        r = run_fwd_sweep(only=name)
     else:
         r = run_extra_sweep(only=name)
         if not r:
@@ -569,6 +603,8 @@ def main(argv=None):
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--only", default=None, metavar="NAME")
     ap.add_argument("--launches", type=int, default=5)
+    ap.add_argument("--only-settle-s", type=float, default=0.0,
+                    help="with --only step: seconds of untimed steps before the launches")
     ap.add_argument("--copy-calibration", type=float, default=None, metavar="MIB")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--kernel", default="bwd_main_kernel")
@@ -597,7 +633,7 @@ def main(argv=None):
     if args.copy_calibration:
         print(json.dumps(copy_calibration(args.copy_calibration)), flush=True)
     if args.only:
-        print(json.dumps(run_only(args.only, args.launches)), flush=True)
+        print(json.dumps(run_only(args.only, args.launches, args.only_settle_s)), flush=True)
         return 0
 
     r = run_step_bench(args.steps, args.warmup, args.settle_s, args.min_timed_ms)
@@ -610,7 +646,7 @@ def main(argv=None):
     if km["main"] >= km["fwd"]:
         roofline = _roofline_mfma(r["bwd_flops"], km["main"], "bwd_main_kernel", STEP_WORKLOAD)
     else:
-        roofline = _roofline_mfma(r["fwd_flops"], km["fwd"], "fwd_bf16_kernel", STEP_WORKLOAD)
+        roofline = _roofline_mfma(r["fwd_flops"], km["fwd"], fwd_kernel(w.d), STEP_WORKLOAD)
     roofline["algorithmic_bytes_whole_backward"] = bwd_algorithmic_bytes(w.B, w.H, w.N, w.d)
 
     line = dict(
