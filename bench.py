@@ -288,7 +288,8 @@ def run_extra_sweep(only: str = None):
     Llama-3.1-8B's real head sharing (32 query heads over 8 key/value heads)
     for the causal N = 4096 forward and backward, the d = 256 causal forward at
     [1, 16, 4096, 256], the e4m3 forward at [1, 32, 4096, 128] causal (against
-    the fp8 peak), and decode -- one new token per sequence against a
+    the fp8 peak), the d = 256 causal backward (fa_bwd: preprocess, key-tile
+    kernel, query-tile dQ kernel), and decode -- one new token per sequence against a
     32k-token cache, split across workgroups by key range -- whose bound is
     HBM (every key and value byte is read once per key/value head)."""
     import torch
@@ -337,6 +338,21 @@ def run_extra_sweep(only: str = None):
                 ms, mn, 2.5 * fwd_flops(B, H, N, d, True))
             del dq, dk, dv, ws
         del q, k, v, do, o, lse
+
+    if want("d256_n4096_causal_bwd"):
+        B2, H2, N2, d2 = 1, 16, 4096, 256
+        q, k, v, do = (t.cuda() for t in make_gqa_inputs(B2, H2, H2, N2, d2, seed=9, with_do=True))
+        o = torch.empty_like(q)
+        lse = torch.empty((B2, H2, N2), dtype=torch.float32, device="cuda")
+        fa.fa_fwd(q, k, v, o, lse, True, 1 / 16.0)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws = torch.empty(fa.fa_bwd_workspace_size(B2, H2, N2, d2), dtype=torch.uint8,
+                         device="cuda")
+        ms, mn = _time_launches(
+            lambda: fa.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, True, 1 / 16.0),
+            per_repeat=4)
+        out["d256_n4096_causal_bwd"] = entry(ms, mn, 2.5 * fwd_flops(B2, H2, N2, d2, True))
+        del q, k, v, do, o, lse, dq, dk, dv, ws
 
     if want("d256_n4096_causal_fwd"):
         B2, H2, N2, d2 = 1, 16, 4096, 256

@@ -120,6 +120,16 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(const float* __restrict__ d
 // ---------------------------------------------------------------------------
 // 2. main kernel
 // ---------------------------------------------------------------------------
+// The value unchanged, but unknown to the compiler from here on: per-lane
+// offsets derived from it are recomputed where they are used instead of
+// being computed once before the loop and held in registers for its whole
+// length (at d = 256 the registers hold K, V and the dK, dV accumulators and
+// have no room for them).
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 template <int D>
 struct BwdCfg {
   static constexpr int WAVES = D == 64 ? 8 : 4;   // d=64: 2 waves/SIMD; else 1
@@ -245,9 +255,10 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_main_kernel(
     const float* L2h = L2 + qhead(g) * Npad;
     const float* Dh = Dv + qhead(g) * Npad;
     const unsigned st = lds0 + C::OFF_ST + (t & 1) * C::STAGE;
+    const int ln = D == 256 ? opaque(lane) : lane;
 #pragma unroll
     for (int j = 0; j < C::QDMA; ++j) {
-      const int slot = (j * C::WAVES + w) * 64 + lane;
+      const int slot = (j * C::WAVES + w) * 64 + ln;
       const int row = slot / C::CPRD;
       const int chunk = (slot % C::CPRD) ^ swz<C::CPRD, SWZ_BOTH>(row);
       const int src = min(q0 + row, Nq - 1);
@@ -316,9 +327,9 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_main_kernel(
   // row-operand reads of Q / dO (A of S and dP): row 32qs + n, features 16cc + 8h
   // (chunk index and swizzle occupy disjoint bits, so feature chunk cc / block
   // db is the cc = 0 / db = 0 offset XOR 32 cc / 64 db: two base registers
-  // instead of an offset per chunk)
+  // instead of an offset per chunk; the per-chunk offsets are formed in the
+  // query loop)
   const int qro0 = tile_off<C::CPRD, SWZ_BOTH>(n, 8 * h);
-  auto qro = [&](int cc) __attribute__((always_inline)) { return qro0 ^ (32 * cc); };
   // transposing reads: 16-lane group g reads rows 4*(g/2) + j (+8 for the
   // second read) and columns 16*(g%2) + 4*(lane%4) of a 32-column block
   const int trow = 4 * (lane >> 5) + ((lane & 15) >> 2);
@@ -326,9 +337,6 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_main_kernel(
   // dO^T / Q^T A operands (rows = queries): rows trow and trow + 8
   const int qtr0 = tile_off<C::CPRD, SWZ_BOTH>(trow, tcol);
   const int qtr1 = tile_off<C::CPRD, SWZ_BOTH>(trow + 8, tcol);
-  auto qtr = [&](int db, int rd) __attribute__((always_inline)) {
-    return (rd ? qtr1 : qtr0) ^ (64 * db);
-  };
   // dS writes: row 32w + n (this lane's key), queries 32qs + 8g + 4h .. +3.
   // The dS tile is row-written and transposing-read, so it uses SWZ_BOTH; its
   // chunk positions are not affine in g, hence one offset per (qs, g).
@@ -418,9 +426,19 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_main_kernel(
     const float* sD = sL2 + kBQ;
     char* dsb = smem + C::OFF_DS + (t & 1) * C::DSTILE;
 
-#pragma unroll
+    // (d = 256 without causal masking: one sub-block body, not two copies --
+    // the copies left the register allocator a few registers short)
+#pragma unroll (D == 256 && !CAUSAL ? 1 : C::NQS)
     for (int qs = 0; qs < C::NQS; ++qs) {
       const int qs0 = q0 + 32 * qs;
+      // d = 256: the operand offsets are recomputed from their bases here
+      const int qro0_ = D == 256 ? opaque(qro0) : qro0;
+      const int qtr0_ = D == 256 ? opaque(qtr0) : qtr0;
+      const int qtr1_ = D == 256 ? opaque(qtr1) : qtr1;
+      auto qro = [&](int cc) __attribute__((always_inline)) { return qro0_ ^ (32 * cc); };
+      auto qtr = [&](int db, int rd) __attribute__((always_inline)) {
+        return (rd ? qtr1_ : qtr0_) ^ (64 * db);
+      };
       uint32_t sk[8];
       // the wave's keys all come after every query of the sub-block: dS = 0
       const bool dead = CAUSAL && (wk0 > qs0 + 31 + koff);
@@ -434,13 +452,14 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_main_kernel(
           s = mfma_32x32x16_bf16(aq, kf[cc], s);
           dp = mfma_32x32x16_bf16(ag, vf[cc], dp);
         }
-        // registers r: query qs0 + 4h + off, off = 8(r/4) + r%4; lane = key
-        f32x4 l2v[4], ddv[4];
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          l2v[g] = *reinterpret_cast<const f32x4*>(sL2 + 32 * qs + 8 * g + 4 * h);
-          ddv[g] = *reinterpret_cast<const f32x4*>(sD + 32 * qs + 8 * g + 4 * h);
-        }
+        // registers r: query qs0 + 4h + off, off = 8(r/4) + r%4; lane = key;
+        // L2 and D of register group g (four queries) read where used
+        auto l2_of = [&](int g) __attribute__((always_inline)) {
+          return *reinterpret_cast<const f32x4*>(sL2 + 32 * qs + 8 * g + 4 * h);
+        };
+        auto d_of = [&](int g) __attribute__((always_inline)) {
+          return *reinterpret_cast<const f32x4*>(sD + 32 * qs + 8 * g + 4 * h);
+        };
         const bool need_mask =
             (qs0 + 31 >= Nq) || (wk0 + 31 >= Nk) || (CAUSAL && wk0 + 31 > qs0 + koff);
         int lo = -1, hi = 1 << 30;   // live offsets: lo < off+1 ... i.e. off >= lo, off < hi
@@ -453,19 +472,24 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_main_kernel(
         // branch-free select in every sub-block cost 4 VALU ops per score)
         auto probs = [&](auto masked) __attribute__((always_inline)) {
 #pragma unroll
-          for (int r = 0; r < 16; r += 2) {
-            float p2[2], ds2[2];
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 l2v = l2_of(g);
+            const f32x4 ddv = d_of(g);
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-              const int rr = r + u;
-              const int off = 8 * (rr >> 2) + (rr & 3);
-              float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rr], c2, -l2v[rr >> 2][rr & 3]));
-              if constexpr (decltype(masked)::value) p = (off < lo || off >= hi) ? 0.f : p;
-              p2[u] = p;
-              ds2[u] = p * (dp[rr] - ddv[rr >> 2][rr & 3]);
+            for (int r = 4 * g; r < 4 * g + 4; r += 2) {
+              float p2[2], ds2[2];
+#pragma unroll
+              for (int u = 0; u < 2; ++u) {
+                const int rr = r + u;
+                const int off = 8 * (rr >> 2) + (rr & 3);
+                float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rr], c2, -l2v[rr & 3]));
+                if constexpr (decltype(masked)::value) p = (off < lo || off >= hi) ? 0.f : p;
+                p2[u] = p;
+                ds2[u] = p * (dp[rr] - ddv[rr & 3]);
+              }
+              pk[r >> 1] = pack_bf16x2(p2[0], p2[1]);
+              sk[r >> 1] = pack_bf16x2(ds2[0], ds2[1]);
             }
-            pk[r >> 1] = pack_bf16x2(p2[0], p2[1]);
-            sk[r >> 1] = pack_bf16x2(ds2[0], ds2[1]);
           }
         };
         if (need_mask)
@@ -735,14 +759,14 @@ __global__ __launch_bounds__(256, D == 128 ? 2 : 1) void bwd_dq_direct_kernel(
   const float dd = qrow < Nq ? Dv[(size_t)bh * Npad + qrow] : 0.f;
 
   // row reads (A of S^T and dP^T): row 32 sb + n, chunk 2 cc + h
-  const int ka = tile_off<C::CPR, SWZ_BOTH>(n, 8 * h);
-  const int va = tile_off<C::CPR, SWZ_ROWS>(n, 8 * h);
+  const int ka0 = tile_off<C::CPR, SWZ_BOTH>(n, 8 * h);
+  const int va0 = tile_off<C::CPR, SWZ_ROWS>(n, 8 * h);
   // transposing reads of the K tile (A of dQ^T = K^T dS^T), the forward's
   // V^T pattern: rows vrow0 (+ 8) of each 16-key chunk, columns 32 db + vcol0
   const int vrow0 = 4 * (lane >> 5) + ((lane & 15) >> 2);
   const int vcol0 = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  const int kt_lo = tile_off<C::CPR, SWZ_BOTH>(vrow0, vcol0);
-  const int kt_hi = tile_off<C::CPR, SWZ_BOTH>(vrow0 + 8, vcol0);
+  const int kt_lo0 = tile_off<C::CPR, SWZ_BOTH>(vrow0, vcol0);
+  const int kt_hi0 = tile_off<C::CPR, SWZ_BOTH>(vrow0 + 8, vcol0);
 
   f32x16 acc[C::NDB];
 #pragma unroll
@@ -757,6 +781,10 @@ __global__ __launch_bounds__(256, D == 128 ? 2 : 1) void bwd_dq_direct_kernel(
     const char* ks = smem + (j & 1) * C::TILE;
     const char* vs = smem + C::OFF_V + (j & 1) * C::TILE;
     const int k0 = j * C::BN;
+    // operand offsets recomputed from their bases each tile rather than held
+    // (at two waves per SIMD the registers are short)
+    const int ka = opaque(ka0), va = opaque(va0);
+    const int kt_lo = opaque(kt_lo0), kt_hi = opaque(kt_hi0);
 
     f32x16 s[C::NSB], dp[C::NSB];
 #pragma unroll
