@@ -120,16 +120,6 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(const float* __restrict__ d
 // ---------------------------------------------------------------------------
 // 2. main kernel
 // ---------------------------------------------------------------------------
-// The value unchanged, but unknown to the compiler from here on: per-lane
-// offsets derived from it are recomputed where they are used instead of
-// being computed once before the loop and held in registers for its whole
-// length (at d = 256 the registers hold K, V and the dK, dV accumulators and
-// have no room for them).
-__device__ __forceinline__ int opaque(int x) {
-  asm volatile("" : "+v"(x));
-  return x;
-}
-
 template <int D>
 struct BwdCfg {
   static constexpr int WAVES = D == 64 ? 8 : 4;   // d=64: 2 waves/SIMD; else 1

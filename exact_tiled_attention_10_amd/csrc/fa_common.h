@@ -43,6 +43,16 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // Round-to-nearest-even float -> bf16 pair packed in one dword (lo = a); one
 // v_cvt_pk_bf16_f32 (two scalar conversions would cost a shift and an or more).
+// The value unchanged, but unknown to the compiler from here on: per-lane
+// offsets derived from it inside a loop are formed where they are used
+// instead of being computed once before the loop and held in registers for
+// its whole length (kernels whose registers are taken by operands and
+// accumulators have no room for them).
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }

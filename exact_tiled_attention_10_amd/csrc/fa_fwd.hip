@@ -819,21 +819,26 @@ __global__ __launch_bounds__(256, 4) void fwd_inorder_kernel(const FwdArgs a) {
 // Head dimension 256 ("Flash Attention, From First Principles", "The rent
 // arithmetic": the accumulator and the query tile grow with d, the tiles
 // shrink).  The ping-pong kernel above needs ~270 registers per wave at this
-// size, past the 256 that two waves per SIMD allow, so this kernel runs ONE
-// wave per SIMD (512 registers: the 32 x 256 accumulator, the query tile and
-// the scores fit with room) and no second group to overlap with: per 32-key
-// tile a wave forms S^T = K Q^T (16 MFMAs), the probabilities against its
-// running max (same lazy rebase as above), and O^T += V^T P^T (16 MFMAs).  At
-// d = 256 a score costs 32 MFMA cycles against a few VALU cycles, so the
-// serial order costs little.  K and V tiles arrive by DMA, two stages deep,
-// one barrier per tile.  Workgroup: 4 waves x 32 queries = 128 queries.
+// size, so this kernel has no second group: per 32-key tile a wave forms
+// S^T = K Q^T (16 MFMAs), the probabilities against its running max (same
+// lazy rebase as above), and O^T += V^T P^T (16 MFMAs), in order.  Two
+// workgroups share a CU (two waves per SIMD, 256 registers each: the 32 x 256
+// accumulator 128, the query operands 64, the rest the scores, probabilities
+// and operand reads), so one workgroup's vector work overlaps the other's
+// matrix work.  The per-lane DMA and operand offsets are formed where they
+// are used (their bases opaque to the compiler): held for the whole loop they
+// spilled, and the DMA addresses then came from scratch memory on the
+// prefetch's path (1 workgroup per CU: 0.211 ms, 2 with the spills: 0.327 ms,
+// 2 without: 0.181 ms at [1, 16, 4096, 256] causal).  K and V tiles arrive by
+// DMA, two stages deep, one barrier per tile.  Workgroup: 4 waves x 32
+// queries = 128 queries, 64 KiB of LDS.
 constexpr int kWaves256 = 4;
 constexpr int kBM256 = 32 * kWaves256;
 static_assert(kBM256 == fwd_rows_per_tile(256), "plan geometry");
 constexpr int kBN256 = 32;
 
 template <bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void fwd_d256_kernel(const FwdArgs a) {
+__global__ __launch_bounds__(256, 2) void fwd_d256_kernel(const FwdArgs a) {
   constexpr int D = 256;
   constexpr int BN = kBN256;
   constexpr int CPR = D / 8;                  // 16-byte chunks per row
@@ -883,9 +888,10 @@ __global__ __launch_bounds__(256, 1) void fwd_d256_kernel(const FwdArgs a) {
     const char* gv = Vb + (size_t)k0 * ROW;
     const unsigned stk = ldsb + (t & 1) * TILE;
     const unsigned stv = ldsb + OFF_V + (t & 1) * TILE;
+    const int ln = opaque(lane);
 #pragma unroll
     for (int i = 0; i < DMA; ++i) {
-      const int slot = (i * kWaves256 + w) * 64 + lane;
+      const int slot = (i * kWaves256 + w) * 64 + ln;
       const int row = slot / CPR;
       const int src_row = min(k0 + row, Nk - 1) - k0;
       const int ck = (slot % CPR) ^ swz<CPR, SWZ_ROWS>(row);
@@ -933,9 +939,10 @@ __global__ __launch_bounds__(256, 1) void fwd_d256_kernel(const FwdArgs a) {
     const int k0 = kb + j * BN;
 
     f32x16 s = {};
+    const int ka_ = opaque(ka), va_ = opaque(va);
 #pragma unroll
     for (int cc = 0; cc < NQC; ++cc) {
-      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + (ka ^ (32 * cc)));
+      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + (ka_ ^ (32 * cc)));
       s = mfma_32x32x16_bf16(kf, qf[cc], s);
     }
     if ((k0 + BN > ke) || (CAUSAL && k0 + BN - 1 > wq0 + koff)) {
@@ -983,7 +990,7 @@ __global__ __launch_bounds__(256, 1) void fwd_d256_kernel(const FwdArgs a) {
           bf16x8, u32x4{pk[4 * half], pk[4 * half + 1], pk[4 * half + 2], pk[4 * half + 3]});
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const char* vp = vs + (va ^ (64 * db)) + 16 * half * ROW;
+        const char* vp = vs + (va_ ^ (64 * db)) + 16 * half * ROW;
         const u32x2 lo = lds_read_tr16(vp);
         const u32x2 hi = lds_read_tr16(vp + 8 * ROW);
         acc[db] = mfma_32x32x16_bf16(__builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y}),
