@@ -74,6 +74,24 @@ def fwd_kernel(d: int) -> str:
     """The forward kernel fa_fwd launches for bf16 inputs of head dimension d."""
     return {64: "fwd_inorder_kernel", 128: "fwd_bf16_kernel", 256: "fwd_d256_kernel"}[d]
 STEP_WORKLOAD = "train_step_n2048"
+# The pages' own figures for this path, printed beside the measurements as
+# context only: other hardware, other precisions, other workloads.
+PAGES_CONTEXT = {
+    "note": "figures the pages quote, measured on other hardware: context, not targets",
+    # "FlashAttention from scratch", "Measured on a real GPU" (the FlashAttention
+    # paper's forward + backward on an A100)
+    "flashattention_vs_standard_fwd_bwd": dict(
+        workload="GPT-2 medium, N=1024, d=64, 16 heads, batch 64; A100",
+        runtime_ms=[41.7, 7.3], speedup=5.7, hbm_gb=[40.3, 4.4], hbm_reduction=9.2),
+    # "LLM Architecture Refresh [3]", section 8, the wall-clock table of naive
+    # attention against the fused scaled-dot-product kernel
+    "fused_vs_naive_wall_clock": dict(
+        workload="causal, 8 heads, d=64, fp32; M-series Mac",
+        n=[512, 1024, 2048, 4096], speedup=[3.45, 4.52, 6.40, 8.16]),
+    # "Flash Attention, From First Principles", "Honesty time -- the
+    # confession list", item 7
+    "flashattention2_fraction_of_peak": dict(hardware="A100", fraction=[0.50, 0.73]),
+}
 # forward shapes: (key, workload, causal)
 SWEEP = [("single_head_fp32_n256", "single_head_fp32_n256", False),
          ("gpt2_medium_n1024", "gpt2_medium_n1024", False),
@@ -421,32 +439,53 @@ def _blas_threads() -> int:
 def run_cpu_baseline(budget_s: float):
     """The float64 oracle (plain forward + Jacobian backward) on whole heads of
     the step workload until ``budget_s`` of wall time is spent (at least one
-    head); throughput in the same counted-FLOP units as the GPU value."""
+    head); throughput in the same counted-FLOP units as the GPU value.  Outside
+    the timed loop, the heads it computed are compared with one GPU step (the
+    bench's own step function): the largest absolute differences of O, lse,
+    dQ, dK and dV, beside the stated tolerances."""
     import numpy as np
+    import torch
     from oracle import naive_bwd, naive_fwd
     from workloads import WORKLOADS, workload_inputs
 
     w = WORKLOADS[STEP_WORKLOAD]
     q, k, v, do = workload_inputs(w, with_do=True)
     f64 = lambda t: t.float().numpy().astype(np.float64)  # noqa: E731
+    sc = float(np.float32(w.scale))   # the scale as the kernels receive it
     heads = [(b, h) for b in range(w.B) for h in range(w.H)]
     done = 0
+    results = []
     t0 = time.perf_counter()
     for (b, h) in heads:
         qq, kk, vv, gg = f64(q[b, h]), f64(k[b, h]), f64(v[b, h]), f64(do[b, h])
-        naive_fwd(qq, kk, vv, w.scale, True)
-        naive_bwd(qq, kk, vv, gg, w.scale, True)
+        fo = naive_fwd(qq, kk, vv, sc, True)
+        bo = naive_bwd(qq, kk, vv, gg, sc, True)
+        results.append(((b, h), fo, bo))
         done += 1
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
     flops = 3.5 * fwd_flops(1, done, w.N, w.d, True)
+
+    step, t = make_step()
+    step()
+    torch.cuda.synchronize()
+    err = dict(o=0.0, lse=0.0, dq=0.0, dk=0.0, dv=0.0)
+    for (b, h), (o_ref, lse_ref), (dq_ref, dk_ref, dv_ref) in results:
+        for key, ref in (("o", o_ref), ("lse", lse_ref), ("dq", dq_ref), ("dk", dk_ref),
+                         ("dv", dv_ref)):
+            got = t[key][b, h].float().cpu().numpy().astype(np.float64)
+            err[key] = max(err[key], float(np.max(np.abs(got - ref))))
+    del step, t
+    torch.cuda.empty_cache()
     return dict(value=round(flops / dt / 1e12, 6), unit="TFLOP/s", cores=_blas_threads(),
                 kind="oracle",
                 sample=f"{done} of {len(heads)} (batch, head) slices of {w.name}, float64 "
                        f"forward + backward, {dt:.1f} s wall",
                 host_cpu=platform.processor() or platform.machine(),
-                host_logical_cpus=os.cpu_count())
+                host_logical_cpus=os.cpu_count(),
+                max_abs_err_vs_gpu={key: float(f"{e:.3e}") for key, e in err.items()},
+                tolerance=dict(o=2e-2, dq=2e-2, dk=2e-2, dv=2e-2, lse=1e-3))
 
 
 def run_cpu_sweep(budget_s: float, rows: int = 256, only: str = None):
@@ -468,25 +507,58 @@ def run_cpu_sweep(budget_s: float, rows: int = 256, only: str = None):
         qq = q[0, 0].float().numpy().astype(np.float64)
         kk = k[0, 0].float().numpy().astype(np.float64)
         vv = v[0, 0].float().numpy().astype(np.float64)
+        sc = float(np.float32(w.scale))   # the scale as the kernels receive it
         r = min(rows, w.N)
         done = 0
         start = 0
+        first = None
         t0 = time.perf_counter()
         while True:
             pos = (np.arange(r) * (w.N // r) + start) % w.N
-            naive_fwd_rows(qq[pos], kk, vv, w.scale, causal, pos)
+            res = naive_fwd_rows(qq[pos], kk, vv, sc, causal, pos)
+            if first is None:
+                first = (pos, res)
             done += r
             start += 1
             if time.perf_counter() - t0 >= budget_s:
                 break
         dt = time.perf_counter() - t0
         flops = fwd_flops(1, 1, w.N, w.d, causal) * done / w.N
+        # outside the timed loop: the first rows against one GPU forward
+        err_o, err_lse = _gpu_rows_err(w, causal, q, k, v, first[0], first[1])
+        f32 = w.dtype == "f32"
         out[key] = dict(value=round(flops / dt / 1e12, 6), unit="TFLOP/s",
                         cores=_blas_threads(), kind="oracle",
                         sample=f"{done} query rows of head (0, 0) of {w.name} "
                                f"({'causal' if causal else 'non-causal'}), float64, "
-                               f"{dt:.1f} s wall; counted FLOP pro rata")
+                               f"{dt:.1f} s wall; counted FLOP pro rata",
+                        rows_checked=int(len(first[0])),
+                        max_abs_err_vs_gpu=dict(o=float(f"{err_o:.3e}"),
+                                                lse=float(f"{err_lse:.3e}")),
+                        tolerance=dict(o=1e-5 if f32 else 2e-2, lse=1e-5 if f32 else 1e-3))
     return out
+
+
+def _gpu_rows_err(w, causal, q, k, v, pos, ref):
+    """Largest |GPU - oracle| of O and lse over query rows ``pos`` of head
+    (0, 0), from one GPU forward of the whole workload."""
+    import numpy as np
+    import torch
+    import exact_tiled_attention_10_amd as fa
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    o = torch.empty_like(qd)
+    lse = torch.empty(qd.shape[:3], dtype=torch.float32, device="cuda")
+    if w.dtype == "f32":
+        fa.fa_fwd_f32(qd, kd, vd, o, lse, causal, w.scale)
+    else:
+        fa.fa_fwd(qd, kd, vd, o, lse, causal, w.scale)
+    torch.cuda.synchronize()
+    idx = torch.as_tensor(pos, dtype=torch.long, device="cuda")
+    got_o = o[0, 0].index_select(0, idx).float().cpu().numpy().astype(np.float64)
+    got_l = lse[0, 0].index_select(0, idx).cpu().numpy().astype(np.float64)
+    del qd, kd, vd, o, lse
+    torch.cuda.empty_cache()
+    return float(np.max(np.abs(got_o - ref[0]))), float(np.max(np.abs(got_l - ref[1])))
 
 
 # ---------------------------------------------------------------------------
@@ -685,15 +757,20 @@ def main(argv=None):
                                   "a second pass of the same repeats (the timed steps "
                                   "carry no events)"),
         roofline=roofline,
+        context=PAGES_CONTEXT,
     )
     if not args.no_sweep:
         line["fwd_sweep"] = run_fwd_sweep()
         line["extra_sweep"] = run_extra_sweep()
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = run_cpu_baseline(args.cpu_seconds)
+        cb = run_cpu_baseline(args.cpu_seconds)
+        cb["gpu_over_oracle"] = round(value / cb["value"], 1) if cb["value"] > 0 else None
+        line["cpu_baseline"] = cb
         if not args.no_sweep:
             cs = run_cpu_sweep(args.cpu_sweep_seconds)
             for key, ent in cs.items():
+                gpu = line["fwd_sweep"][key]["tflops"]
+                ent["gpu_over_oracle"] = round(gpu / ent["value"], 1) if ent["value"] > 0 else None
                 line["fwd_sweep"][key]["cpu_baseline"] = ent
     print(json.dumps(line), flush=True)
     return 0
