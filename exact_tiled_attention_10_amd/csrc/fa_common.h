@@ -194,4 +194,39 @@ __device__ __forceinline__ void map_tile(int bid, int BH, int ntiles, bool heavy
   *tile = heavy_first ? (ntiles - 1 - t) : t;
 }
 
+// map_tile for kernels of which several workgroups share a CU from the
+// start: consecutive passes of `pass` workgroups per XCD (one per compute
+// unit) run in alternating directions, so the compute unit that takes the
+// heaviest tile of one pass takes the lightest of the next and every unit's
+// total comes out alike.
+__device__ __forceinline__ void map_tile_snake(int bid, int BH, int ntiles, bool heavy_first,
+                                               int pass, int* bh, int* tile) {
+  int t, h;
+  if ((BH & 7) == 0) {
+    const int xcd = bid & 7;
+    int j = bid >> 3;
+    const int hpx = BH >> 3;
+    const int nx = hpx * ntiles;
+    const int p = j / pass;
+    if (p & 1) {
+      const int len = min(pass, nx - p * pass);
+      j = p * pass + (len - 1 - (j - p * pass));
+    }
+    t = j / hpx;
+    h = xcd * hpx + (j - t * hpx);
+  } else {
+    int j = bid;
+    const int n = BH * ntiles;
+    const int p = j / (8 * pass);
+    if (p & 1) {
+      const int len = min(8 * pass, n - p * 8 * pass);
+      j = p * 8 * pass + (len - 1 - (j - p * 8 * pass));
+    }
+    t = j / BH;
+    h = j - t * BH;
+  }
+  *bh = h;
+  *tile = heavy_first ? (ntiles - 1 - t) : t;
+}
+
 }  // namespace fa

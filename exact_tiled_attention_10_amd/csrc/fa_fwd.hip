@@ -120,6 +120,7 @@ struct FwdArgs {
   int BH, Nq, Nk, koff, nqt, nsplit, klen, group, negq;
   float c;
   int prio1, prio2, prio3;   // remaining-round thresholds of the issue priorities
+  int pass;                  // compute units per XCD (the snake order's period)
 };
 
 template <int D, int BN, bool CAUSAL>
@@ -589,7 +590,7 @@ __global__ __launch_bounds__(256, 4) void fwd_inorder_kernel(const FwdArgs a) {
       sp = bid % a.nsplit;
       bid /= a.nsplit;
     }
-    map_tile(bid, BH, a.nqt, CAUSAL, &bh, &qt);
+    map_tile_snake(bid, BH, a.nqt, CAUSAL, a.pass, &bh, &qt);
   }
   const size_t base = (size_t)bh * (size_t)Nq * D;
   const size_t kvbase = (size_t)(bh / a.group) * (size_t)Nk * D;
@@ -865,7 +866,7 @@ __global__ __launch_bounds__(256, 2) void fwd_d256_kernel(const FwdArgs a) {
       sp = bid % a.nsplit;
       bid /= a.nsplit;
     }
-    map_tile(bid, BH, a.nqt, CAUSAL, &bh, &qt);
+    map_tile_snake(bid, BH, a.nqt, CAUSAL, a.pass, &bh, &qt);
   }
   const size_t base = (size_t)bh * (size_t)Nq * D;
   const size_t kvbase = (size_t)(bh / a.group) * (size_t)Nk * D;
@@ -1112,7 +1113,7 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const FwdArgs a, float 
       sp = bid % a.nsplit;
       bid /= a.nsplit;
     }
-    map_tile(bid, BH, a.nqt, CAUSAL, &bh, &qt);
+    map_tile_snake(bid, BH, a.nqt, CAUSAL, a.pass, &bh, &qt);
   }
   const size_t base = (size_t)bh * (size_t)Nq * D;
   const size_t kvbase = (size_t)(bh / a.group) * (size_t)Nk * D;
@@ -1785,6 +1786,7 @@ hipError_t launch_inorder(FwdArgs a, hipStream_t stream) {
   a.prio1 = most / 4;
   a.prio2 = most / 2;
   a.prio3 = 3 * most / 4;
+  a.pass = max(1, device_cus() / 8);
   auto kern = fwd_inorder_kernel<D, CAUSAL>;
   hipError_t e = hipFuncSetAttribute((const void*)kern,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, C::SMEM);
@@ -1797,8 +1799,9 @@ hipError_t launch_inorder(FwdArgs a, hipStream_t stream) {
 }
 
 template <bool CAUSAL>
-hipError_t launch_d256(const FwdArgs& a, hipStream_t stream) {
+hipError_t launch_d256(FwdArgs a, hipStream_t stream) {
   constexpr int smem = 4 * kBN256 * 256 * 2;
+  a.pass = max(1, device_cus() / 8);
   auto kern = fwd_d256_kernel<CAUSAL>;
   hipError_t e =
       hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, smem);
@@ -1810,8 +1813,9 @@ hipError_t launch_d256(const FwdArgs& a, hipStream_t stream) {
 }
 
 template <bool CAUSAL>
-hipError_t launch_fp8(const FwdArgs& a, float vscale, hipStream_t stream) {
+hipError_t launch_fp8(FwdArgs a, float vscale, hipStream_t stream) {
   constexpr int smem = 4 * kBNF8 * 128;
+  a.pass = max(1, device_cus() / 8);
   auto kern = fwd_fp8_kernel<CAUSAL>;
   hipError_t e =
       hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, smem);
