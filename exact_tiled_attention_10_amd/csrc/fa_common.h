@@ -168,6 +168,15 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const void* lds_ptr) {
 // have completed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Wait until at most N of this wave's vector memory operations are still
+// outstanding (they complete in issue order): N = the DMAs of the tiles that
+// may stay in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmem_but() {
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
 // Work-tile order for the forward and backward grids.
 //
 // Workgroups are dispatched round-robin over the 8 XCDs (workgroup i lands on

@@ -1324,9 +1324,10 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const FwdArgs a, float 
 // per key / value head, and each workgroup (one wave) streams one range of the
 // keys.  S^T = K Q^T (lane = packed row), the lazy-rebase softmax and
 // O^T += V^T P^T are the forward kernel's; ranges merge through
-// fwd_merge_kernel.  32-key tiles by DMA, two stages (a wave's own, no
-// barrier).
+// fwd_merge_kernel.  32-key tiles by DMA, three stages (a wave's own, no
+// barrier): tile j is read while tiles j + 1 and j + 2 are in flight.
 constexpr int kBNDec = 32;
+constexpr int kDecStages = 3;
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(64, 2) void fwd_decode_kernel(const FwdArgs a) {
@@ -1337,7 +1338,8 @@ __global__ __launch_bounds__(64, 2) void fwd_decode_kernel(const FwdArgs a) {
   constexpr int NQC = D / 16;
   constexpr int NDB = D / 32;
   constexpr int DMA = TILE / (16 * 64);
-  constexpr int OFF_V = 2 * TILE;
+  constexpr int NST = kDecStages;             // tile j read, j + 1 and j + 2 in flight
+  constexpr int OFF_V = NST * TILE;
   extern __shared__ __attribute__((aligned(1024))) char smem_raw[];
 
   const int lane = threadIdx.x;
@@ -1373,11 +1375,12 @@ __global__ __launch_bounds__(64, 2) void fwd_decode_kernel(const FwdArgs a) {
       const int src_row = min(k0 + row, Nk - 1) - k0;
       const int ck = (slot % CPR) ^ swz<CPR, SWZ_ROWS>(row);
       const int cv = (slot % CPR) ^ swz<CPR, SWZ_TR>(row);
-      dma16(gk, (unsigned)(src_row * ROW + ck * 16), ldsb + (t & 1) * TILE + i * 1024);
-      dma16(gv, (unsigned)(src_row * ROW + cv * 16), ldsb + OFF_V + (t & 1) * TILE + i * 1024);
+      dma16(gk, (unsigned)(src_row * ROW + ck * 16), ldsb + (t % NST) * TILE + i * 1024);
+      dma16(gv, (unsigned)(src_row * ROW + cv * 16), ldsb + OFF_V + (t % NST) * TILE + i * 1024);
     }
   };
   if (nkt > 0) issue(0);
+  if (nkt > 1) issue(1);
 
   bf16x8 qf[NQC];
   {
@@ -1406,10 +1409,15 @@ __global__ __launch_bounds__(64, 2) void fwd_decode_kernel(const FwdArgs a) {
   const int last = live ? (CAUSAL ? min(ke - 1, pos + koff) : ke - 1) : -1;
 
   for (int j = 0; j < nkt; ++j) {
-    wait_vmem();   // this wave's DMA of tile j landed (tile j - 1's reads are done)
-    if (j + 1 < nkt) issue(j + 1);
-    const char* ks = smem_raw + (j & 1) * TILE;
-    const char* vs = smem_raw + OFF_V + (j & 1) * TILE;
+    // tile j landed (the DMAs complete in order; tile j + 1's may still fly),
+    // and tile j - 1, whose stage tile j + 2 takes, was read last round
+    if (j + 1 < nkt)
+      wait_vmem_but<2 * DMA>();
+    else
+      wait_vmem();
+    if (j + 2 < nkt) issue(j + 2);
+    const char* ks = smem_raw + (j % NST) * TILE;
+    const char* vs = smem_raw + OFF_V + (j % NST) * TILE;
     const int k0 = kb + j * BN;
 
     f32x16 s = {};
@@ -1766,7 +1774,7 @@ hipError_t launch_merge(const FwdArgs& a, int d, hipStream_t stream) {
 
 template <int D, bool CAUSAL>
 hipError_t launch_decode(const FwdArgs& a, hipStream_t stream) {
-  constexpr int smem = 4 * kBNDec * D * 2;
+  constexpr int smem = 2 * kDecStages * kBNDec * D * 2;
   auto kern = fwd_decode_kernel<D, CAUSAL>;
   hipError_t e =
       hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, smem);

@@ -14,8 +14,9 @@ inline int pad_rows(int N) { return (N + kBwdQueryBlock - 1) / kBwdQueryBlock * 
 
 // Plan of a forward launch.  Decode: when all query rows that read a key /
 // value head fit one wave (group * Nq <= 32, d = 64 or 128) the packed-rows
-// kernel runs, its keys split into ranges of at least 128 keys aiming at four
-// one-wave workgroups per CU.  Otherwise the tile kernels, whose keys are
+// kernel runs, its keys split into ranges of at least 128 keys aiming at the
+// one-wave workgroups per CU its three LDS stages allow (three at d = 128,
+// 48 KiB each; four at d = 64).  Otherwise the tile kernels, whose keys are
 // split only when the query tiles alone leave compute units idle (fewer
 // workgroups than CUs): ranges of at least four 64-key tiles, two workgroups
 // per CU.  Splitting needs the caller's workspace (has_ws).
@@ -28,7 +29,9 @@ FwdPlan fwd_plan(int BH, int group, int Nq, int Nk, int d, bool has_ws, int cus)
     pl.decode = 1;
     if (!has_ws) return pl;
     const long long heads = BH / group;
-    int ns = (int)((4LL * cus + heads - 1) / heads);
+    // one-wave workgroups per CU that the decode kernel's LDS stages allow
+    const long long per_cu = d == 128 ? 3 : 4;
+    int ns = (int)((per_cu * cus + heads - 1) / heads);
     ns = std::min(ns, std::max(1, Nk / 128));
     if (ns <= 1) return pl;
     const int tiles_per = (nkt + ns - 1) / ns;
