@@ -1731,6 +1731,186 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_kernel(
   }
 }
 
+// fp32 with the keys split over the waves, for grids too small to fill the
+// GPU (the single-head N = 256 workload is two 128-query tiles, eight SIMDs
+// at work, bound by the fp32 matrix rate of each).  A workgroup owns 32
+// queries; wave w of four takes key tiles w, w + 4, .. (each staged through
+// its own LDS region, no barrier) with its own running max, sum and
+// accumulator, the partial results of disjoint key sets; at the end the
+// other waves hand theirs to wave 0 through LDS, which combines them by the
+// merge law of composite blocks ("Flash Attention, From First Principles",
+// "The scaffold"): the largest max, every part rescaled to it, one division.
+// Single-head N = 256: 28 -> 14.5 us (eight waves per workgroup, two per
+// SIMD, were slower: 16.8 us).
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void fwd_f32_split_kernel(
+    const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
+    float* __restrict__ O, float* __restrict__ LSE, int BH, int N, int nqt, float c, int negq) {
+  using C = FwdF32Cfg<D>;
+  constexpr int WAVES = 4;
+  constexpr int WTILE = 2 * C::TILE;              // a wave's K and V tile (floats)
+  constexpr int PER = C::BN * D / 4 / 64;         // 16-byte chunks per lane per tensor
+  extern __shared__ __attribute__((aligned(16))) float smemf[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 31;
+  const int h = lane >> 5;
+
+  int bh, qt;
+  map_tile(blockIdx.x, BH, nqt, CAUSAL, &bh, &qt);
+  const size_t base = (size_t)bh * (size_t)N * D;
+  const float* Qh = Q + base;
+  const float* Kh = K + base;
+  const float* Vh = V + base;
+  const int q0 = qt * 32;
+  const int qrow = q0 + n;
+
+  float qf[D / 2];
+#pragma unroll
+  for (int i = 0; i < D / 2; ++i) {
+    float x = (qrow < N) ? Qh[(size_t)qrow * D + 2 * i + h] : 0.f;
+    qf[i] = negq ? -x : x;
+  }
+  const int kend = CAUSAL ? min(N, q0 + 32) : N;
+  const int nkt = (kend + C::BN - 1) / C::BN;
+
+  f32x16 acc[C::NDB];
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+  float m = kNegInf;
+  float lsum = 0.f;
+  float* ks = smemf + w * WTILE;
+  float* vs = ks + C::TILE;
+
+  for (int kt = w; kt < nkt; kt += WAVES) {
+    const int k0 = kt * C::BN;
+    // this wave's tile into its LDS region (rows past N read as 0)
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int ci = i * 64 + lane;
+      const int row = ci / (D / 4);
+      const int col = (ci % (D / 4)) * 4;
+      f32x4 kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
+      if (k0 + row < N) {
+        kv = *reinterpret_cast<const f32x4*>(Kh + (size_t)(k0 + row) * D + col);
+        vv = *reinterpret_cast<const f32x4*>(Vh + (size_t)(k0 + row) * D + col);
+      }
+      *reinterpret_cast<f32x4*>(ks + row * C::RS + col) = kv;
+      *reinterpret_cast<f32x4*>(vs + row * C::RS + col) = vv;
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the writes above are done
+    __builtin_amdgcn_wave_barrier();
+
+    f32x16 s;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = 0.f;
+    const float* krow = ks + n * C::RS + h;
+#pragma unroll
+    for (int i = 0; i < D / 2; ++i) s = mfma_32x32x2_f32(krow[2 * i], qf[i], s);
+    if ((k0 + C::BN > N) || (CAUSAL && k0 + C::BN - 1 > q0)) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = k0 + 8 * (r >> 2) + 4 * h + (r & 3);
+        bool dead = key >= N;
+        if (CAUSAL) dead = dead || key > qrow;
+        if (dead) s[r] = kNegInf;
+      }
+    }
+    float mx = kNegInf;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    mx = fmaxf(mx, wave_xor32(mx));
+    const float m_new = fmaxf(m, mx * c);
+    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+    const float alpha = exp2f(m - m_use);
+    float pr[16];
+    float ps = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -m_use));
+      ps += pr[r];
+    }
+    lsum = lsum * alpha + ps;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+    m = m_new;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = 8 * (r >> 2) + 4 * h + (r & 3);
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db)
+        acc[db] = mfma_32x32x2_f32(vs[key * C::RS + 32 * db + n], pr[r], acc[db]);
+    }
+    // the next tile overwrites this region: every lane's reads are done
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  // waves 1..3 publish (max, sum, accumulator) in the layout every wave
+  // shares (lane = query, registers = features); wave 0 merges
+  const float lt = lsum + wave_xor32(lsum);
+  __syncthreads();   // every wave is past its last tile read
+  float* part = smemf;                                    // [WAVES - 1][NDB * 16][64]
+  float* stat = smemf + (WAVES - 1) * C::NDB * 16 * 64;   // [WAVES - 1][2][64]
+  if (w > 0) {
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) part[((w - 1) * C::NDB * 16 + db * 16 + r) * 64 + lane] =
+          acc[db][r];
+    stat[((w - 1) * 2 + 0) * 64 + lane] = m;
+    stat[((w - 1) * 2 + 1) * 64 + lane] = lt;
+  }
+  __syncthreads();
+  if (w != 0) return;
+  float mw[WAVES], lw[WAVES];
+  mw[0] = m;
+  lw[0] = lt;
+#pragma unroll
+  for (int v = 1; v < WAVES; ++v) {
+    mw[v] = stat[((v - 1) * 2 + 0) * 64 + lane];
+    lw[v] = stat[((v - 1) * 2 + 1) * 64 + lane];
+  }
+  float mm = mw[0];
+#pragma unroll
+  for (int v = 1; v < WAVES; ++v) mm = fmaxf(mm, mw[v]);
+  float wt[WAVES];
+  float den = 0.f;
+#pragma unroll
+  for (int v = 0; v < WAVES; ++v) {
+    wt[v] = mw[v] == kNegInf ? 0.f : exp2f(mw[v] - mm);   // a part that saw no key weighs 0
+    den += wt[v] * lw[v];
+  }
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+  if (qrow < N) {
+    float* orow = O + base + (size_t)qrow * D;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * db + 8 * g + 4 * h;
+        f32x4 out;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g + e;
+          float x = wt[0] * acc[db][r];
+#pragma unroll
+          for (int v = 1; v < WAVES; ++v)
+            x += wt[v] * part[((v - 1) * C::NDB * 16 + db * 16 + r) * 64 + lane];
+          out[e] = x * inv;
+        }
+        *reinterpret_cast<f32x4*>(orow + d0) = out;
+      }
+    if (h == 0) LSE[(size_t)bh * N + qrow] = den > 0.f ? (mm + __log2f(den)) * kLn2 : kNegInf;
+  }
+}
+
 // Softmax scale in log2 units.  scale == 0 (uniform attention) uses a tiny
 // positive factor instead so masked scores still map to -inf, never NaN:
 // every finite score then rounds to the same exponent, 0.
@@ -1843,6 +2023,22 @@ hipError_t launch_f32(const float* q, const float* k, const float* v, float* o, 
   float c;
   int negq;
   split_scale(scale, &c, &negq);
+  if ((long long)BH * nqt < device_cus()) {
+    // too few 128-query tiles to fill the GPU: 32-query workgroups with the
+    // keys split over their waves
+    auto kern = fwd_f32_split_kernel<D, CAUSAL>;
+    constexpr int W = 4;
+    constexpr int smem = W * 2 * C::TILE * 4;
+    static_assert(smem >= ((W - 1) * C::NDB * 16 * 64 + (W - 1) * 2 * 64) * 4, "merge staging");
+    static_assert(smem <= 160 * 1024, "LDS budget");
+    hipError_t e =
+        hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+    if (e != hipSuccess) return e;
+    const int nqt32 = (N + 31) / 32;
+    hipLaunchKernelGGL(kern, dim3(BH * nqt32), dim3(64 * W), smem, stream, q, k, v, o, lse, BH,
+                       N, nqt32, c, negq);
+    return hipGetLastError();
+  }
   auto kern = fwd_f32_kernel<D, CAUSAL>;
   hipError_t e = hipFuncSetAttribute((const void*)kern,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, C::SMEM_BYTES);

@@ -92,6 +92,25 @@ def test_f32_small_and_ragged(N, causal, d):
     assert eo <= TOL_F32 and el <= TOL_LSE
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_f32_grid_that_fills_the_gpu(causal, d):
+    """fa_fwd_f32 on a grid of at least one 128-query tile per CU (4 x 32
+    heads x 300 rows: 384 tiles), where the tile kernel runs rather than the
+    key-split kernel the small cases above take: sampled whole heads."""
+    _say(f"[fwd f32 large grid] d={d} causal={causal}")
+    q, k, v = make_inputs(4, 32, 300, d, torch.float32, seed=260 + d)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = _run(q, k, v, causal, scale)
+    worst_o = worst_l = 0.0
+    for (b, h) in [(0, 0), (1, 7), (2, 17), (3, 31)]:
+        ro, rl = naive_fwd(_f64(q[b, h]), _f64(k[b, h]), _f64(v[b, h]), _s32(scale), causal)
+        worst_o = max(worst_o, float(np.max(np.abs(o[b, h] - ro))))
+        worst_l = max(worst_l, float(np.max(np.abs(lse[b, h] - rl))))
+    _say(f"   max|dO|={worst_o:.3e} max|dlse|={worst_l:.3e}")
+    assert worst_o <= TOL_F32 and worst_l <= TOL_LSE
+
+
 def test_single_head_fp32_workload_full():
     """Single-head fp32 workload at full size (1 x 1 x 256 x 64, non-causal)."""
     w = WORKLOADS["single_head_fp32_n256"]
