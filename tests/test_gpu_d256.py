@@ -138,3 +138,29 @@ def test_d256_backward_gqa_and_lengths(causal):
     q = make_gqa_inputs(1, 4, 2, 150, D, seed=1600, with_do=True)
     k, v = make_gqa_inputs(1, 4, 2, 400, D, seed=1601)[1:]
     _bwd_check(q[0], k, v, q[3], causal, 1 / math.sqrt(D))
+
+
+def test_d256_backward_bench_shape_every_head():
+    """[1, 16, 4096, 256] causal, the inputs the bench times (fa_fwd then
+    fa_bwd, seed 9): every element of dQ, dK and dV of every head against the
+    oracle, 2e-2."""
+    from oracle import naive_bwd
+    q, k, v, do = make_gqa_inputs(1, 16, 16, 4096, D, seed=9, with_do=True)
+    scale = 1 / 16.0
+    qd, kd, vd, dod = (t.cuda() for t in (q, k, v, do))
+    o = torch.empty_like(qd)
+    lse = torch.empty((1, 16, 4096), dtype=torch.float32, device="cuda")
+    fa.fa_fwd(qd, kd, vd, o, lse, True, scale)
+    dq, dk, dv = (torch.full_like(qd, float("nan")) for _ in range(3))
+    ws = torch.full((fa.fa_bwd_workspace_size(1, 16, 4096, D),), 0xFF, dtype=torch.uint8,
+                    device="cuda")
+    fa.fa_bwd(qd, kd, vd, o, dod, lse, dq, dk, dv, ws, True, scale)
+    torch.cuda.synchronize()
+    worst = 0.0
+    for h in range(16):
+        ref = naive_bwd(_f64(q[0, h]), _f64(k[0, h]), _f64(v[0, h]), _f64(do[0, h]), _s32(scale),
+                        True)
+        errs = [float(np.max(np.abs(_f64(g[0, h]) - r))) for g, r in zip((dq, dk, dv), ref)]
+        _say(f"   head {h}: max|d dQ|={errs[0]:.3e} |d dK|={errs[1]:.3e} |d dV|={errs[2]:.3e}")
+        worst = max(worst, max(errs))
+    assert worst <= TOL
