@@ -89,10 +89,19 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
       acc += bf16_bits_to_float(a[k] & 0xffffu) * bf16_bits_to_float(b[k] & 0xffffu);
       acc += bf16_bits_to_float(a[k] >> 16) * bf16_bits_to_float(b[k] >> 16);
     }
-    if (dQacc) {   // only the atomic (d = 64) path has an accumulator
-      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-      *reinterpret_cast<f32x4*>(dQacc + off) = z;
-      *reinterpret_cast<f32x4*>(dQacc + off + 4) = z;
+  }
+  if (dQacc) {   // only the atomic (d = 64) path has an accumulator
+    // the wave zeroes 512 consecutive elements as two contiguous 1 KiB runs
+    // (a lane's own 8 elements as two 16-byte halves 16 bytes apart took
+    // 0.6 us longer over the training-step shape)
+    const size_t w0 = (gid - (gid & 63)) * 8;   // the wave's first element
+    const size_t nel = (size_t)(prow / Npad) * N * D;
+    const int ln = threadIdx.x & 63;
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const size_t e = w0 + (size_t)u * 256 + 4 * ln;
+      if (e < nel) *reinterpret_cast<f32x4*>(dQacc + e) = z;
     }
   }
 #pragma unroll
@@ -418,7 +427,8 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_main_kernel(
 
     // (d = 256 without causal masking: one sub-block body, not two copies --
     // the copies left the register allocator a few registers short)
-#pragma unroll (D == 256 && !CAUSAL ? 1 : C::NQS)
+    constexpr int kQsUnroll = D == 256 && !CAUSAL ? 1 : C::NQS;
+#pragma unroll kQsUnroll
     for (int qs = 0; qs < C::NQS; ++qs) {
       const int qs0 = q0 + 32 * qs;
       // d = 256: the operand offsets are recomputed from their bases here
