@@ -415,24 +415,19 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(const FwdArgs a) {
   // The two groups run separate loops (the same number of barriers): inside
   // one loop the scores are live across the back edge for one group and the
   // probabilities for the other, and merging the two would keep both live.
-  // At d = 64 the softmax phase is the longer one (the same vector work per
-  // score, half the matrix work), so there the DMAs go with the matrix
-  // phases instead: group 0 issues K tile j + 1 as round j begins, group 1
-  // V tile j as its matrix half begins.
-  constexpr bool DMA_WITH_MATRIX = D == 64;
+  // The DMAs go with the softmax phases: group 1 issues K tile j + 1 as round
+  // j begins, group 0 V tile j as its softmax half begins.
   auto round = [&](int j, auto parity, auto group, auto kind) __attribute__((always_inline)) {
     constexpr int G = decltype(group)::value;
-    if (G == (DMA_WITH_MATRIX ? 0 : 1) && j + 1 < nkt)
-      issue(j + 1, 0u, Kb, koffA, koffB, rows_t{});
+    if (G == 1 && j + 1 < nkt) issue(j + 1, 0u, Kb, koffA, koffB, rows_t{});
     if constexpr (G == 0) {
       matrix_phase(parity, kind);
       phase_barrier();
-      if (!DMA_WITH_MATRIX && j < nkt) issue(j, (unsigned)C::OFF_V, Vb, voffA, voffB, tr_t{});
+      if (j < nkt) issue(j, (unsigned)C::OFF_V, Vb, voffA, voffB, tr_t{});
       softmax_phase(j);
     } else {
       softmax_phase(j - 1);
       phase_barrier();
-      if (DMA_WITH_MATRIX && j < nkt) issue(j, (unsigned)C::OFF_V, Vb, voffA, voffB, tr_t{});
       matrix_phase(parity, kind);
     }
     __builtin_amdgcn_s_waitcnt(0);   // this wave's DMAs landed, its LDS reads done
