@@ -19,12 +19,12 @@
 //                   dP = dO V^T                (MFMA)
 //                   dS = P * (dP - D)
 //                   dK^T += Q^T dS             (MFMA)
-//                 and writes dS (bf16) to LDS.  At the start of the next
+//                 and, at d = 64, writes dS (bf16) to LDS.  At the start of the next
 //                 iteration each wave forms its share of dQ = dS K from the
 //                 previous block's dS (double-buffered) and the key tile in LDS
-//                 -- 32x32 blocks over all the tile's keys (one per wave on
-//                 waves 0..3 at d = 64, two per wave at d = 128), so every dQ
-//                 element has one writer per key tile -- and adds it, times
+//                 -- 32x32 blocks over all the tile's keys, one per wave on
+//                 waves 0..3, so every dQ element has one writer per key
+//                 tile -- and adds it, times
 //                 scale, into the fp32 accumulator with hardware float
 //                 atomics; one barrier per block suffices.  The atomics are
 //                 the kernel's scarcest resource (measured: removing them

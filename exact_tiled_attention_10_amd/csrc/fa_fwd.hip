@@ -38,6 +38,13 @@
 // stages deep.  Both tiles stay row-major in LDS (XOR-swizzled against bank
 // conflicts); the V^T operand of the PV product is read with the transposing
 // ds_read_b64_tr_b16, so no register shuffling is needed.
+//
+// That is the head-dimension-128 kernel (fwd_bf16_kernel).  The same steps run
+// in: fwd_inorder_kernel (d = 64: 128-query tiles, every wave in order, four
+// workgroups per CU), fwd_d256_kernel (d = 256), fwd_fp8_kernel (e4m3
+// inputs), fwd_decode_kernel (a few query rows per key / value head, keys
+// split and merged by fwd_merge_kernel), fwd_f32_kernel and, for grids too
+// small to fill the GPU, fwd_f32_split_kernel (fp32 inputs).
 #include <algorithm>
 #include <type_traits>
 
