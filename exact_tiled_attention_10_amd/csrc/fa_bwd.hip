@@ -4,7 +4,7 @@
 // scratch", Step 4 and Follow-up questions).
 //
 // Three launches on the caller's stream:
-//   1. bwd_pre:   per row, L2 = lse * log2(e) and D = sum_c dO_c * O_c (fp32),
+//   1. bwd_pre:   per row, L2 = lse * log2(e) and -D = -sum_c dO_c * O_c (fp32),
 //                 into a workspace padded to 64 rows per head; zero the fp32 dQ
 //                 accumulator.
 //   2. bwd_main:  one workgroup per key tile of one (batch, head); each wave
@@ -62,7 +62,7 @@ inline size_t round256(size_t b) { return (b + 255) / 256 * 256; }
 inline int pad_rows(int N) { return (N + kBQ - 1) / kBQ * kBQ; }
 
 // ---------------------------------------------------------------------------
-// 1. L2 = lse*log2(e), D = rowsum(dO * O); zero the dQ accumulator
+// 1. L2 = lse*log2(e), -D = -rowsum(dO * O); zero the dQ accumulator
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict__ O,
@@ -107,7 +107,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
 #pragma unroll
   for (int s = TPR / 2; s >= 1; s >>= 1) acc += __shfl_xor(acc, s, 64);
   if (prow_id < prow && part == 0) {
-    Dv[prow_id] = live ? acc : 0.f;
+    Dv[prow_id] = live ? -acc : 0.f;   // -D: the dP accumulators start from it
     L2[prow_id] = live ? LSE[bh * N + i] * kLog2e : 0.f;
   }
 }
@@ -443,8 +443,24 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_main_kernel(
       // the wave's keys all come after every query of the sub-block: dS = 0
       const bool dead = CAUSAL && (wk0 > qs0 + 31 + koff);
       if (!dead) {
-        const f32x16 zero = {};
-        f32x16 s = zero, dp = zero;
+        // registers r: query qs0 + 4h + off, off = 8(r/4) + r%4; lane = key.
+        // L2 of register group g (four queries) is read where used; the dP
+        // accumulator starts from -D of each register's query, so the
+        // products leave dP - D in it and dS = P (dP - D) is one multiply
+        auto l2_of = [&](int g) __attribute__((always_inline)) {
+          return *reinterpret_cast<const f32x4*>(sL2 + 32 * qs + 8 * g + 4 * h);
+        };
+        auto nd_of = [&](int g) __attribute__((always_inline)) {
+          return *reinterpret_cast<const f32x4*>(sD + 32 * qs + 8 * g + 4 * h);
+        };
+        f32x16 s = {};
+        f32x16 dp;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 nd = nd_of(g);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dp[4 * g + e] = nd[e];
+        }
 #pragma unroll
         for (int cc = 0; cc < C::NDC; ++cc) {
           const bf16x8 aq = *reinterpret_cast<const bf16x8*>(sQ + qro(cc) + 32 * qs * C::RBD);
@@ -452,14 +468,6 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_main_kernel(
           s = mfma_32x32x16_bf16(aq, kf[cc], s);
           dp = mfma_32x32x16_bf16(ag, vf[cc], dp);
         }
-        // registers r: query qs0 + 4h + off, off = 8(r/4) + r%4; lane = key;
-        // L2 and D of register group g (four queries) read where used
-        auto l2_of = [&](int g) __attribute__((always_inline)) {
-          return *reinterpret_cast<const f32x4*>(sL2 + 32 * qs + 8 * g + 4 * h);
-        };
-        auto d_of = [&](int g) __attribute__((always_inline)) {
-          return *reinterpret_cast<const f32x4*>(sD + 32 * qs + 8 * g + 4 * h);
-        };
         const bool need_mask =
             (qs0 + 31 >= Nq) || (wk0 + 31 >= Nk) || (CAUSAL && wk0 + 31 > qs0 + koff);
         int lo = -1, hi = 1 << 30;   // live offsets: lo < off+1 ... i.e. off >= lo, off < hi
@@ -474,7 +482,6 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_main_kernel(
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const f32x4 l2v = l2_of(g);
-            const f32x4 ddv = d_of(g);
 #pragma unroll
             for (int r = 4 * g; r < 4 * g + 4; r += 2) {
               float p2[2], ds2[2];
@@ -485,7 +492,7 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_main_kernel(
                 float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rr], c2, -l2v[rr & 3]));
                 if constexpr (decltype(masked)::value) p = (off < lo || off >= hi) ? 0.f : p;
                 p2[u] = p;
-                ds2[u] = p * (dp[rr] - ddv[rr & 3]);
+                ds2[u] = p * dp[rr];
               }
               pk[r >> 1] = pack_bf16x2(p2[0], p2[1]);
               sk[r >> 1] = pack_bf16x2(ds2[0], ds2[1]);
@@ -592,7 +599,7 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_main_kernel(
   }
 }
 
-// workspace layout: L2 [BH * Npad], D [BH * Npad], dQ accumulator [BH * N * d]
+// workspace layout: L2 [BH * Npad], -D [BH * Npad], dQ accumulator [BH * N * d]
 struct WsLayout {
   float* l2;
   float* dv;
@@ -756,7 +763,7 @@ __global__ __launch_bounds__(256, D == 128 ? 2 : 1) void bwd_dq_direct_kernel(
     gf[cc] = __builtin_bit_cast(bf16x8, b);
   }
   const float l2 = qrow < Nq ? L2[(size_t)bh * Npad + qrow] : 0.f;
-  const float dd = qrow < Nq ? Dv[(size_t)bh * Npad + qrow] : 0.f;
+  const float nd = qrow < Nq ? Dv[(size_t)bh * Npad + qrow] : 0.f;   // -D of the query
 
   // row reads (A of S^T and dP^T): row 32 sb + n, chunk 2 cc + h
   const int ka0 = tile_off<C::CPR, SWZ_BOTH>(n, 8 * h);
@@ -820,7 +827,7 @@ __global__ __launch_bounds__(256, D == 128 ? 2 : 1) void bwd_dq_direct_kernel(
               const int off = 32 * sb + 8 * (rr >> 2) + (rr & 3);
               p = off > lim ? 0.f : p;   // select after the exp: l2 may be -inf
             }
-            d2[u] = p * (dp[sb][rr] - dd);
+            d2[u] = p * (dp[sb][rr] + nd);
           }
           dsk[sb][r >> 1] = pack_bf16x2(d2[0], d2[1]);
         }

@@ -191,7 +191,7 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o,
  * fa_bwd_workspace_size -- bytes of device workspace fa_bwd needs.
  *
  * Returns 0 for invalid shapes.  The workspace holds, per row, lse * log2(e)
- * and D = rowsum(dO * O) (float32, each head padded to a multiple of 64 rows)
+ * and -D = -rowsum(dO * O) (float32, each head padded to a multiple of 64 rows)
  * and, at d = 64 only, the float32 dQ accumulator ([B, H, N, d]).
  */
 size_t fa_bwd_workspace_size(int B, int H, int N, int d);
@@ -313,7 +313,7 @@ int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
  * that schedule or time the stages separately.  Each validates like fa_bwd
  * (its own pointers only) and reads/writes the workspace as documented.
  *
- * fa_bwd_preprocess -- lse * log2(e) and D = rowsum(dO * O) into the
+ * fa_bwd_preprocess -- lse * log2(e) and -D = -rowsum(dO * O) into the
  *                      workspace; at d = 64 zeroes the workspace's fp32 dQ
  *                      accumulator.
  * fa_bwd_main       -- the key-tile kernel: recomputes P from q, k and the
