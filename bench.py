@@ -18,6 +18,11 @@ step on its launch stream, for the per-kernel durations of the roofline.
 Prints ONE JSON line.  Throughput counts 4*N^2*d FLOP per (batch, head) for
 the forward, halved when causal, and 2.5x that for the backward.
 
+With --cold every timed repeat is one call (one step, one forward) and a
+512 MiB device buffer -- more than the eight 4 MiB L2s and the 256 MiB
+last-level cache together -- is written before it, outside the timed region,
+so the inputs come from HBM; the default keeps caches warm.
+
 Extra modes (each prints its own JSON):
   --only NAME              run just one workload: the step (--launches steps
                            after --only-settle-s seconds of untimed ones), or
@@ -183,17 +188,44 @@ def _settle(fn, seconds: float) -> int:
     return n
 
 
+# --cold: the buffer written before every timed repeat (None: warm caches)
+COLD_MIB = 512
+_cold_buf = None
+
+
+def set_cold(on: bool):
+    global _cold_buf
+    import torch
+    _cold_buf = torch.empty(COLD_MIB << 20, dtype=torch.uint8, device="cuda") if on else None
+
+
+def _flush_caches(i: int):
+    """Cold mode: write the whole buffer (a value that changes per repeat) and
+    wait for it, so the next timed call finds no input in any cache."""
+    if _cold_buf is not None:
+        import torch
+        _cold_buf.fill_(i & 0xFF)
+        torch.cuda.synchronize()
+
+
+def _per_repeat(n: int) -> int:
+    return 1 if _cold_buf is not None else n
+
+
 def _repeats(fn, per_repeat: int, min_ms: float, min_repeats: int = 5):
     """Per-call ms of repeats of ``per_repeat`` calls of ``fn`` (HIP events on
     the current stream, device synchronised around each repeat) until at
-    least ``min_ms`` of GPU time is covered."""
+    least ``min_ms`` of GPU time is covered.  Cold mode: one call per repeat,
+    caches flushed before each."""
     import torch
+    per_repeat = _per_repeat(per_repeat)
     stream = torch.cuda.current_stream()
     s = torch.cuda.Event(enable_timing=True)
     e = torch.cuda.Event(enable_timing=True)
     out, total = [], 0.0
     while len(out) < min_repeats or total < min_ms:
         torch.cuda.synchronize()
+        _flush_caches(len(out))
         s.record(stream)
         for _ in range(per_repeat):
             fn()
@@ -222,15 +254,17 @@ def run_step_bench(steps: int, warmup: int, settle_s: float, min_timed_ms: float
     kernel_ms = {"fwd": [], "pre": [], "main": [], "fin": []}
     inst = []
     timed = 0.0
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    per = _per_repeat(steps)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(per)]
     while len(inst) < 5 or timed < min_timed_ms:
         torch.cuda.synchronize()
-        for i in range(steps):
+        _flush_caches(len(inst))
+        for i in range(per):
             step(evs[i])
         torch.cuda.synchronize()
         span = evs[0][0].elapsed_time(evs[-1][4])
         timed += span
-        inst.append(span / steps)
+        inst.append(span / per)
         for e in evs:
             for j, key in enumerate(("fwd", "pre", "main", "fin")):
                 kernel_ms[key].append(e[j].elapsed_time(e[j + 1]))
@@ -238,8 +272,8 @@ def run_step_bench(steps: int, warmup: int, settle_s: float, min_timed_ms: float
     bf = 2.5 * ff
     med = {k: statistics.median(v) for k, v in kernel_ms.items()}
     return dict(workload=w, ms_per_step=statistics.median(reps), ms_min=min(reps),
-                ms_mean=statistics.fmean(reps), repeats=len(reps),
-                timed_ms=sum(reps) * steps, settle_steps=n_settle, settle_s=settle_s,
+                ms_mean=statistics.fmean(reps), repeats=len(reps), steps_per_repeat=per,
+                timed_ms=sum(reps) * per, settle_steps=n_settle, settle_s=settle_s,
                 step_flops=ff + bf, fwd_flops=ff, bwd_flops=bf,
                 instrumented_ms_per_step=statistics.median(inst), kernel_ms=med)
 
@@ -277,7 +311,7 @@ def run_fwd_sweep(settle_s: float = 0.2, min_ms: float = 150.0, only: str = None
         tf = flops / (ms * 1e-3) / 1e12
         ent = dict(B=w.B, H=w.H, N=w.N, d=w.d, causal=causal, dtype=w.dtype,
                    fwd_ms=round(ms, 5), fwd_ms_min=round(min(reps), 5),
-                   repeats=len(reps), launches_per_repeat=10, tflops=round(tf, 1))
+                   repeats=len(reps), launches_per_repeat=_per_repeat(10), tflops=round(tf, 1))
         if f32:
             # two workgroups: a latency-bound correctness shape, no roofline claim
             ent["pct_of_fp32_peak"] = round(100 * tf / PEAK_FP32_TFLOPS, 2)
@@ -699,6 +733,8 @@ def main(argv=None):
     ap.add_argument("--workload", default=STEP_WORKLOAD)
     ap.add_argument("--algorithmic-bytes", type=float, default=None)
     ap.add_argument("--copy-mib", type=float, default=256.0)
+    ap.add_argument("--cold", action="store_true",
+                    help=f"write a {COLD_MIB} MiB buffer before every timed repeat of one call")
     args = ap.parse_args(argv)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -718,6 +754,7 @@ def main(argv=None):
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
+    set_cold(args.cold)
     if args.copy_calibration:
         print(json.dumps(copy_calibration(args.copy_calibration)), flush=True)
     if args.only:
@@ -746,7 +783,9 @@ def main(argv=None):
                     step="fa_fwd + fa_bwd (preprocess, main, finalize)",
                     pct_of_bf16_peak=round(100 * value / PEAK_BF16_TFLOPS, 2)),
         timing=dict(settle_s=r["settle_s"], settle_steps=r["settle_steps"],
-                    repeats=r["repeats"], steps_per_repeat=args.steps,
+                    repeats=r["repeats"], steps_per_repeat=r["steps_per_repeat"],
+                    caches=(f"cold: {COLD_MIB} MiB written before every timed step"
+                            if args.cold else "warm"),
                     timed_ms=round(r["timed_ms"], 2),
                     ms_per_step_median=round(ms, 5), ms_per_step_min=round(r["ms_min"], 5),
                     ms_per_step_mean=round(r["ms_mean"], 5),

@@ -95,3 +95,14 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_cold_mode_times_one_call_per_repeat(monkeypatch):
+    """--cold parses, and with the flush buffer set every timed repeat is one
+    call (the buffer is written before each); warm repeats keep their length."""
+    assert bench.main(["--cold", "--gpus", "2"]) == 2     # parsed, then refused before any GPU use
+    monkeypatch.setattr(bench, "_cold_buf", None)
+    assert bench._per_repeat(20) == 20
+    monkeypatch.setattr(bench, "_cold_buf", object())
+    assert bench._per_repeat(20) == 1
+    assert bench.COLD_MIB * 2 ** 20 > 8 * 4 * 2 ** 20 + 256 * 2 ** 20   # past every L2 and the LLC
