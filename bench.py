@@ -71,6 +71,7 @@ KERNEL_SOURCES = {
     "fwd_inorder_kernel": [CSRC + "fa_fwd.hip", CSRC + "fa_common.h"],
     "fwd_fp8_kernel": [CSRC + "fa_fwd.hip", CSRC + "fa_common.h"],
     "fwd_d256_kernel": [CSRC + "fa_fwd.hip", CSRC + "fa_common.h"],
+    "fwd_d256_pair_kernel": [CSRC + "fa_fwd.hip", CSRC + "fa_common.h"],
     "fwd_decode_kernel": [CSRC + "fa_fwd.hip", CSRC + "fa_common.h"],
 }
 
@@ -412,8 +413,10 @@ def run_extra_sweep(only: str = None):
         o = torch.empty_like(q)
         lse = torch.empty((B2, H2, N2), dtype=torch.float32, device="cuda")
         ms, mn = _time_launches(lambda: fa.fa_fwd(q, k, v, o, lse, True, 1 / 16.0))
+        # one wave of workgroups under causal masking: the balanced-pair kernel
         out["d256_n4096_causal_fwd"] = entry(ms, mn, fwd_flops(B2, H2, N2, d2, True),
-                                             kernel="fwd_d256_kernel", key="d256_n4096_causal_fwd",
+                                             kernel="fwd_d256_pair_kernel",
+                                             key="d256_n4096_causal_fwd",
                                              unit_bytes=fwd_algorithmic_bytes(B2, H2, N2, d2))
         del q, k, v, o, lse
 

@@ -41,10 +41,11 @@
 //
 // That is the head-dimension-128 kernel (fwd_bf16_kernel).  The same steps run
 // in: fwd_inorder_kernel (d = 64: 128-query tiles, every wave in order, four
-// workgroups per CU), fwd_d256_kernel (d = 256), fwd_fp8_kernel (e4m3
-// inputs), fwd_decode_kernel (a few query rows per key / value head, keys
-// split and merged by fwd_merge_kernel), fwd_f32_kernel and, for grids too
-// small to fill the GPU, fwd_f32_split_kernel (fp32 inputs).
+// workgroups per CU), fwd_d256_kernel and fwd_d256_pair_kernel (d = 256; the
+// second for causal grids of one wave: balanced pairs of query tiles),
+// fwd_fp8_kernel (e4m3 inputs), fwd_decode_kernel (a few query rows per key /
+// value head, keys split and merged by fwd_merge_kernel), fwd_f32_kernel and,
+// for grids too small to fill the GPU, fwd_f32_split_kernel (fp32 inputs).
 #include <algorithm>
 #include <type_traits>
 
@@ -1035,6 +1036,276 @@ __global__ __launch_bounds__(256, 2) void fwd_d256_kernel(const FwdArgs a) {
   }
 }
 
+// Causal head dimension 256 with balanced workgroups.  Two workgroups of the
+// kernel above share a CU, and under causal masking with exactly one
+// workgroup per slot (B*H*N/128 = 2 x CUs) the CU that holds a short and a
+// long tile runs the long one alone, at one wave per SIMD, for most of the
+// kernel ([1, 16, 4096, 256]: 31 % of peak causal against 43 % non-causal).
+// Here one workgroup of two groups of four waves (two waves per SIMD, the
+// same register budget) owns the pair of query tiles p and nqt - 1 - p of one
+// head, whose causal key ranges add up to the same length for every p, and
+// deals the key tiles so both groups do the same number of rounds: group 1
+// takes the first s key tiles of the heavy tile, group 0 the whole light tile
+// and then the heavy tile's remaining key tiles.  Each group streams its own
+// K / V tiles through its own two LDS stages; one workgroup barrier per
+// round.  At the end the heavy tile's two partial results -- (running max,
+// running sum, unnormalised output) of the same rows over disjoint key ranges
+// -- are merged through LDS by the composite-block law of "Flash Attention,
+// From First Principles", "The scaffold" (rescale both by exp(m_part - m),
+// add), and group 0 writes the output.
+template <bool CAUSAL>
+__global__ __launch_bounds__(512, 2) void fwd_d256_pair_kernel(const FwdArgs a) {
+  constexpr int D = 256;
+  constexpr int BN = kBN256;
+  constexpr int CPR = D / 8;                  // 16-byte chunks per row
+  constexpr int ROW = CPR * 16;               // bytes per row
+  constexpr int TILE = BN * ROW;              // one K or V tile (16 KiB)
+  constexpr int NQC = D / 16;                 // k-steps of the score product
+  constexpr int NDB = D / 32;                 // 32-feature output blocks
+  constexpr int DMA = TILE / (16 * 64 * kWaves256);   // DMAs per lane per tile
+  constexpr int OFF_V = 2 * TILE;
+  constexpr int GROUP_LDS = 4 * TILE;         // a group's two K / V stages
+  extern __shared__ __attribute__((aligned(1024))) char smem_raw[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wg = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wg >> 2;                    // wave wg runs on SIMD wg % 4
+  const int w = wg & 3;                       // 32-query block inside a tile
+  const int n = lane & 31;
+  const int h = lane >> 5;
+  const int BH = a.BH, Nq = a.Nq, Nk = a.Nk, koff = a.koff;
+  const float c = a.c;
+
+  // pair p of head bh; whole heads per XCD when the head count allows
+  int bh, p;
+  {
+    const int bid = blockIdx.x;
+    if ((BH & 7) == 0) {
+      const int j = bid >> 3, hpx = BH >> 3;
+      p = j / hpx;
+      bh = (bid & 7) * hpx + (j - p * hpx);
+    } else {
+      p = bid / BH;
+      bh = bid - p * BH;
+    }
+  }
+  const int ta = p, tb = a.nqt - 1 - p;       // light and heavy tile
+  auto nkt_of = [&](int qt) {
+    const int ke = min(Nk, qt * kBM256 + kBM256 + koff);
+    return ke > 0 ? (ke + BN - 1) / BN : 0;
+  };
+  const int ra = nkt_of(ta), rb = nkt_of(tb);
+  const int sk = (ra + rb + 1) / 2;           // group 1: heavy tile's key tiles [0, sk)
+  const int nr = grp ? sk : ra + rb - sk;     // this group's rounds (group 0's <= group 1's)
+
+  const size_t kvbase = (size_t)(bh / a.group) * (size_t)Nk * D;
+  const char* Kb = reinterpret_cast<const char*>(a.K + kvbase);
+  const char* Vb = reinterpret_cast<const char*>(a.V + kvbase);
+  const size_t base = (size_t)bh * (size_t)Nq * D;
+
+  // round j of this group -> key tile index of its current query tile
+  auto key_tile = [&](int j) { return grp ? j : (j < ra ? j : sk + (j - ra)); };
+
+  // DMA of round t into this group's stage t & 1
+  const unsigned ldsb = __builtin_amdgcn_readfirstlane(lds_addr(smem_raw)) + grp * GROUP_LDS;
+  auto issue = [&](int t) __attribute__((always_inline)) {
+    const int k0 = key_tile(t) * BN;
+    const char* gk = Kb + (size_t)k0 * ROW;
+    const char* gv = Vb + (size_t)k0 * ROW;
+    const unsigned stk = ldsb + (t & 1) * TILE;
+    const unsigned stv = ldsb + OFF_V + (t & 1) * TILE;
+    const int ln = opaque(lane);
+#pragma unroll
+    for (int i = 0; i < DMA; ++i) {
+      const int slot = (i * kWaves256 + w) * 64 + ln;
+      const int row = slot / CPR;
+      const int src_row = min(k0 + row, Nk - 1) - k0;
+      const int ck = (slot % CPR) ^ swz<CPR, SWZ_ROWS>(row);
+      const int cv = (slot % CPR) ^ swz<CPR, SWZ_TR>(row);
+      const unsigned dst = (unsigned)((i * kWaves256 + w) * 1024);
+      dma16(gk, (unsigned)(src_row * ROW + ck * 16), stk + dst);
+      dma16(gv, (unsigned)(src_row * ROW + cv * 16), stv + dst);
+    }
+  };
+  if (nr > 0) issue(0);
+
+  // the group's current query tile: group 1 the heavy one, group 0 the light
+  // one and, from round ra on, the heavy one
+  int qt = grp ? tb : ta;
+  int wq0 = qt * kBM256 + 32 * w;
+  int qrow = wq0 + n;
+  int ke = min(Nk, qt * kBM256 + kBM256 + koff);
+  bf16x8 qf[NQC];
+  auto load_q = [&]() __attribute__((always_inline)) {
+    const uint32_t flip = a.negq ? 0x80008000u : 0u;
+    const uint16_t* Qh = a.Q + base;
+#pragma unroll
+    for (int cc = 0; cc < NQC; ++cc) {
+      u32x4 raw = {0u, 0u, 0u, 0u};
+      if (qrow < Nq)
+        raw = *reinterpret_cast<const u32x4*>(Qh + (size_t)qrow * D + 16 * cc + 8 * h);
+      raw ^= flip;
+      qf[cc] = __builtin_bit_cast(bf16x8, raw);
+    }
+  };
+  load_q();
+  const int ka = tile_off<CPR, SWZ_ROWS>(n, 8 * h);
+  const int vrow0 = 4 * (lane >> 5) + ((lane & 15) >> 2);
+  const int vcol0 = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int va = tile_off<CPR, SWZ_TR>(vrow0, vcol0);
+
+  f32x16 acc[NDB];
+  float m, lsum;
+  auto reset = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+    m = kMInit;
+    lsum = 0.f;
+  };
+  reset();
+  // one deferred division, then O and the log-sum-exp of the current tile
+  auto store_out = [&]() __attribute__((always_inline)) {
+    const float lt = lsum + wave_xor32(lsum);
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const float lse = lt > 0.f ? (m + __log2f(lt)) * kLn2 : kNegInf;
+    if (qrow < Nq) {
+      uint16_t* orow = a.O + base + (size_t)qrow * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = 32 * db + 8 * g + 4 * h;
+          u32x2 out = {pack_bf16x2(acc[db][4 * g + 0] * inv, acc[db][4 * g + 1] * inv),
+                       pack_bf16x2(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv)};
+          *reinterpret_cast<u32x2*>(orow + d0) = out;
+        }
+      if (h == 0) a.LSE[(size_t)bh * Nq + qrow] = lse;
+    }
+  };
+  // group 0: the light tile is done -- its output out, the heavy tile's rows in
+  auto switch_tile = [&]() __attribute__((always_inline)) {
+    store_out();
+    qt = tb;
+    wq0 = qt * kBM256 + 32 * w;
+    qrow = wq0 + n;
+    ke = min(Nk, qt * kBM256 + kBM256 + koff);
+    load_q();
+    reset();
+  };
+
+  for (int j = 0; j < sk; ++j) {
+    // this group's tile j landed for its waves; every wave is done with round j - 1
+    wait_vmem();
+    __syncthreads();
+    if (j >= nr) continue;                    // group 0 with one round fewer
+    if (j + 1 < nr) issue(j + 1);
+    if (grp == 0 && j == ra) switch_tile();
+    const char* ks = smem_raw + grp * GROUP_LDS + (j & 1) * TILE;
+    const char* vs = smem_raw + grp * GROUP_LDS + OFF_V + (j & 1) * TILE;
+    const int k0 = key_tile(j) * BN;
+
+    f32x16 s = {};
+    const int ka_ = opaque(ka), va_ = opaque(va);
+#pragma unroll
+    for (int cc = 0; cc < NQC; ++cc) {
+      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + (ka_ ^ (32 * cc)));
+      s = mfma_32x32x16_bf16(kf, qf[cc], s);
+    }
+    if ((k0 + BN > ke) || (CAUSAL && k0 + BN - 1 > wq0 + koff)) {
+      int lim = ke - 1 - k0 - 4 * h;
+      if (CAUSAL) lim = min(lim, qrow + koff - k0 - 4 * h);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int off = 8 * (r >> 2) + (r & 3);
+        s[r] = off > lim ? kNegInf : s[r];
+      }
+    }
+    uint32_t pk[8];
+    auto probs = [&]() __attribute__((always_inline)) {
+      float part[2] = {0.f, 0.f};
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -m));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r + 1], c, -m));
+        pk[r >> 1] = pack_bf16x2(p0, p1);
+        part[(r >> 1) & 1] += p0 + p1;
+      }
+      return part[0] + part[1];
+    };
+    float ps = probs();
+    if (__any(ps > kSumBound)) {
+      float mx = kNegInf;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+      mx = fmaxf(mx, wave_xor32(mx));
+      const float m_new = fmaxf(m, mx * c);
+      const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+      lsum *= alpha;
+      m = m_new;
+      ps = probs();
+    }
+    lsum += ps;
+
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const bf16x8 b = __builtin_bit_cast(
+          bf16x8, u32x4{pk[4 * half], pk[4 * half + 1], pk[4 * half + 2], pk[4 * half + 3]});
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const char* vp = vs + (va_ ^ (64 * db)) + 16 * half * ROW;
+        const u32x2 lo = lds_read_tr16(vp);
+        const u32x2 hi = lds_read_tr16(vp + 8 * ROW);
+        acc[db] = mfma_32x32x16_bf16(__builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y}),
+                                     b, acc[db]);
+      }
+    }
+  }
+  // group 0 took no key tile of the heavy tile: the light tile is still open
+  // and the heavy tile's share of group 0 is empty (m = kMInit, sum 0)
+  if (grp == 0 && nr == ra) switch_tile();
+
+  // merge the heavy tile: group 1 parks (acc, m, sum) in LDS (the stages are
+  // free: every wave is past its last round), group 0 adds it to its own
+  // share with both rescaled to the larger max, and writes the rows
+  __syncthreads();
+  char* park = smem_raw + w * (NDB * 16 * 64 * 4);   // 32 KiB per 32-row block
+  float* park_ml = reinterpret_cast<float*>(smem_raw + 4 * NDB * 16 * 64 * 4) + 2 * (w * 64 + lane);
+  if (grp == 1) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<f32x4*>(park + ((db * 4 + g) * 64 + lane) * 16) =
+            f32x4{acc[db][4 * g], acc[db][4 * g + 1], acc[db][4 * g + 2], acc[db][4 * g + 3]};
+    park_ml[0] = m;
+    park_ml[1] = lsum;
+  }
+  __syncthreads();
+  if (grp == 0) {
+    const float m1 = park_ml[0], l1 = park_ml[1];
+    const float mm = fmaxf(m, m1);
+    const float a0 = __builtin_amdgcn_exp2f(m - mm), a1 = __builtin_amdgcn_exp2f(m1 - mm);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 o1 = *reinterpret_cast<const f32x4*>(park + ((db * 4 + g) * 64 + lane) * 16);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[db][4 * g + e] = acc[db][4 * g + e] * a0 + o1[e] * a1;
+      }
+    lsum = lsum * a0 + l1 * a1;
+    m = mm;
+    store_out();
+  }
+}
+
 // FP8 forward ("LLM Architecture Refresh [3]", section 8: the FA-3 direction
 // of lower-precision matrix inputs).  Q, K and V arrive as OCP e4m3 bytes
 // with one dequantisation factor per tensor; both products run on
@@ -1992,6 +2263,27 @@ template <bool CAUSAL>
 hipError_t launch_d256(FwdArgs a, hipStream_t stream) {
   constexpr int smem = 4 * kBN256 * 256 * 2;
   a.pass = max(1, device_cus() / 8);
+  if constexpr (CAUSAL) {
+    // only where the plain grid is a single wave of workgroups (two per CU):
+    // with more, the hardware's dispatch of the later ones balances the CUs
+    // and the plain kernel is faster ([2, 16, 4096, 256]: 39.0 % against
+    // 37.1 % of peak; [1, 16, 4096, 256]: 30.9 % against 36.7 %)
+    if (a.nsplit == 1 && a.nqt >= 2 && a.nqt % 2 == 0 && a.Nk > 0 && a.koff >= 0 &&
+        (long long)a.BH * a.nqt <= 2LL * device_cus()) {
+      // balanced pairs of query tiles: two K / V stage sets, then the merge's
+      // parked float32 output (4 x 32 rows x 256) and (max, sum) per lane
+      constexpr int park = 4 * 32 * 256 * 4 + 4 * 64 * 8;
+      constexpr int smem_pair = 2 * smem > park ? 2 * smem : park;
+      static_assert(smem_pair <= 160 * 1024, "LDS budget");
+      auto kp = fwd_d256_pair_kernel<true>;
+      hipError_t e = hipFuncSetAttribute((const void*)kp,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, smem_pair);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(kp, dim3(a.BH * (a.nqt / 2)), dim3(2 * 64 * kWaves256), smem_pair,
+                         stream, a);
+      return hipGetLastError();
+    }
+  }
   auto kern = fwd_d256_kernel<CAUSAL>;
   hipError_t e =
       hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, smem);

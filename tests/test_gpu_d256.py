@@ -1,7 +1,9 @@
 """GPU parity of the head-dimension-256 forward (fa_fwd, fa_fwd_gqa and
 fa_fwd_kv at d = 256) against the float64 oracle.
 
-d = 256 runs its own kernel (one wave per SIMD, 32-key tiles); the operation
+d = 256 runs its own kernels (32-key tiles; causal with an even number of
+query tiles: balanced pairs of tiles, the heavy one split over two wave
+groups and merged); the operation
 and the tolerances are those of the other forwards: O within 2e-2 (bf16
 output), lse within 1e-3, max abs over every element.
 """
@@ -52,7 +54,7 @@ def _cmp(o, lse, ro, rl):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("N", [1, 31, 33, 129, 257, 1000])
+@pytest.mark.parametrize("N", [1, 31, 33, 129, 256, 257, 1000, 2048])
 def test_d256_forward(N, causal):
     _say(f"[d256 fwd] N={N} causal={causal}")
     q, k, v = make_inputs(2, 3, N, D, torch.bfloat16, seed=1000 + N)
@@ -63,15 +65,16 @@ def test_d256_forward(N, causal):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-def test_d256_forward_gqa(causal):
-    q, k, v = make_gqa_inputs(1, 8, 2, 300, D, seed=1100)
+@pytest.mark.parametrize("N", [300, 512])
+def test_d256_forward_gqa(N, causal):
+    q, k, v = make_gqa_inputs(1, 8, 2, N, D, seed=1100 + N)
     o, lse = fa.forward(q.cuda(), k.cuda(), v.cuda(), causal, 0.07)
     torch.cuda.synchronize()
     _cmp(o, lse, *naive_fwd_gqa(_f64(q), _f64(k), _f64(v), _s32(0.07), causal))
 
 
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("nq,nk", [(1, 3000), (40, 700), (300, 100)])
+@pytest.mark.parametrize("nq,nk", [(1, 3000), (40, 700), (300, 100), (256, 700), (1000, 1030)])
 def test_d256_forward_kv(nq, nk, causal):
     _say(f"[d256 kv] Nq={nq} Nk={nk} causal={causal}")
     q = make_gqa_inputs(1, 4, 2, nq, D, seed=1200 + nq)[0]
@@ -106,6 +109,26 @@ def test_d256_large_sampled():
         wl = max(wl, float(np.max(np.abs(gl[0, h, rows] - rl))))
     _say(f"[d256 4096 sampled] max|dO|={wo:.3e} max|dlse|={wl:.3e}")
     assert wo <= TOL and wl <= TOL_LSE
+
+
+def test_d256_causal_pairs_full_heads():
+    """[1, 16, 4096, 256] causal, every row of three heads (one per pair
+    position: heads on different XCDs) -- the balanced pair kernel, whose
+    heavy tiles are split between two wave groups and merged -- against the
+    oracle."""
+    from oracle import naive_fwd_rows
+    q, k, v = make_inputs(1, 16, 4096, D, torch.bfloat16, seed=1500)
+    scale = 1 / math.sqrt(D)
+    o, lse = fa.forward(q.cuda(), k.cuda(), v.cuda(), True, scale)
+    torch.cuda.synchronize()
+    go, gl = _f64(o), _f64(lse)
+    rows = np.arange(4096)
+    for h in (0, 7, 15):
+        ro, rl = naive_fwd_rows(_f64(q[0, h]), _f64(k[0, h]), _f64(v[0, h]), _s32(scale), True, rows)
+        eo = float(np.max(np.abs(go[0, h] - ro)))
+        el = float(np.max(np.abs(gl[0, h] - rl)))
+        _say(f"[d256 pairs head {h}] max|dO|={eo:.3e} max|dlse|={el:.3e}")
+        assert eo <= TOL and el <= TOL_LSE
 
 
 # --- backward at d = 256 -----------------------------------------------------------
