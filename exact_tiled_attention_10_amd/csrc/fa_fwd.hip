@@ -275,7 +275,10 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(const FwdArgs a) {
   // Matrix phase of round j: O^T += V^T P^T for tile j - 1 (skipped in the
   // first round) and the scores S^T = K Q^T of tile j (skipped in the last),
   // in steps of two value-product MFMAs (one 16-key chunk, two 32-feature
-  // blocks) and two score MFMAs (two 16-feature k-steps).  The operands of
+  // blocks) and two score MFMAs (16-feature k-step t of both 32-key
+  // sub-blocks), issued value, score, value, score: the two score
+  // accumulators are independent chains, so no MFMA waits on the one just
+  // before it (one wave per SIMD issues every MFMA of a phase).  The operands of
   // step t + 1 are read from LDS (into the other half of a double buffer)
   // before the MFMAs of step t are issued, so the LDS latency hides behind
   // the matrix work; scheduling barriers keep that order.
@@ -312,29 +315,29 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(const FwdArgs a) {
         }
       }
       if constexpr (DO_S) {
+        // feature chunk t of both 32-key sub-blocks: two independent chains
 #pragma unroll
         for (int i = 0; i < 2; ++i)
-          o.k[i] = *reinterpret_cast<const bf16x8*>(
-              ks + kaddr(half * (C::NQC / 2) + 2 * u + i) + sb * 32 * C::ROW_BYTES);
+          o.k[i] = *reinterpret_cast<const bf16x8*>(ks + kaddr(t) + i * 32 * C::ROW_BYTES);
       }
     };
     auto compute = [&](const StepOps& o, int t) __attribute__((always_inline)) {
       const int kc = t / SUB, u = t % SUB, sb = kc >> 1, half = kc & 1;
-      if constexpr (DO_PV) {
-        const bf16x8 b = __builtin_bit_cast(
-            bf16x8, u32x4{pk[sb][4 * half + 0], pk[sb][4 * half + 1], pk[sb][4 * half + 2],
-                          pk[sb][4 * half + 3]});
-#pragma unroll
-        for (int i = 0; i < 2; ++i) acc[2 * u + i] = mfma_32x32x16_bf16(o.v[i], b, acc[2 * u + i]);
-      }
+      static_assert(NSTEP == C::NQC && NSB == 2, "one feature chunk per step");
       if constexpr (DO_S) {
-        if (half == 0 && u == 0) {
+        if (t == 0) {
           const f32x16 zero = {};
-          s[sb] = zero;
+          s[0] = zero;
+          s[1] = zero;
         }
+      }
+      const bf16x8 b = __builtin_bit_cast(
+          bf16x8, u32x4{pk[sb][4 * half + 0], pk[sb][4 * half + 1], pk[sb][4 * half + 2],
+                        pk[sb][4 * half + 3]});
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-          s[sb] = mfma_32x32x16_bf16(o.k[i], qf[half * (C::NQC / 2) + 2 * u + i], s[sb]);
+      for (int i = 0; i < 2; ++i) {
+        if constexpr (DO_PV) acc[2 * u + i] = mfma_32x32x16_bf16(o.v[i], b, acc[2 * u + i]);
+        if constexpr (DO_S) s[i] = mfma_32x32x16_bf16(o.k[i], qf[t], s[i]);
       }
     };
     __builtin_amdgcn_s_setprio(1);
