@@ -22,6 +22,7 @@ from .attention import (
     naive_probs,
     naive_fwd,
     naive_fwd_rows,
+    naive_bwd_rows,
     naive_bwd,
     visible_mask,
     kv_head_of,
@@ -45,6 +46,7 @@ __all__ = [
     "naive_probs",
     "naive_fwd",
     "naive_fwd_rows",
+    "naive_bwd_rows",
     "naive_bwd",
     "visible_mask",
     "kv_head_of",

@@ -25,7 +25,10 @@ dS_ij = P_ij (dP_ij - sum_k P_ik dP_ik); dQ = s dS K, dK = s dS^T Q, the scale
 factor s multiplying both ("FlashAttention from scratch", Follow-up questions).
 
 To bound memory the score matrix is formed ``row_chunk`` query rows at a time;
-each row's arithmetic is unchanged by that (softmax is row-wise).
+each row's arithmetic is unchanged by that (softmax is row-wise).  For the same
+reason ``naive_fwd_rows`` and ``naive_bwd_rows`` evaluate the definitions for
+selected rows only (checks at sizes where the whole score matrix is out of
+reach); both are pinned against the full forms and torch's float64 autograd.
 """
 
 from __future__ import annotations
@@ -188,6 +191,37 @@ def naive_bwd(q, k, v, do, scale: float, causal: bool = False,
                                               scale, causal, row_chunk)
     return dq, dk, dv
 
+
+
+def naive_bwd_rows(q_rows, k, v, do_rows, scale: float, causal: bool, positions,
+                   keys=None):
+    """What selected query rows of one head carry into the gradients (sampled checks).
+
+    q_rows, do_rows: [R, d] queries and output gradients at sequence positions
+    ``positions`` (R distinct ints); k, v: [N, d] the head's full keys and
+    values; ``keys``: the key indices whose contributions are returned (all by
+    default).  Returns (dQ [R, d] of those rows, their part of dK and of dV
+    [len(keys), d]).  Same definition as ``naive_bwd`` (the softmax Jacobian,
+    "FlashAttention from scratch", Follow-up questions), restricted to the
+    given rows: dQ of a row needs only that row, and dK, dV are sums over
+    rows, so for keys that only the given rows see (under causal masking, the
+    last keys of the sequence when the rows are the last positions) the parts
+    returned are those keys' whole gradients.
+    """
+    q_rows = _as_f64(q_rows)
+    k = _as_f64(k)
+    v = _as_f64(v)
+    do_rows = _as_f64(do_rows)
+    scale = float(scale)
+    pos = np.asarray(positions, dtype=np.int64)
+    s = scale * (q_rows @ k.T)
+    if causal:
+        s = np.where(np.arange(k.shape[0])[None, :] <= pos[:, None], s, -np.inf)
+    p = softmax_rows(s)
+    dp = do_rows @ v.T
+    ds = p * (dp - np.sum(p * dp, axis=1, keepdims=True))
+    sel = np.arange(k.shape[0]) if keys is None else np.asarray(keys, dtype=np.int64)
+    return scale * (ds @ k), scale * (ds[:, sel].T @ q_rows), p[:, sel].T @ do_rows
 
 # ---------------------------------------------------------------------------
 # Grouped-query attention

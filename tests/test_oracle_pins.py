@@ -363,6 +363,60 @@ def test_sampled_rows_match_full_oracle(causal):
     np.testing.assert_allclose(l_r, lse[pos], atol=1e-14)
 
 
+
+def _autograd_f64(q, k, v, do, scale, causal):
+    tq, tk, tv = (torch.from_numpy(x).requires_grad_(True) for x in (q, k, v))
+    o = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal,
+                                                         scale=scale)
+    o.backward(torch.from_numpy(do))
+    return tq.grad.numpy(), tk.grad.numpy(), tv.grad.numpy()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_sampled_backward_rows_match_library_autograd(causal):
+    """The row-wise backward used for full-size checks: each row's dQ, and the
+    rows' parts of dK and dV summed over a partition of all rows, equal torch's
+    float64 autograd of its own SDPA (a library routine)."""
+    from oracle import naive_bwd_rows
+    rng = np.random.default_rng(14)
+    n, d, scale = 41, 8, 0.35
+    q, k, v, do = (rng.standard_normal((n, d)) for _ in range(4))
+    gq, gk, gv = _autograd_f64(q, k, v, do, scale, causal)
+    dk = np.zeros((n, d))
+    dv = np.zeros((n, d))
+    for part in (np.arange(0, 13), np.array([13, 20, 40]), np.arange(14, 20),
+                 np.arange(21, 40)):
+        dq_r, dk_p, dv_p = naive_bwd_rows(q[part], k, v, do[part], scale, causal, part)
+        assert np.max(np.abs(dq_r - gq[part])) < 1e-12
+        dk += dk_p
+        dv += dv_p
+    assert np.max(np.abs(dk - gk)) < 1e-12
+    assert np.max(np.abs(dv - gv)) < 1e-12
+    # a subset of keys returns the same parts as the full set
+    keys = np.array([0, 7, 40])
+    _, dk_s, dv_s = naive_bwd_rows(q[:13], k, v, do[:13], scale, causal, np.arange(13), keys)
+    _, dk_f, dv_f = naive_bwd_rows(q[:13], k, v, do[:13], scale, causal, np.arange(13))
+    np.testing.assert_array_equal(dk_s, dk_f[keys])
+    np.testing.assert_array_equal(dv_s, dv_f[keys])
+
+
+def test_causal_last_rows_carry_whole_gradients_of_last_keys():
+    """Under causal masking the last t keys are seen only by the last t queries,
+    so those rows' parts are the keys' complete dK and dV (the form the
+    maximum-length GPU check uses)."""
+    from oracle import naive_bwd_rows
+    rng = np.random.default_rng(15)
+    n, d, t, scale = 50, 8, 6, 0.3
+    q, k, v, do = (rng.standard_normal((n, d)) for _ in range(4))
+    _, gk, gv = _autograd_f64(q, k, v, do, scale, True)
+    rows = np.arange(n - t, n)
+    _, dk_p, dv_p = naive_bwd_rows(q[rows], k, v, do[rows], scale, True, rows, rows)
+    assert np.max(np.abs(dk_p - gk[rows])) < 1e-12
+    assert np.max(np.abs(dv_p - gv[rows])) < 1e-12
+    # and the same keys with one row fewer are not complete
+    _, dk_m, _ = naive_bwd_rows(q[rows[1:]], k, v, do[rows[1:]], scale, True, rows[1:], rows)
+    assert np.max(np.abs(dk_m - gk[rows])) > 1e-6
+
 # --- grouped-query attention -------------------------------------------------
 
 @pytest.mark.parametrize("causal", [False, True])
