@@ -87,6 +87,24 @@ def make_inputs(B: int, H: int, N: int, d: int, dtype=torch.bfloat16,
     return tuple(out)
 
 
+
+def make_device_inputs(B: int, H: int, N: int, d: int, dtype=torch.bfloat16,
+                       seed: int = 0, with_do: bool = False, device: str = "cuda"):
+    """``make_inputs`` drawn on the device, for sizes whose host-side draw
+    would dominate a test (the longest sequences).
+
+    Same recipe (torch.randn float32 in the order q, k, v, dO, then the cast),
+    from torch's generator of that device seeded with ``seed``; its stream of
+    numbers differs from the CPU generator's, so these are other inputs of the
+    same distribution, not the same inputs.
+    """
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    shape = (B, H, N, d)
+    out = [torch.randn(shape, generator=g, dtype=torch.float32, device=device).to(dtype)
+           for _ in range(4 if with_do else 3)]
+    return tuple(out)
+
 def workload_inputs(w: Workload, with_do: bool = None):
     """Inputs for a named workload (dO included for backward workloads)."""
     if with_do is None:
