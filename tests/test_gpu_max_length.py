@@ -14,7 +14,10 @@ the CPU against the full forms and torch's float64 autograd):
   rows) against the oracle, every output finite;
 * backward, d = 64: dQ of the same rows, and dK, dV of the last 16 keys,
   whose gradients under causal masking come only from the last 16 queries
-  (so the oracle's rows carry them whole).
+  (so the oracle's rows carry them whole);
+* decode (``fa_fwd_kv``): one new token of 32 query heads against a cache of
+  2^22 keys in 8 key/value heads, d = 128 (the split-key path and its merge),
+  three query heads on three key/value heads against the oracle.
 
 Inputs are drawn on the device (``make_device_inputs``); the oracle receives
 the float64 upcast of exactly the values the GPU received.  Tolerances are the
@@ -125,3 +128,29 @@ def test_backward_at_max_length():
     assert ek < TOL_BF16 and ev < TOL_BF16
     assert ek <= bk
     assert ev <= bv
+
+
+def test_decode_against_max_length_cache():
+    H, Hkv, d = 32, 8, 128
+    _say(f"[max length N={N}] decode, {H}/{Hkv} heads, d={d}")
+    q = make_device_inputs(1, H, 1, d, seed=80)[0]
+    _, k, v = make_device_inputs(1, Hkv, N, d, seed=81)
+    scale = 1.0 / math.sqrt(d)
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full((1, H, 1), float("nan"), dtype=torch.float32, device="cuda")
+    nb = fa.fa_fwd_kv_workspace_size(1, H, Hkv, 1, N, d)
+    ws = torch.empty((max(1, nb),), dtype=torch.uint8, device="cuda")
+    fa.fa_fwd_kv(q, k, v, o, lse, ws if nb else None, True, scale)
+    torch.cuda.synchronize()
+    _say(f"  workspace {nb} bytes")
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
+    for h in (0, 13, 31):
+        g = h // (H // Hkv)
+        ro, rl = naive_fwd_rows(_f64(q[0, h]), _f64(k[0, g]), _f64(v[0, g]), _s32(scale), True,
+                                np.array([N - 1]))
+        eo = np.abs(_f64(o[0, h]) - ro).max()
+        el = abs(float(lse[0, h, 0]) - rl[0])
+        _say(f"  head {h} (key/value head {g}): max |dO| {eo:.3g}, |dlse| {el:.3g}")
+        assert eo < TOL_BF16
+        assert el < TOL_LSE
+
