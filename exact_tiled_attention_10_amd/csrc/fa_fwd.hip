@@ -382,21 +382,40 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(const FwdArgs a) {
   auto softmax_phase = [&](int j) __attribute__((always_inline)) {
     if (j < 0 || j >= nkt) return;
     const int k0 = kb + j * BN;
+    if (CAUSAL && k0 > wq0 + 31 + koff) {
+      // every key of the tile after every query of the wave: P = 0
+#pragma unroll
+      for (int sb = 0; sb < NSB; ++sb)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pk[sb][i] = 0u;
+      return;
+    }
     if ((k0 + BN > ke) || (CAUSAL && k0 + BN - 1 > wq0 + koff)) {
       // register r of sub-block sb holds key k0 + 4h + off(sb, r) with
       // off = 32sb + 8(r/4) + r%4; it is dead past the lane's limit (the
       // last key its query sees under causal masking, and ke - 1).  Scores
       // of a tile with no visible key give p = 0: m is finite (kMInit or a
       // real maximum), so exp2(-inf - m) = 0 and no rebase is triggered.
+      // Sub-blocks wholly visible to the wave keep their scores; wholly
+      // invisible ones take -inf without a compare.
       int lim = ke - 1 - k0 - 4 * h;
       if (CAUSAL) lim = min(lim, qrow + koff - k0 - 4 * h);
 #pragma unroll
-      for (int sb = 0; sb < NSB; ++sb)
+      for (int sb = 0; sb < NSB; ++sb) {
+        const int sk0 = k0 + 32 * sb;
+        const bool full = sk0 + 31 < ke && (!CAUSAL || sk0 + 31 <= wq0 + koff);
+        const bool dead = sk0 >= ke || (CAUSAL && sk0 > wq0 + 31 + koff);
+        if (dead) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int off = 32 * sb + 8 * (r >> 2) + (r & 3);
-          s[sb][r] = off > lim ? kNegInf : s[sb][r];
+          for (int r = 0; r < 16; ++r) s[sb][r] = kNegInf;
+        } else if (!full) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int off = 32 * sb + 8 * (r >> 2) + (r & 3);
+            s[sb][r] = off > lim ? kNegInf : s[sb][r];
+          }
         }
+      }
     }
     float ps = probs();
     if (__any(ps > kSumBound)) {
