@@ -724,7 +724,6 @@ __global__ __launch_bounds__(256, 4) void fwd_inorder_kernel(const FwdArgs a) {
     const char* ks = smem_raw + (j & 1) * C::STAGE;
     const char* vs = ks + C::TILE;
 
-    const bool need_mask = (k0 + BN > ke) || (CAUSAL && k0 + BN - 1 > wq0 + koff);
     // the tile in two halves of 32 keys (half the score and probability
     // registers of a whole tile live at once): per half S^T (lane = query;
     // register r holds key k0 + 32 sb + 8 (r / 4) + 4 h + r % 4), mask,
@@ -739,7 +738,9 @@ __global__ __launch_bounds__(256, 4) void fwd_inorder_kernel(const FwdArgs a) {
             *reinterpret_cast<const bf16x8*>(ks + (ka ^ (32 * cc)) + sb * 32 * C::ROW);
         s = mfma_32x32x16_bf16(kf, qf[cc], s);
       }
-      if (need_mask) {
+      // a half wholly visible to the wave (keys before every query, all < ke)
+      // needs no mask
+      if ((k0 + 32 * sb + 32 > ke) || (CAUSAL && k0 + 32 * sb + 31 > wq0 + koff)) {
         int lim = ke - 1 - k0 - 32 * sb - 4 * h;
         if (CAUSAL) lim = min(lim, qrow + koff - k0 - 32 * sb - 4 * h);
 #pragma unroll
