@@ -964,6 +964,7 @@ __global__ __launch_bounds__(256, 2) void fwd_d256_kernel(const FwdArgs a) {
     const char* ks = smem_raw + (j & 1) * TILE;
     const char* vs = smem_raw + OFF_V + (j & 1) * TILE;
     const int k0 = kb + j * BN;
+    if (CAUSAL && k0 > wq0 + 31 + koff) continue;   // every key after every query
 
     f32x16 s = {};
     const int ka_ = opaque(ka), va_ = opaque(va);
@@ -1229,6 +1230,7 @@ __global__ __launch_bounds__(512, 2) void fwd_d256_pair_kernel(const FwdArgs a) 
     const char* ks = smem_raw + grp * GROUP_LDS + (j & 1) * TILE;
     const char* vs = smem_raw + grp * GROUP_LDS + OFF_V + (j & 1) * TILE;
     const int k0 = key_tile(j) * BN;
+    if (CAUSAL && k0 > wq0 + 31 + koff) continue;   // every key after every query
 
     f32x16 s = {};
     const int ka_ = opaque(ka), va_ = opaque(va);
@@ -1498,6 +1500,7 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const FwdArgs a, float 
     const char* ks = smem_raw + (j & 1) * TILE;
     const char* vs = smem_raw + OFF_V + (j & 1) * TILE;
     const int k0 = kb + j * BN;
+    if (CAUSAL && k0 > wq0 + 31 + koff) continue;   // every key after every query
 
     f32x16 s[2];
 #pragma unroll
@@ -1513,15 +1516,26 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const FwdArgs a, float 
       }
     }
     if ((k0 + BN > ke) || (CAUSAL && k0 + BN - 1 > wq0 + koff)) {
+      // sub-blocks wholly visible to the wave keep their scores, wholly
+      // invisible ones take -inf without a compare
       int lim = ke - 1 - k0 - 4 * h;
       if (CAUSAL) lim = min(lim, qrow + koff - k0 - 4 * h);
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
+      for (int sb = 0; sb < 2; ++sb) {
+        const int sk0 = k0 + 32 * sb;
+        const bool full = sk0 + 31 < ke && (!CAUSAL || sk0 + 31 <= wq0 + koff);
+        const bool dead = sk0 >= ke || (CAUSAL && sk0 > wq0 + 31 + koff);
+        if (dead) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int off = 32 * sb + 8 * (r >> 2) + (r & 3);
-          s[sb][r] = off > lim ? kNegInf : s[sb][r];
+          for (int r = 0; r < 16; ++r) s[sb][r] = kNegInf;
+        } else if (!full) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int off = 32 * sb + 8 * (r >> 2) + (r & 3);
+            s[sb][r] = off > lim ? kNegInf : s[sb][r];
+          }
         }
+      }
     }
     auto probs = [&]() __attribute__((always_inline)) {
       float part[4];
