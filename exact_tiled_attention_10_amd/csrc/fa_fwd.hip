@@ -1838,10 +1838,14 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(const float* __restrict_
   const int part = (int)(gid % TPR);
   if (row >= (size_t)rows) return;
   float mx = kNegInf;
+  // (unrolled so several splits' loads are in flight at once: the loop is
+  // latency-bound, a few thousand threads for the whole merge)
+#pragma unroll 8
   for (int s = 0; s < nsplit; ++s) mx = fmaxf(mx, Lpart[(size_t)s * rows + row]);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float den = 0.f;
   if (mx != kNegInf) {
+#pragma unroll 8
     for (int s = 0; s < nsplit; ++s) {
       const float wgt = __expf(Lpart[(size_t)s * rows + row] - mx);
       den += wgt;
