@@ -1825,29 +1825,38 @@ __global__ __launch_bounds__(64, 2) void fwd_decode_kernel(const FwdArgs a) {
 // scaffold": blocks over disjoint keys combine through their log-sum-exps):
 // lse = log sum_s e^{lse_s}, O = sum_s e^{lse_s - lse} O_s.  Ranges with
 // lse_s = -inf weigh 0; a row with no visible key at all keeps O = 0 and
-// lse = -inf.  One thread per (row, 8 features).
+// lse = -inf.  A row's D / 8 feature threads are repeated over 2^sg_log2
+// split groups (split s to group s mod 2^sg_log2) whose maxima, weights and
+// weighted sums are combined through LDS: with many splits (the decode's
+// ranges) one thread per row would walk them all, one latency after another.
 template <int D>
 __global__ __launch_bounds__(256) void fwd_merge_kernel(const float* __restrict__ Opart,
                                                         const float* __restrict__ Lpart,
                                                         uint16_t* __restrict__ O,
                                                         float* __restrict__ LSE, int rows,
-                                                        int nsplit) {
+                                                        int nsplit, int sg_log2) {
   constexpr int TPR = D / 8;
-  const size_t gid = (size_t)blockIdx.x * 256 + threadIdx.x;
-  const size_t row = gid / TPR;
-  const int part = (int)(gid % TPR);
-  if (row >= (size_t)rows) return;
+  __shared__ float red[256 * 9];
+  const int SG = 1 << sg_log2;
+  const int per_row = TPR << sg_log2;   // threads per row (<= 256)
+  const int t = threadIdx.x;
+  const int lr = t / per_row;
+  const int sg = (t - lr * per_row) / TPR;
+  const int part = t % TPR;
+  const size_t row = (size_t)blockIdx.x * (256 / per_row) + lr;
+  const bool live = row < (size_t)rows;
   float mx = kNegInf;
-  // (unrolled so several splits' loads are in flight at once: the loop is
-  // latency-bound, a few thousand threads for the whole merge)
-#pragma unroll 8
-  for (int s = 0; s < nsplit; ++s) mx = fmaxf(mx, Lpart[(size_t)s * rows + row]);
+  if (live)
+    for (int s = sg; s < nsplit; s += SG) mx = fmaxf(mx, Lpart[(size_t)s * rows + row]);
+  red[t] = mx;
+  __syncthreads();
+  float gmx = kNegInf;
+  for (int g = 0; g < SG; ++g) gmx = fmaxf(gmx, red[lr * per_row + g * TPR]);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float den = 0.f;
-  if (mx != kNegInf) {
-#pragma unroll 8
-    for (int s = 0; s < nsplit; ++s) {
-      const float wgt = __expf(Lpart[(size_t)s * rows + row] - mx);
+  if (live && gmx != kNegInf) {
+    for (int s = sg; s < nsplit; s += SG) {
+      const float wgt = __expf(Lpart[(size_t)s * rows + row] - gmx);
       den += wgt;
       const f32x4* src = reinterpret_cast<const f32x4*>(Opart + ((size_t)s * rows + row) * D +
                                                         part * 8);
@@ -1859,11 +1868,23 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(const float* __restrict_
       }
     }
   }
+  __syncthreads();   // every thread has read the maxima
+  red[9 * t] = den;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) red[9 * t + 1 + i] = acc[i];
+  __syncthreads();
+  if (!live || sg != 0) return;
+  for (int g = 1; g < SG; ++g) {
+    const float* o = red + 9 * (lr * per_row + g * TPR + part);
+    den += o[0];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] += o[1 + i];
+  }
   const float inv = den > 0.f ? 1.f / den : 0.f;
   u32x4 out = {pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
                pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv)};
   *reinterpret_cast<u32x4*>(O + row * D + part * 8) = out;
-  if (part == 0) LSE[row] = den > 0.f ? mx + __logf(den) : kNegInf;
+  if (part == 0) LSE[row] = den > 0.f ? gmx + __logf(den) : kNegInf;
 }
 
 // ---------------------------------------------------------------------------
@@ -2252,17 +2273,21 @@ hipError_t launch_bf16(const FwdArgs& a, hipStream_t stream) {
 
 hipError_t launch_merge(const FwdArgs& a, int d, hipStream_t stream) {
   const size_t rows = (size_t)a.BH * a.Nq;
-  const size_t threads = rows * (d / 8);
-  const dim3 grid((unsigned)((threads + 255) / 256));
+  // split groups: about four splits per thread, at most 256 threads per row
+  const int tpr = d / 8;
+  int sg_log2 = 0;
+  while ((4 << sg_log2) < a.nsplit && (tpr << (sg_log2 + 1)) <= 256) ++sg_log2;
+  const size_t rows_per_wg = 256 / ((size_t)tpr << sg_log2);
+  const dim3 grid((unsigned)((rows + rows_per_wg - 1) / rows_per_wg));
   if (d == 256)
     hipLaunchKernelGGL(fwd_merge_kernel<256>, grid, dim3(256), 0, stream, a.Opart, a.Lpart, a.O,
-                       a.LSE, (int)rows, a.nsplit);
+                       a.LSE, (int)rows, a.nsplit, sg_log2);
   else if (d == 128)
     hipLaunchKernelGGL(fwd_merge_kernel<128>, grid, dim3(256), 0, stream, a.Opart, a.Lpart, a.O,
-                       a.LSE, (int)rows, a.nsplit);
+                       a.LSE, (int)rows, a.nsplit, sg_log2);
   else
     hipLaunchKernelGGL(fwd_merge_kernel<64>, grid, dim3(256), 0, stream, a.Opart, a.Lpart, a.O,
-                       a.LSE, (int)rows, a.nsplit);
+                       a.LSE, (int)rows, a.nsplit, sg_log2);
   return hipGetLastError();
 }
 
