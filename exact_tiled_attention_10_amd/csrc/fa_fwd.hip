@@ -2121,24 +2121,39 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_split_kernel(
   float* ks = smemf + w * WTILE;
   float* vs = ks + C::TILE;
 
-  for (int kt = w; kt < nkt; kt += WAVES) {
+  // the wave's next tile is read from global memory into registers while
+  // the current one is computed (rows past N read as 0)
+  f32x4 kreg[PER], vreg[PER];
+  auto fetch = [&](int kt) __attribute__((always_inline)) {
     const int k0 = kt * C::BN;
-    // this wave's tile into its LDS region (rows past N read as 0)
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int ci = i * 64 + lane;
       const int row = ci / (D / 4);
       const int col = (ci % (D / 4)) * 4;
-      f32x4 kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
+      kreg[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      vreg[i] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (k0 + row < N) {
-        kv = *reinterpret_cast<const f32x4*>(Kh + (size_t)(k0 + row) * D + col);
-        vv = *reinterpret_cast<const f32x4*>(Vh + (size_t)(k0 + row) * D + col);
+        kreg[i] = *reinterpret_cast<const f32x4*>(Kh + (size_t)(k0 + row) * D + col);
+        vreg[i] = *reinterpret_cast<const f32x4*>(Vh + (size_t)(k0 + row) * D + col);
       }
-      *reinterpret_cast<f32x4*>(ks + row * C::RS + col) = kv;
-      *reinterpret_cast<f32x4*>(vs + row * C::RS + col) = vv;
+    }
+  };
+  if (w < nkt) fetch(w);
+  for (int kt = w; kt < nkt; kt += WAVES) {
+    const int k0 = kt * C::BN;
+    // this wave's tile into its LDS region
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int ci = i * 64 + lane;
+      const int row = ci / (D / 4);
+      const int col = (ci % (D / 4)) * 4;
+      *reinterpret_cast<f32x4*>(ks + row * C::RS + col) = kreg[i];
+      *reinterpret_cast<f32x4*>(vs + row * C::RS + col) = vreg[i];
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the writes above are done
     __builtin_amdgcn_wave_barrier();
+    if (kt + WAVES < nkt) fetch(kt + WAVES);
 
     f32x16 s;
 #pragma unroll
