@@ -7,7 +7,8 @@ and key lengths 1-400, equal in half of the cases; causal or not; a scale of
 either sign.  Each runs the forward through the entry point its shape calls
 for (``fa_fwd``, ``fa_fwd_gqa`` or ``fa_fwd_kv``), NaN-prefilled outputs,
 against ``naive_fwd_kv``; every other one also runs the backward (``fa_bwd``,
-``fa_bwd_gqa`` or ``fa_bwd_kv``) against ``naive_bwd_kv``.  Tolerances: 2e-2
+``fa_bwd_gqa`` or ``fa_bwd_kv``) against ``naive_bwd_kv``; twelve more run
+fp32 inputs through ``fa_fwd_f32`` against ``naive_fwd``.  Tolerances: 2e-2
 on O and 1e-3 on the lse of rows that see a key (rows that see none must be
 O = 0, lse = -inf); the gradients within max(2e-2, 2^-7 max|ref|), one bf16
 ulp of the largest reference magnitude -- the bar the grouped-head and
@@ -131,3 +132,41 @@ def test_random_shape(case):
     bq, bk = d_term_bounds_kv(_f64(q), _f64(k), _f64(v), _f64(do), _s32(scale), causal)
     for g, r, bnd in zip((dq, dk, dv), ref, (bq, bk, 0.0)):
         assert np.max(np.abs(_f64(g) - r) - (tol + bnd)) <= 0.0
+
+
+def _draw_f32(count=12, seed=20261203):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(count):
+        d = int(rng.choice([64, 128]))
+        B = int(rng.integers(1, 3))
+        H = int(rng.integers(1, 5))
+        n = int(rng.integers(1, 401))
+        causal = bool(rng.random() < 0.5)
+        scale = float(rng.uniform(0.05, 0.3)) * (-1.0 if rng.random() < 0.15 else 1.0)
+        out.append((i, d, B, H, n, causal, round(scale, 4)))
+    return out
+
+
+CASES_F32 = _draw_f32()
+
+
+@pytest.mark.parametrize("case", CASES_F32, ids=[f"f{c[0]}" for c in CASES_F32])
+def test_random_shape_fp32(case):
+    """fp32 inputs (``fa_fwd_f32``) on twelve seeded random shapes: O within
+    1e-5, lse within 1e-3."""
+    from oracle import naive_fwd
+    from workloads import make_inputs
+    i, d, B, H, n, causal, scale = case
+    _say(f"[random fp32 {i}] d={d} B={B} H={H} N={n} causal={causal} scale={scale}")
+    q, k, v = make_inputs(B, H, n, d, torch.float32, seed=3000 + i)
+    qd, kd, vd = (t.cuda() for t in (q, k, v))
+    o = torch.full_like(qd, float("nan"))
+    lse = torch.full((B, H, n), float("nan"), dtype=torch.float32, device="cuda")
+    fa.fa_fwd_f32(qd, kd, vd, o, lse, causal, scale)
+    torch.cuda.synchronize()
+    ro, rl = naive_fwd(_f64(q), _f64(k), _f64(v), _s32(scale), causal)
+    eo = float(np.max(np.abs(_f64(o) - ro)))
+    el = float(np.max(np.abs(_f64(lse) - rl)))
+    _say(f"   max|dO|={eo:.3e} max|dlse|={el:.3e}")
+    assert eo <= 1e-5 and el <= TOL_LSE
