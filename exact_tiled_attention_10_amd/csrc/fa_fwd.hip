@@ -702,6 +702,7 @@ __global__ __launch_bounds__(256, 4) void fwd_inorder_kernel(const FwdArgs a) {
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
   float m = kMInit;
   float lsum = 0.f;
+  bool fresh = true;   // no half processed yet (wave-uniform)
 
   for (int j = 0; j < nkt; ++j) {
     // tile j landed for every wave; every wave is done with tile j - 1 (and,
@@ -764,6 +765,17 @@ __global__ __launch_bounds__(256, 4) void fwd_inorder_kernel(const FwdArgs a) {
         }
         return (part[0] + part[1]) + (part[2] + part[3]);
       };
+      if (fresh) {
+        // the wave's first half: m takes the true running max before any
+        // probability (against m's start value every p would overflow and
+        // force the rebase below); acc and l are still zero
+        float mx = kNegInf;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+        mx = fmaxf(mx, wave_xor32(mx));
+        m = fmaxf(m, mx * c);
+        fresh = false;
+      }
       float ps = probs();
       if (__any(ps > kSumBound)) {
         float mx = kNegInf;
