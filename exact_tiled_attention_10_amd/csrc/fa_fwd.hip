@@ -1504,6 +1504,7 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const FwdArgs a, float 
   float m = kMInit;
   float lsum = 0.f;
   int pw[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  bool fresh = true;   // no tile processed yet (wave-uniform)
 
   for (int j = 0; j < nkt; ++j) {
     wait_vmem();
@@ -1572,6 +1573,18 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const FwdArgs a, float 
         }
       return (part[0] + part[1]) + (part[2] + part[3]);
     };
+    if (fresh) {
+      // the wave's first tile: m takes the true running max before any
+      // probability (acc and l are still zero)
+      float mx = kNegInf;
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sb][r]);
+      mx = fmaxf(mx, wave_xor32(mx));
+      m = fmaxf(m, mx * c);
+      fresh = false;
+    }
     float ps = probs();
     if (__any(ps > kSumBound)) {
       float mx = kNegInf;
