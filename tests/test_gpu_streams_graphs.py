@@ -12,7 +12,10 @@ so the calls run on any stream and can be recorded into a HIP graph.
   NaN-filled and the workspace set to 0xFF by eager work between replays
   (so every replay must rewrite every output and re-zero its own dQ
   accumulator); each replay against the eager run, bit for bit where the
-  kernels are deterministic, and every gradient against the oracle.
+  kernels are deterministic, and every gradient against the oracle;
+* graph: one decoding token through ``fa_fwd_kv``'s split-key path (its
+  workspace written by one kernel and merged by the next) replayed the same
+  way.
 """
 
 import math
@@ -135,3 +138,44 @@ def test_graph_replays_of_the_staged_step(d):
                 continue
             assert torch.equal(a, b), f"replay {rep}: {name} differs from the eager run"
         _oracle_check(q, k, v, do, scale, causal, o, lse, dq, dk, dv, f"replay {rep}")
+
+
+def test_graph_replays_of_split_key_decode():
+    """One decoding token of 32 query heads over 8 key/value heads (d = 128,
+    4096 cached keys, batch 2) through ``fa_fwd_kv`` -- the split-key kernel
+    writing the caller's workspace and the merge reading it -- captured once
+    and replayed three times with NaN-filled outputs and a 0xFF workspace
+    between replays: each replay bit-identical to the eager run, and against
+    the oracle."""
+    from oracle import naive_fwd_kv
+    from workloads import make_gqa_inputs
+    B, H, Hkv, Nk, d = 2, 32, 8, 4096, 128
+    scale = 1.0 / math.sqrt(d)
+    _say(f"[graph decode] B={B} H={H} Hkv={Hkv} Nk={Nk} d={d}")
+    q = make_gqa_inputs(B, H, Hkv, 1, d, seed=330, with_do=False)[0].cuda()
+    _, k, v = (t.cuda() for t in make_gqa_inputs(B, H, Hkv, Nk, d, seed=331))
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full((B, H, 1), float("nan"), dtype=torch.float32, device="cuda")
+    nb = fa.fa_fwd_kv_workspace_size(B, H, Hkv, 1, Nk, d)
+    assert nb > 0, "the decode shape should take the split-key path"
+    ws = torch.full((nb,), 0xFF, dtype=torch.uint8, device="cuda")
+    fa.fa_fwd_kv(q, k, v, o, lse, ws, True, scale)
+    torch.cuda.synchronize()
+    eager = (o.clone(), lse.clone())
+    ro, rl = naive_fwd_kv(_f64(q), _f64(k), _f64(v), _s32(scale), True)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fa.fa_fwd_kv(q, k, v, o, lse, ws, True, scale)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        o.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        ws.fill_(0xFF)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, eager[0]) and torch.equal(lse, eager[1]), f"replay {rep}"
+        eo = float(np.abs(_f64(o) - ro).max())
+        el = float(np.abs(_f64(lse) - rl).max())
+        _say(f"   replay {rep}: O {eo:.3e} lse {el:.3e}")
+        assert eo <= TOL and el <= TOL_LSE
